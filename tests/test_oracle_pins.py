@@ -1,0 +1,317 @@
+"""Pins for the fp64 oracle: each test checks it against something other than
+itself (brute force, closed forms, library routines, finite differences,
+invariants of the mathematics), chosen so that a dropped term, a wrong sign,
+index or boundary, or a transposed operand fails at least one of them."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.spatial.distance import cdist
+
+from _pins import (brute_force, delannoy, log_delannoy, monotone_paths,
+                   rel_err, zero_dist_marginals)
+from sdtw_inputs import block_waves, pair_batch
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rand_dist(rng, B, N, M, scale=3.0):
+    return rng.random((B, N, M)) * scale
+
+
+# --- the distance -----------------------------------------------------------
+
+def test_sqeuclid_matches_scipy_cdist(O):
+    x, y = pair_batch(3, 7, 11, 5, seed=1)
+    d = O.sqeuclid(x.numpy(), y.numpy())
+    for b in range(3):
+        ref = cdist(x[b].double().numpy(), y[b].double().numpy(), "sqeuclidean")
+        np.testing.assert_allclose(d[b], ref, rtol=1e-13, atol=1e-13)
+    assert (d >= 0).all()  # README "Notes": squared distances are never negative
+
+
+def test_sqeuclid_round_f32_is_nearest_float(O):
+    x, y = pair_batch(2, 9, 6, 33, seed=2)
+    exact = O.sqeuclid(x.numpy(), y.numpy())
+    r = O.sqeuclid(x.numpy(), y.numpy(), round_f32=True)
+    # nearest fp32: no other fp32 is closer to the exact value
+    r32 = r.astype(np.float32)
+    up = np.nextafter(r32, np.float32(np.inf)).astype(np.float64)
+    dn = np.nextafter(r32, np.float32(-np.inf)).astype(np.float64)
+    err = np.abs(r - exact)
+    assert (err <= np.abs(up - exact)).all() and (err <= np.abs(dn - exact)).all()
+
+
+# --- forward and backward against brute force over all paths ---------------
+
+@pytest.mark.parametrize("N,M", [(1, 1), (1, 5), (4, 1), (2, 2), (3, 4), (5, 3),
+                                 (5, 5), (6, 6), (4, 7)])
+@pytest.mark.parametrize("gamma", [0.1, 1.0, 10.0])
+def test_forward_backward_match_brute_force(O, N, M, gamma):
+    rng = np.random.default_rng(N * 100 + M + int(gamma * 7))
+    dist = _rand_dist(rng, 2, N, M)
+    loss, R = O.forward(dist, gamma)
+    E = O.backward(dist, R, gamma)
+    for b in range(2):
+        v, Eb, _, npaths = brute_force(dist[b], gamma)
+        assert abs(loss[b] - v) <= 1e-12 * max(1.0, abs(v))
+        np.testing.assert_allclose(E[b], Eb, rtol=1e-10, atol=1e-12)
+        assert npaths == delannoy(N - 1, M - 1)
+
+
+def test_path_count_is_delannoy():
+    for n, m in [(1, 1), (2, 2), (3, 5), (7, 7)]:
+        assert len(monotone_paths(n, m)) == delannoy(n - 1, m - 1)
+    assert delannoy(6, 6) == 8989 and delannoy(7, 7) == 48639
+
+
+def test_local_backward_agrees_with_logspace(O):
+    rng = np.random.default_rng(7)
+    for gamma in (0.01, 0.3, 1.0, 5.0):
+        dist = _rand_dist(rng, 3, 37, 23)
+        _, R = O.forward(dist, gamma)
+        E1 = O.backward(dist, R, gamma)
+        E2 = O.backward_local(R, gamma)
+        np.testing.assert_allclose(E1, E2, rtol=1e-7, atol=1e-9)
+
+
+# --- closed forms --------------------------------------------------------------
+
+@pytest.mark.parametrize("N,M", [(1, 9), (8, 1), (1, 1)])
+def test_single_path_closed_form(O, N, M):
+    rng = np.random.default_rng(3)
+    dist = _rand_dist(rng, 2, N, M)
+    loss, R = O.forward(dist, 0.7)
+    E = O.backward(dist, R, 0.7)
+    np.testing.assert_allclose(loss, dist.sum(axis=(1, 2)), rtol=1e-14)
+    np.testing.assert_allclose(E, np.ones_like(E), rtol=1e-13)
+
+
+def test_two_by_two_golden(O):
+    g = json.load(open(os.path.join(GOLD, "two_by_two.json")))
+    dist = np.array([g["dist"]])
+    loss, R = O.forward(dist, g["gamma"])
+    E = O.backward(dist, R, g["gamma"])
+    assert abs(loss[0] - g["value"]) < 1e-14
+    np.testing.assert_allclose(E[0], np.array(g["E"]), rtol=1e-13)
+
+
+@pytest.mark.parametrize("N,M", [(2, 3), (5, 7), (16, 16), (16, 9), (33, 20)])
+@pytest.mark.parametrize("gamma", [0.05, 1.0])
+def test_zero_distance_delannoy(O, N, M, gamma):
+    dist = np.zeros((1, N, M))
+    loss, R = O.forward(dist, gamma)
+    E = O.backward(dist, R, gamma)
+    assert abs(loss[0] + gamma * log_delannoy(N - 1, M - 1)) <= 1e-12 * max(1, abs(loss[0]))
+    np.testing.assert_allclose(E[0], zero_dist_marginals(N, M), rtol=1e-10, atol=1e-13)
+
+
+def test_zero_distance_golden_large(O):
+    vals = json.load(open(os.path.join(GOLD, "log_delannoy.json")))["values"]
+    for v in vals:
+        if v["N"] * v["M"] > 600_000:
+            continue
+        x = np.full((1, v["N"], 3), 0.25, dtype=np.float32)
+        y = np.full((1, v["M"], 3), 0.25, dtype=np.float32)
+        dist = O.sqeuclid(x, y)
+        assert (dist == 0).all()
+        loss, _ = O.forward(dist, 1.0, keep_R=False)
+        assert abs(loss[0] + v["log_delannoy"]) <= 1e-9 * v["log_delannoy"]
+        if v["log_delannoy"] > 0:
+            assert loss[0] < 0  # Soft-DTW can be negative
+
+
+# --- gamma -> 0 and hard DTW ---------------------------------------------------
+
+def test_hard_dtw_brute_force(O):
+    rng = np.random.default_rng(11)
+    dist = _rand_dist(rng, 4, 5, 6)
+    d = O.dtw(dist)
+    for b in range(4):
+        _, _, cmin, _ = brute_force(dist[b], 1.0)
+        assert abs(d[b] - cmin) < 1e-12
+
+
+@pytest.mark.parametrize("gamma", [1e-3, 1e-2, 0.1, 1.0])
+def test_gamma_sandwich(O, gamma):
+    rng = np.random.default_rng(5)
+    dist = _rand_dist(rng, 3, 40, 31)
+    sd, _ = O.forward(dist, gamma, keep_R=False)
+    hard = O.dtw(dist)
+    lnp = log_delannoy(39, 30)
+    assert (sd <= hard + 1e-9).all()
+    assert (sd >= hard - gamma * lnp - 1e-9).all()
+
+
+# --- gradients ---------------------------------------------------------------------
+
+def test_E_is_dloss_ddist_finite_differences(O):
+    rng = np.random.default_rng(9)
+    dist = _rand_dist(rng, 1, 5, 6)
+    gamma = 0.6
+    _, R = O.forward(dist, gamma)
+    E = O.backward(dist, R, gamma)
+    h = 1e-6
+    for i in range(5):
+        for j in range(6):
+            dp = dist.copy()
+            dm = dist.copy()
+            dp[0, i, j] += h
+            dm[0, i, j] -= h
+            fd = (O.forward(dp, gamma)[0][0] - O.forward(dm, gamma)[0][0]) / (2 * h)
+            assert abs(fd - E[0, i, j]) < 1e-7
+
+
+def test_gradients_finite_differences(O):
+    # Inputs on a 2^-8 grid so x +- 2^-8 stays exact in fp32.
+    g = torch.Generator().manual_seed(4)
+    x = (torch.randint(-400, 400, (2, 4, 3), generator=g).float() / 256).numpy()
+    y = (torch.randint(-400, 400, (2, 5, 3), generator=g).float() / 256).numpy()
+    gamma = 0.8
+    gl = np.array([0.25, -1.5])
+    loss, gx, gy = O.value_and_grad(x, y, gamma, gl, round_dist_f32=False)
+    h = 2.0 ** -8
+
+    def L(xx, yy):
+        return (O.value_and_grad(xx, yy, gamma, gl, False)[0] * gl).sum()
+
+    for arr, grad in ((x, gx), (y, gy)):
+        for idx in np.ndindex(arr.shape):
+            p = arr.copy()
+            m = arr.copy()
+            p[idx] += h
+            m[idx] -= h
+            if arr is x:
+                fd = (L(p, y) - L(m, y)) / (2 * h)
+            else:
+                fd = (L(x, p) - L(x, m)) / (2 * h)
+            assert abs(fd - grad[idx]) < 2e-4 * max(1.0, abs(grad[idx]))
+
+
+def test_chain_rule_against_cdist_vjp(O):
+    # dL/dx via autograd of torch's fp64 cdist(...)**2 contracted with E.
+    x, y = pair_batch(2, 6, 8, 4, seed=12)
+    E = np.random.default_rng(1).random((2, 6, 8))
+    gl = np.array([0.5, 2.0])
+    gx, gy = O.sqeuclid_vjp(x.numpy(), y.numpy(), E, gl)
+    xt = x.double().requires_grad_()
+    yt = y.double().requires_grad_()
+    d = torch.cdist(xt, yt) ** 2
+    (d * torch.from_numpy(E) * torch.from_numpy(gl)[:, None, None]).sum().backward()
+    np.testing.assert_allclose(gx, xt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(gy, yt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_translation_invariance_of_gradients(O):
+    x, y = pair_batch(3, 30, 17, 6, seed=3)
+    _, gx, gy = O.value_and_grad(x.numpy(), y.numpy(), 0.5)
+    s = gx.sum(axis=1) + gy.sum(axis=1)
+    assert np.abs(s).max() < 1e-12 * max(1.0, np.abs(gx).max())
+
+
+# --- invariants --------------------------------------------------------------------
+
+def test_symmetry(O):
+    x, y = pair_batch(2, 19, 27, 4, seed=6)
+    l1, gx1, gy1 = O.value_and_grad(x.numpy(), y.numpy(), 0.3)
+    l2, gx2, gy2 = O.value_and_grad(y.numpy(), x.numpy(), 0.3)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12)
+    np.testing.assert_allclose(gx1, gy2, rtol=1e-9, atol=1e-13)
+    np.testing.assert_allclose(gy1, gx2, rtol=1e-9, atol=1e-13)
+
+
+def test_reversal(O):
+    x, y = pair_batch(2, 23, 14, 3, seed=8)
+    xr = np.ascontiguousarray(x.numpy()[:, ::-1])
+    yr = np.ascontiguousarray(y.numpy()[:, ::-1])
+    l1, _, _, E1 = O.value_and_grad(x.numpy(), y.numpy(), 0.7, want_E=True)
+    l2, _, _, E2 = O.value_and_grad(xr, yr, 0.7, want_E=True)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12)
+    np.testing.assert_allclose(E1, E2[:, ::-1, ::-1], rtol=1e-8, atol=1e-12)
+
+
+def test_power_of_two_scale_covariance(O):
+    x, y = pair_batch(2, 21, 18, 5, seed=10)
+    l1, gx1, gy1 = O.value_and_grad(x.numpy(), y.numpy(), 0.25, round_dist_f32=False)
+    l2, gx2, gy2 = O.value_and_grad(2 * x.numpy(), 2 * y.numpy(), 1.0, round_dist_f32=False)
+    np.testing.assert_array_equal(l2, 4 * l1)
+    np.testing.assert_allclose(gx2, 2 * gx1, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(gy2, 2 * gy1, rtol=1e-12, atol=1e-15)
+
+
+def test_E_structure(O):
+    x, y = pair_batch(2, 41, 29, 4, seed=13)
+    _, _, _, E = O.value_and_grad(x.numpy(), y.numpy(), 0.5, want_E=True)
+    N, M = 41, 29
+    assert np.allclose(E[:, 0, 0], 1) and np.allclose(E[:, -1, -1], 1)
+    assert (E >= 0).all() and (E <= 1 + 1e-12).all()
+    assert (E.sum(axis=2) >= 1 - 1e-9).all() and (E.sum(axis=1) >= 1 - 1e-9).all()
+    tot = E.sum(axis=(1, 2))
+    assert (tot >= max(N, M) - 1e-9).all() and (tot <= N + M - 1 + 1e-9).all()
+
+
+def test_normalized_self_is_zero(O):
+    x, _ = pair_batch(2, 15, 15, 3, seed=14)
+    xn = x.numpy()
+    loss, gx, gy = O.normalized_value_and_grad(xn, xn.copy(), 1.0)
+    np.testing.assert_array_equal(loss, 0.0)
+    assert np.abs(gx).max() < 1e-12 and np.abs(gy).max() < 1e-12
+    with pytest.raises(ValueError):
+        O.normalized_value_and_grad(xn, xn[:, :10].copy(), 1.0)
+
+
+def test_normalized_matches_composition(O):
+    x, y = pair_batch(2, 12, 12, 2, seed=15)
+    xn, yn = x.numpy(), y.numpy()
+    loss, _, _ = O.normalized_value_and_grad(xn, yn, 0.9)
+    lxy = O.value_and_grad(xn, yn, 0.9)[0]
+    lxx = O.value_and_grad(xn, xn, 0.9)[0]
+    lyy = O.value_and_grad(yn, yn, 0.9)[0]
+    np.testing.assert_allclose(loss, lxy - 0.5 * (lxx + lyy), rtol=1e-14)
+
+
+def test_small_gamma_is_finite(O):
+    x, y = pair_batch(2, 300, 170, 8, seed=16)
+    loss, gx, gy = O.value_and_grad(x.numpy(), y.numpy(), 0.01)
+    assert np.isfinite(loss).all() and np.isfinite(gx).all() and np.isfinite(gy).all()
+
+
+# --- Adam and the barycenter ----------------------------------------------------------
+
+def test_adam_matches_torch_optim(O):
+    rng = np.random.default_rng(2)
+    A = rng.standard_normal((6, 6))
+    Q = A @ A.T + np.eye(6)
+    b = rng.standard_normal(6)
+    p = rng.standard_normal(6)
+    pt = torch.tensor(p.copy(), requires_grad=True)
+    opt = torch.optim.Adam([pt], lr=0.1)
+    st = O.adam_init(p.shape)
+    for _ in range(25):
+        g = Q @ p - b
+        O.adam_step(p, g, st, 0.1)
+        opt.zero_grad()
+        (0.5 * pt @ torch.from_numpy(Q) @ pt - torch.from_numpy(b) @ pt).backward()
+        opt.step()
+    np.testing.assert_allclose(p, pt.detach().numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_barycenter_decreases_objective(O):
+    X = block_waves(4, 30, 2, seed=0).numpy()
+    z, hist = O.barycenter(X, gamma=1.0, max_iter=15, lr=0.1)
+    assert z.shape == (30, 2)
+    assert hist[-1] < hist[0]
+
+
+def test_block_waves_recipe():
+    X = block_waves(10, 100, 3, seed=0)
+    assert X.shape == (10, 100, 3) and X.dtype == torch.float32
+    s = torch.sign(X)
+    # square wave of period 50: half the samples high, half low per channel
+    frac = (s > 0).float().mean(dim=1)
+    assert ((frac > 0.35) & (frac < 0.65)).all()
+    resid = X - torch.where(X > 0, 1.0, -1.0)
+    assert 0.07 < resid.std().item() < 0.13
