@@ -1,0 +1,102 @@
+"""ctypes binding of libsdtw.so: the C ABI of include/sdtw.h, same names.
+
+Argument marshalling only -- every step of the computation runs in the HIP
+kernels behind these calls.  Pointers are passed as integers (device
+addresses), streams as integers (hipStream_t handles, 0 = null stream).
+If the library is not built this module raises at first use; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsdtw.so")
+
+SDTW_OK = 0
+SDTW_ERR_INVALID_ARG = 1
+SDTW_ERR_WORKSPACE = 2
+SDTW_ERR_HIP = 3
+SDTW_ERR_UNSUPPORTED = 4
+
+SDTW_MODE_UNFUSED = 0
+SDTW_MODE_FUSED = 1
+
+# (name, restype, argtypes) for every entry point declared in include/sdtw.h.
+_I64 = ctypes.c_int64
+_P = ctypes.c_void_p
+_F = ctypes.c_float
+_I = ctypes.c_int
+SIGNATURES = {
+    "sdtw_abi_version": (_I, []),
+    "sdtw_status_string": (ctypes.c_char_p, [_I]),
+    "sdtw_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, _I]),
+    "sdtw_dist": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "sdtw_forward": (_I, [_P, _P, _I64, _I64, _I64, _I64, _F, _I, _P,
+                          ctypes.c_size_t, _P, _P]),
+    "sdtw_backward": (_I, [_P, _P, _I64, _I64, _I64, _I64, _F, _I, _P,
+                           ctypes.c_size_t, _P, _P, _P, _P, _P]),
+}
+
+_lib = None
+
+
+class SdtwError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sdtw_status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built: run `python -m "
+                "differentiable_series_alignment_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def sdtw_abi_version() -> int:
+    return lib().sdtw_abi_version()
+
+
+def sdtw_status_string(status: int) -> str:
+    return lib().sdtw_status_string(int(status)).decode()
+
+
+def sdtw_workspace_bytes(B: int, N: int, M: int, D: int, mode: int) -> int:
+    return int(lib().sdtw_workspace_bytes(B, N, M, D, mode))
+
+
+def sdtw_dist(x: int, y: int, dist: int, B: int, N: int, M: int, D: int,
+              stream: int = 0) -> int:
+    return lib().sdtw_dist(x, y, dist, B, N, M, D, stream)
+
+
+def sdtw_forward(x: int, y: int, B: int, N: int, M: int, D: int, gamma: float,
+                 mode: int, workspace: int, workspace_bytes: int, loss: int,
+                 stream: int = 0) -> int:
+    return lib().sdtw_forward(x, y, B, N, M, D, gamma, mode, workspace,
+                              workspace_bytes, loss, stream)
+
+
+def sdtw_backward(x: int, y: int, B: int, N: int, M: int, D: int, gamma: float,
+                  mode: int, workspace: int, workspace_bytes: int, grad_loss: int,
+                  grad_x: int | None, grad_y: int | None, align: int | None,
+                  stream: int = 0) -> int:
+    return lib().sdtw_backward(x, y, B, N, M, D, gamma, mode, workspace,
+                               workspace_bytes, grad_loss, grad_x, grad_y, align,
+                               stream)
+
+
+def check(status: int, where: str) -> None:
+    if status != SDTW_OK:
+        raise SdtwError(status, where)

@@ -1,0 +1,173 @@
+// C ABI of the gfx950 Soft-DTW library: argument validation, workspace
+// layout and kernel sequencing.  Declarations and contracts: include/sdtw.h.
+#include <math.h>
+#include <string.h>
+
+#include "sdtw.h"
+#include "sdtw_kernels.h"
+
+namespace {
+
+using sdtw::DPArgs;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Private workspace layout.  Every region starts on a 256-byte boundary.
+struct Layout {
+  int64_t nbands = 0, nseg = 0;
+  size_t ctrl = 0, ctrl_words = 0;  // u32 ticket + per-segment progress
+  size_t loss64 = 0;                // fp64 [B]
+  size_t H = 0;                     // fp64 [B, nseg, M]
+  size_t R = 0;                     // fp64 [B, N, M]
+  size_t dist = 0;                  // fp32 [B, N, M] (unfused only)
+  size_t total = 0;
+};
+
+bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool sizes_ok(int64_t B, int64_t N, int64_t M, int64_t D) {
+  if (B < 1 || N < 1 || M < 1 || D < 1) return false;
+  if (B > 65535) return false;                 // grid-dimension limit
+  if (N > (int64_t(1) << 31) || M > (int64_t(1) << 31) || D > (int64_t(1) << 24))
+    return false;
+  size_t nm, bnm, bytes;
+  if (!mul_ok((size_t)N, (size_t)M, &nm)) return false;
+  if (!mul_ok(nm, (size_t)B, &bnm)) return false;
+  if (!mul_ok(bnm, 16, &bytes)) return false;  // R + Dist + slack
+  return bytes < (SIZE_MAX >> 2);
+}
+
+bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L) {
+  (void)D;
+  if (!sizes_ok(B, N, M, D) || (mode != SDTW_MODE_UNFUSED && mode != SDTW_MODE_FUSED))
+    return false;
+  L->nbands = (N + 63) / 64;
+  L->nseg = (L->nbands + sdtw::kBandsPerWG - 1) / sdtw::kBandsPerWG;
+  size_t off = 0;
+  L->ctrl = off;
+  L->ctrl_words = 1 + (size_t)B * (size_t)L->nseg;
+  off += align_up(L->ctrl_words * 4);
+  L->loss64 = off;
+  off += align_up((size_t)B * 8);
+  L->H = off;
+  off += align_up((size_t)B * (size_t)L->nseg * (size_t)M * 8);
+  L->R = off;
+  off += align_up((size_t)B * (size_t)N * (size_t)M * 8);
+  if (mode == SDTW_MODE_UNFUSED) {
+    L->dist = off;
+    off += align_up((size_t)B * (size_t)N * (size_t)M * 4);
+  }
+  L->total = off;
+  return true;
+}
+
+bool gamma_ok(float g) { return isfinite(g) && g > 0.f; }
+
+DPArgs dp_args(const Layout& L, char* ws, const float* x, const float* y,
+               int64_t B, int64_t N, int64_t M, int64_t D, float gamma) {
+  DPArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.y = y;
+  a.ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl);
+  a.loss64 = reinterpret_cast<double*>(ws + L.loss64);
+  a.H = reinterpret_cast<double*>(ws + L.H);
+  a.R = reinterpret_cast<double*>(ws + L.R);
+  a.dist = L.dist ? reinterpret_cast<const float*>(ws + L.dist) : nullptr;
+  a.N = N;
+  a.M = M;
+  a.D = D;
+  a.B = (int)B;
+  a.nbands = (int)L.nbands;
+  a.nseg = (int)L.nseg;
+  const double g = (double)gamma;
+  a.k2 = M_LOG2E / g;
+  a.g_ln2 = g * M_LN2;
+  return a;
+}
+
+int check_ws(const Layout& L, void* ws, size_t bytes) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return SDTW_ERR_INVALID_ARG;
+  if (bytes < L.total) return SDTW_ERR_WORKSPACE;
+  return SDTW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdtw_abi_version(void) { return SDTW_ABI_VERSION; }
+
+const char* sdtw_status_string(int status) {
+  switch (status) {
+    case SDTW_OK: return "ok";
+    case SDTW_ERR_INVALID_ARG: return "invalid argument";
+    case SDTW_ERR_WORKSPACE: return "workspace too small";
+    case SDTW_ERR_HIP: return "HIP runtime error";
+    case SDTW_ERR_UNSUPPORTED: return "unsupported request";
+    default: return "unknown status";
+  }
+}
+
+size_t sdtw_workspace_bytes(int64_t B, int64_t N, int64_t M, int64_t D, int mode) {
+  Layout L;
+  if (!make_layout(B, N, M, D, mode, &L)) return 0;
+  return L.total;
+}
+
+int sdtw_dist(const float* x, const float* y, float* dist, int64_t B, int64_t N,
+              int64_t M, int64_t D, void* stream) {
+  if (!x || !y || !dist || !sizes_ok(B, N, M, D)) return SDTW_ERR_INVALID_ARG;
+  hipError_t e = sdtw::launch_dist(x, y, dist, B, N, M, D, (hipStream_t)stream);
+  return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
+}
+
+int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M,
+                 int64_t D, float gamma, int mode, void* workspace,
+                 size_t workspace_bytes, float* loss, void* stream) {
+  if (!x || !y || !loss || !gamma_ok(gamma)) return SDTW_ERR_INVALID_ARG;
+  Layout L;
+  if (!make_layout(B, N, M, D, mode, &L)) return SDTW_ERR_INVALID_ARG;
+  int st = check_ws(L, workspace, workspace_bytes);
+  if (st != SDTW_OK) return st;
+  if (mode == SDTW_MODE_FUSED) return SDTW_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma);
+  a.loss = loss;
+  hipError_t e = sdtw::launch_zero_u32(a.ctrl, (int64_t)L.ctrl_words, s);
+  if (e == hipSuccess)
+    e = sdtw::launch_dist(x, y, reinterpret_cast<float*>(ws + L.dist), B, N, M, D, s);
+  if (e == hipSuccess) e = sdtw::launch_dp(a, false, false, s);
+  return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
+}
+
+int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t M,
+                  int64_t D, float gamma, int mode, void* workspace,
+                  size_t workspace_bytes, const float* grad_loss, float* grad_x,
+                  float* grad_y, float* align, void* stream) {
+  if (!x || !y || !grad_loss || !gamma_ok(gamma)) return SDTW_ERR_INVALID_ARG;
+  Layout L;
+  if (!make_layout(B, N, M, D, mode, &L)) return SDTW_ERR_INVALID_ARG;
+  int st = check_ws(L, workspace, workspace_bytes);
+  if (st != SDTW_OK) return st;
+  if (mode == SDTW_MODE_FUSED) return SDTW_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma);
+  float* E = align ? align : reinterpret_cast<float*>(ws + L.dist);
+  a.E = E;
+  hipError_t e = sdtw::launch_zero_u32(a.ctrl, (int64_t)L.ctrl_words, s);
+  if (e == hipSuccess) e = sdtw::launch_dp(a, true, false, s);
+  if (e == hipSuccess && (grad_x || grad_y))
+    e = sdtw::launch_chain(E, x, y, grad_loss, grad_x, grad_y, B, N, M, D, s);
+  return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+"""PyTorch-facing Soft-DTW on the gfx950 library (libsdtw.so).
+
+API of the README "SoftDTW-CUDA (PyTorch + Numba)": ``SoftDTW(gamma=1.0,
+dist="sqeuclidean", fused=False, normalize=False)`` called as
+``loss_fn(x, y)`` -> (B,) ("Usage", "Fused Mode", "Normalization") and
+``softdtw_barycenter(sequences, gamma, max_iter, lr, fused)`` -> (N, D)
+("Time Series Barycenters").  PyTorch provides device memory, streams and
+autograd; every Soft-DTW step runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib as L
+
+
+def _stream(device: torch.device) -> int:
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _validate(x: torch.Tensor, y: torch.Tensor, gamma: float):
+    """Input checks of the README's test list ("Tests": gamma, device, empty
+    sequences, shape mismatches)."""
+    if not isinstance(x, torch.Tensor) or not isinstance(y, torch.Tensor):
+        raise ValueError("x and y must be tensors")
+    g = float(gamma)
+    if not math.isfinite(g) or g <= 0.0:
+        raise ValueError(f"gamma must be finite and > 0, got {gamma}")
+    if x.dim() != 3 or y.dim() != 3:
+        raise ValueError(f"x and y must be (B, N, D) and (B, M, D); got {tuple(x.shape)} and {tuple(y.shape)}")
+    if x.shape[0] != y.shape[0]:
+        raise ValueError(f"batch sizes differ: {x.shape[0]} vs {y.shape[0]}")
+    if x.shape[2] != y.shape[2]:
+        raise ValueError(f"feature dimensions differ: {x.shape[2]} vs {y.shape[2]}")
+    if min(x.shape) < 1 or min(y.shape) < 1:
+        raise ValueError("empty sequences or batch are not supported")
+    if x.dtype != torch.float32 or y.dtype != torch.float32:
+        raise ValueError("x and y must be float32")
+    if x.device.type != "cuda" or y.device.type != "cuda":
+        raise ValueError("x and y must be on a GPU (there is no CPU path)")
+    if x.device != y.device:
+        raise ValueError(f"x and y are on different devices: {x.device} vs {y.device}")
+
+
+def _workspace(B, N, M, D, mode, device):
+    nbytes = L.sdtw_workspace_bytes(B, N, M, D, mode)
+    if nbytes == 0:
+        raise ValueError(f"unsupported sizes B={B} N={N} M={M} D={D}")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("workspace is not 256-byte aligned")
+    return ws
+
+
+class _SoftDTWFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, y, gamma, mode):
+        x = x.contiguous()
+        y = y.contiguous()
+        B, N, D = x.shape
+        M = y.shape[1]
+        with torch.cuda.device(x.device):
+            ws = _workspace(B, N, M, D, mode, x.device)
+            loss = torch.empty(B, dtype=torch.float32, device=x.device)
+            L.check(L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, gamma,
+                                   mode, ws.data_ptr(), ws.numel(), loss.data_ptr(),
+                                   _stream(x.device)), "sdtw_forward")
+        ctx.save_for_backward(x, y)
+        ctx.ws = ws
+        ctx.gamma = gamma
+        ctx.mode = mode
+        ctx.consumed = False
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        x, y = ctx.saved_tensors
+        B, N, D = x.shape
+        M = y.shape[1]
+        need_x, need_y = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        gx = torch.empty_like(x) if need_x else None
+        gy = torch.empty_like(y) if need_y else None
+        gl = grad_loss.contiguous().to(torch.float32)
+        ws = ctx.ws
+        s = _stream(x.device)
+        with torch.cuda.device(x.device):
+            if ctx.consumed and ctx.mode == L.SDTW_MODE_UNFUSED:
+                # A second backward (retain_graph): the unfused backward
+                # replaced the distances in the workspace, so rebuild them.
+                scratch = torch.empty(B, dtype=torch.float32, device=x.device)
+                L.check(L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, ctx.gamma,
+                                       ctx.mode, ws.data_ptr(), ws.numel(),
+                                       scratch.data_ptr(), s), "sdtw_forward")
+            L.check(L.sdtw_backward(x.data_ptr(), y.data_ptr(), B, N, M, D, ctx.gamma,
+                                    ctx.mode, ws.data_ptr(), ws.numel(), gl.data_ptr(),
+                                    gx.data_ptr() if gx is not None else None,
+                                    gy.data_ptr() if gy is not None else None,
+                                    None, s), "sdtw_backward")
+        ctx.consumed = True
+        return gx, gy, None, None
+
+
+def soft_dtw(x: torch.Tensor, y: torch.Tensor, gamma: float = 1.0,
+             fused: bool = False) -> torch.Tensor:
+    """Per-pair Soft-DTW loss (B,) with autograd support."""
+    _validate(x, y, gamma)
+    mode = L.SDTW_MODE_FUSED if fused else L.SDTW_MODE_UNFUSED
+    return _SoftDTWFunction.apply(x, y, float(gamma), mode)
+
+
+class SoftDTW(torch.nn.Module):
+    """``SoftDTW(gamma=1.0, dist="sqeuclidean", fused=False, normalize=False)``.
+
+    ``normalize=True`` returns SoftDTW(x,y) - (SoftDTW(x,x) + SoftDTW(y,y))/2
+    and requires x.shape == y.shape (README "Normalization")."""
+
+    def __init__(self, gamma: float = 1.0, dist: str = "sqeuclidean",
+                 fused: bool = False, normalize: bool = False):
+        super().__init__()
+        if dist != "sqeuclidean":
+            raise ValueError(f"only dist='sqeuclidean' is supported, got {dist!r}")
+        g = float(gamma)
+        if not math.isfinite(g) or g <= 0.0:
+            raise ValueError(f"gamma must be finite and > 0, got {gamma}")
+        self.gamma = g
+        self.dist = dist
+        self.fused = bool(fused)
+        self.normalize = bool(normalize)
+
+    def forward(self, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+        if self.normalize:
+            if tuple(x.shape) != tuple(y.shape):
+                raise ValueError("normalize=True requires x.shape == y.shape")
+            _validate(x, y, self.gamma)
+            xy = soft_dtw(x, y, self.gamma, self.fused)
+            xx = soft_dtw(x, x, self.gamma, self.fused)
+            yy = soft_dtw(y, y, self.gamma, self.fused)
+            return xy - 0.5 * (xx + yy)
+        return soft_dtw(x, y, self.gamma, self.fused)
+
+    def extra_repr(self) -> str:
+        return (f"gamma={self.gamma}, dist={self.dist!r}, fused={self.fused}, "
+                f"normalize={self.normalize}")
+
+
+def sqeuclidean(x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+    """The (B, N, M) fp32 squared-Euclidean distance tensor of the unfused
+    mode, computed by the library's distance kernel."""
+    _validate(x, y, 1.0)
+    x = x.contiguous()
+    y = y.contiguous()
+    B, N, D = x.shape
+    M = y.shape[1]
+    out = torch.empty((B, N, M), dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        L.check(L.sdtw_dist(x.data_ptr(), y.data_ptr(), out.data_ptr(), B, N, M, D,
+                            _stream(x.device)), "sdtw_dist")
+    return out
+
+
+def alignment(x: torch.Tensor, y: torch.Tensor, gamma: float = 1.0,
+              fused: bool = False):
+    """(loss[B], E[B,N,M]): the loss and the alignment matrix dloss/dDist."""
+    _validate(x, y, gamma)
+    x = x.contiguous()
+    y = y.contiguous()
+    B, N, D = x.shape
+    M = y.shape[1]
+    mode = L.SDTW_MODE_FUSED if fused else L.SDTW_MODE_UNFUSED
+    s = _stream(x.device)
+    with torch.cuda.device(x.device):
+        ws = _workspace(B, N, M, D, mode, x.device)
+        loss = torch.empty(B, dtype=torch.float32, device=x.device)
+        E = torch.empty((B, N, M), dtype=torch.float32, device=x.device)
+        gl = torch.ones(B, dtype=torch.float32, device=x.device)
+        L.check(L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, float(gamma), mode,
+                               ws.data_ptr(), ws.numel(), loss.data_ptr(), s), "sdtw_forward")
+        L.check(L.sdtw_backward(x.data_ptr(), y.data_ptr(), B, N, M, D, float(gamma), mode,
+                                ws.data_ptr(), ws.numel(), gl.data_ptr(), None, None,
+                                E.data_ptr(), s), "sdtw_backward")
+    return loss, E
+
+
+def softdtw_barycenter(sequences: torch.Tensor, gamma: float = 1.0,
+                       max_iter: int = 100, lr: float = 0.1, fused: bool = False,
+                       return_history: bool = False):
+    """Soft-DTW barycenter of K sequences (K, N, D) by Adam (README "Time
+    Series Barycenters"; review page, "Proposed method").  The iterate starts
+    at the pointwise mean and minimises mean_k SoftDTW(z, X_k)."""
+    if sequences.dim() != 3:
+        raise ValueError("sequences must be (K, N, D)")
+    X = sequences.detach().contiguous()
+    z = X.mean(dim=0).clone().requires_grad_(True)
+    opt = torch.optim.Adam([z], lr=lr)
+    loss_fn = SoftDTW(gamma=gamma, fused=fused)
+    hist = []
+    for _ in range(int(max_iter)):
+        opt.zero_grad(set_to_none=True)
+        loss = loss_fn(z.unsqueeze(0).expand_as(X), X).mean()
+        loss.backward()
+        opt.step()
+        if return_history:
+            hist.append(loss.detach())
+    z = z.detach()
+    if return_history:
+        return z, torch.stack(hist).cpu() if hist else torch.empty(0)
+    return z

@@ -1,0 +1,113 @@
+/*
+ * sdtw.h -- C ABI of the MI355X (gfx950) Soft-DTW library (libsdtw.so).
+ *
+ * Operation.  Soft-DTW (Cuturi & Blondel, ICML 2017; credited in the
+ * "Acknowledgments" of the README "SoftDTW-CUDA (PyTorch + Numba)") between
+ * x[b] (N x D) and y[b] (M x D) for every pair b of a batch:
+ *
+ *   Dist[b,i,j] = ||x[b,i,:] - y[b,j,:]||^2            (squared Euclidean)
+ *   R[0,0] = 0,  R[i,0] = R[0,j] = +inf,
+ *   R[i,j] = Dist[b,i-1,j-1] + softmin_g(R[i-1,j-1], R[i-1,j], R[i,j-1]),
+ *   softmin_g(a) = -g log sum_k exp(-a_k/g),        loss[b] = R[N,M].
+ *
+ * The gradient is the alignment matrix E = dloss/dDist, obtained by a
+ * log-space backward recursion with the exponential taken at the end (review
+ * page "SoftDTW-CUDA-Torch: Memory-Efficient GPU-Accelerated Soft Dynamic Time
+ * Warping for PyTorch", section "Proposed method"), pushed through Dist:
+ *   dx[b,i] = 2 gl[b] sum_j E[i,j] (x_i - y_j),
+ *   dy[b,j] = 2 gl[b] sum_i E[i,j] (y_j - x_i).
+ *
+ * Modes (README "Usage": unfused = explicit distance tensor; "Fused Mode" = no
+ * distance tensor; "Limitations": fused supports squared Euclidean only):
+ *   SDTW_MODE_UNFUSED  materialises Dist (fp32, B x N x M) in the workspace;
+ *                      the backward overwrites it with E.
+ *   SDTW_MODE_FUSED    recomputes distances from x and y inside the dynamic
+ *                      programme; no B x N x M distance or E tensor exists.
+ * Both modes keep the forward DP state (fp64, B x N x M) for the backward.
+ * Distances are accumulated in fp64 and rounded once to fp32 in both modes,
+ * so fused and unfused see identical distances.
+ *
+ * Conventions for every entry point:
+ *  - x is [B,N,D], y is [B,M,D], fp32, row-major and contiguous, in device
+ *    memory; every other array argument is a device pointer too.
+ *  - B, N, M, D >= 1 (the README's "empty sequences" are rejected); lengths
+ *    are unbounded apart from memory; products such as B*N*M must fit int64.
+ *  - gamma must be finite and > 0.
+ *  - All work is enqueued on `stream` (a hipStream_t; 0 = the null stream)
+ *    without host synchronisation.  Arguments are validated on the host before
+ *    any HIP call; invalid calls return an error and enqueue nothing.  Faults
+ *    inside kernels surface at the caller's next synchronisation.
+ *  - The library never allocates device memory and keeps no global mutable
+ *    state; the caller owns every buffer.  Calls on distinct workspaces may
+ *    run concurrently on distinct streams.  Nothing is printed.
+ */
+#ifndef SDTW_H
+#define SDTW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDTW_ABI_VERSION 1
+
+typedef enum {
+    SDTW_OK = 0,
+    SDTW_ERR_INVALID_ARG = 1, /* bad size, gamma, pointer or mode          */
+    SDTW_ERR_WORKSPACE = 2,   /* workspace_bytes below sdtw_workspace_bytes */
+    SDTW_ERR_HIP = 3,         /* a HIP runtime call or launch failed        */
+    SDTW_ERR_UNSUPPORTED = 4  /* request outside what the library supports  */
+} sdtw_status_t;
+
+typedef enum {
+    SDTW_MODE_UNFUSED = 0,
+    SDTW_MODE_FUSED = 1
+} sdtw_mode_t;
+
+/* Version of this ABI (SDTW_ABI_VERSION). */
+int sdtw_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *sdtw_status_string(int status);
+
+/* Bytes of device workspace that sdtw_forward / sdtw_backward need for this
+ * problem and mode (a multiple of 256; the pointer must be 256-byte aligned).
+ * Returns 0 for invalid sizes or mode.  Layout is private to the library. */
+size_t sdtw_workspace_bytes(int64_t B, int64_t N, int64_t M, int64_t D,
+                            int mode);
+
+/* Squared Euclidean distances dist[b,i,j] = ||x[b,i]-y[b,j]||^2 (fp32,
+ * [B,N,M] row-major, caller-allocated), accumulated in fp64 and rounded once
+ * (README "Usage", unfused mode's explicit distance computation; "Notes":
+ * never negative). */
+int sdtw_dist(const float *x, const float *y, float *dist, int64_t B,
+              int64_t N, int64_t M, int64_t D, void *stream);
+
+/* Forward pass: loss[b] = Soft-DTW(x[b], y[b]) (fp32, [B]).  Leaves in the
+ * workspace what sdtw_backward needs (README "Usage": loss_fn(x, y) returns a
+ * per-pair loss).  Soft-DTW can be negative (README "Notes"). */
+int sdtw_forward(const float *x, const float *y, int64_t B, int64_t N,
+                 int64_t M, int64_t D, float gamma, int mode, void *workspace,
+                 size_t workspace_bytes, float *loss, void *stream);
+
+/* Backward pass for upstream gradients grad_loss[b] (fp32, [B]); the
+ * workspace must be as sdtw_forward left it for the same arguments.
+ * grad_x ([B,N,D]) and grad_y ([B,M,D]) are written (not accumulated); either
+ * may be NULL to skip it.  align ([B,N,M] fp32), if not NULL, receives E
+ * (unfused mode only; SDTW_ERR_UNSUPPORTED in fused mode).  In unfused mode
+ * the distance tensor in the workspace is replaced by E, so a second
+ * sdtw_backward on the same workspace needs sdtw_forward to run again first;
+ * in fused mode the workspace is left unchanged and the backward may be
+ * repeated. */
+int sdtw_backward(const float *x, const float *y, int64_t B, int64_t N,
+                  int64_t M, int64_t D, float gamma, int mode, void *workspace,
+                  size_t workspace_bytes, const float *grad_loss,
+                  float *grad_x, float *grad_y, float *align, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDTW_H */

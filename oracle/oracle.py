@@ -235,14 +235,16 @@ def barycenter_objective_and_grad(z, X, gamma: float, round_dist_f32: bool = Tru
 
 
 def barycenter(X, gamma: float = 1.0, max_iter: int = 100, lr: float = 0.1,
-               round_dist_f32: bool = True):
-    """Adam on mean_k SoftDTW(z, X_k), z initialised to the pointwise mean.
+               round_dist_f32: bool = True, z0=None):
+    """Adam on mean_k SoftDTW(z, X_k), z initialised to the pointwise mean
+    (or to ``z0`` when given).
 
     Reading: the iterate is kept in fp32 between steps (the sequences are
     fp32 and the objective is evaluated on fp32 inputs); the Adam update
     itself is fp64.  Returns (z, objective history)."""
     X = _f32(X)
-    z = X.astype(np.float64).mean(axis=0)
+    z = (X.astype(np.float64).mean(axis=0) if z0 is None
+         else np.asarray(z0, dtype=np.float64).copy())
     st = adam_init(z.shape)
     hist = []
     for _ in range(max_iter):

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/sdtw.h, and rejects invalid calls on the host before any
+HIP call (README "SoftDTW-CUDA (PyTorch + Numba)", "Tests": validation of
+gamma, device, empty sequences and shape mismatches)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from differentiable_series_alignment_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdtw.h")
+FAKE = 1 << 20  # a non-null address that must never be dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdtw_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(L.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert L.sdtw_abi_version() == 1
+
+
+def test_status_strings():
+    for st in range(0, 6):
+        s = L.sdtw_status_string(st)
+        assert isinstance(s, str) and s
+    assert L.sdtw_status_string(L.SDTW_OK) == "ok"
+
+
+def test_workspace_bytes():
+    a = L.sdtw_workspace_bytes(32, 512, 512, 64, L.SDTW_MODE_UNFUSED)
+    b = L.sdtw_workspace_bytes(32, 512, 512, 64, L.SDTW_MODE_FUSED)
+    cells = 32 * 512 * 512
+    assert a % 256 == 0 and b % 256 == 0
+    assert a >= cells * 12 and b >= cells * 8 and b < a
+    for bad in [(0, 4, 4, 1), (1, 0, 4, 1), (1, 4, 0, 1), (1, 4, 4, 0), (-1, 4, 4, 1)]:
+        assert L.sdtw_workspace_bytes(*bad, L.SDTW_MODE_UNFUSED) == 0
+    assert L.sdtw_workspace_bytes(1, 4, 4, 1, 7) == 0
+
+
+def _fwd(**kw):
+    a = dict(x=FAKE, y=FAKE, B=2, N=4, M=5, D=3, gamma=1.0, mode=0,
+             workspace=FAKE * 256, workspace_bytes=1 << 30, loss=FAKE, stream=0)
+    a.update(kw)
+    return L.sdtw_forward(**a)
+
+
+def _bwd(**kw):
+    a = dict(x=FAKE, y=FAKE, B=2, N=4, M=5, D=3, gamma=1.0, mode=0,
+             workspace=FAKE * 256, workspace_bytes=1 << 30, grad_loss=FAKE,
+             grad_x=FAKE, grad_y=FAKE, align=None, stream=0)
+    a.update(kw)
+    return L.sdtw_backward(**a)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(gamma=0.0), dict(gamma=-1.0), dict(gamma=float("nan")), dict(gamma=float("inf")),
+    dict(B=0), dict(N=0), dict(M=0), dict(D=0), dict(N=-3),
+    dict(x=None), dict(y=None), dict(mode=2), dict(workspace=None),
+    dict(workspace=FAKE * 256 + 8),
+])
+def test_forward_backward_reject_invalid(kw):
+    if "loss" not in kw:
+        assert _fwd(**kw) == L.SDTW_ERR_INVALID_ARG
+    assert _bwd(**kw) == L.SDTW_ERR_INVALID_ARG
+
+
+def test_null_outputs_rejected():
+    assert _fwd(loss=None) == L.SDTW_ERR_INVALID_ARG
+    assert _bwd(grad_loss=None) == L.SDTW_ERR_INVALID_ARG
+
+
+def test_small_workspace_rejected():
+    need = L.sdtw_workspace_bytes(2, 4, 5, 3, 0)
+    assert _fwd(workspace_bytes=need - 1) == L.SDTW_ERR_WORKSPACE
+    assert _bwd(workspace_bytes=need - 256) == L.SDTW_ERR_WORKSPACE
+
+
+def test_dist_rejects_invalid():
+    assert L.sdtw_dist(None, FAKE, FAKE, 1, 2, 2, 2) == L.SDTW_ERR_INVALID_ARG
+    assert L.sdtw_dist(FAKE, FAKE, None, 1, 2, 2, 2) == L.SDTW_ERR_INVALID_ARG
+    assert L.sdtw_dist(FAKE, FAKE, FAKE, 1, 0, 2, 2) == L.SDTW_ERR_INVALID_ARG
+
+
+# --- Python layer ---------------------------------------------------------------
+
+def test_python_layer_validation_on_cpu():
+    from differentiable_series_alignment_amd import SoftDTW, soft_dtw
+    x = torch.randn(2, 5, 3)
+    y = torch.randn(2, 6, 3)
+    with pytest.raises(ValueError, match="GPU"):
+        soft_dtw(x, y)                                  # no CPU path
+    with pytest.raises(ValueError, match="sqeuclidean"):
+        SoftDTW(dist="euclidean")
+    with pytest.raises(ValueError, match="gamma"):
+        SoftDTW(gamma=0.0)
+    with pytest.raises(ValueError, match="gamma"):
+        soft_dtw(x, y, gamma=-1.0)
+    with pytest.raises(ValueError, match="batch"):
+        soft_dtw(x, torch.randn(3, 6, 3))
+    with pytest.raises(ValueError, match="feature"):
+        soft_dtw(x, torch.randn(2, 6, 4))
+    with pytest.raises(ValueError, match="empty"):
+        soft_dtw(x, torch.randn(2, 0, 3))
+    with pytest.raises(ValueError, match="float32"):
+        soft_dtw(x.double(), y.double())
+    with pytest.raises(ValueError, match="shape"):
+        SoftDTW(normalize=True)(x, y)
+    with pytest.raises(ValueError):
+        soft_dtw(x[0], y[0])                            # not 3-D
