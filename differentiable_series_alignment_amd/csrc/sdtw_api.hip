@@ -15,13 +15,14 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Private workspace layout.  Every region starts on a 256-byte boundary.
+// The cell arrays use the band-step layout of sdtw_kernels.h.
 struct Layout {
-  int64_t nbands = 0, nseg = 0;
+  int64_t nbands = 0, nseg = 0, S = 0;
   size_t ctrl = 0, ctrl_words = 0;  // u32 ticket + per-segment progress
   size_t loss64 = 0;                // fp64 [B]
   size_t H = 0;                     // fp64 [B, nseg, M]
-  size_t R = 0;                     // fp64 [B, N, M]
-  size_t dist = 0;                  // fp32 [B, N, M] (unfused only)
+  size_t R = 0;                     // fp64 band-step forward state
+  size_t dist = 0;                  // fp32 band-step distances / E (unfused)
   size_t total = 0;
 };
 
@@ -39,7 +40,7 @@ bool sizes_ok(int64_t B, int64_t N, int64_t M, int64_t D) {
   size_t nm, bnm, bytes;
   if (!mul_ok((size_t)N, (size_t)M, &nm)) return false;
   if (!mul_ok(nm, (size_t)B, &bnm)) return false;
-  if (!mul_ok(bnm, 16, &bytes)) return false;  // R + Dist + slack
+  if (!mul_ok(bnm, 64, &bytes)) return false;  // R + Dist + padding, generously
   return bytes < (SIZE_MAX >> 2);
 }
 
@@ -49,6 +50,8 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
     return false;
   L->nbands = (N + 63) / 64;
   L->nseg = (L->nbands + sdtw::kBandsPerWG - 1) / sdtw::kBandsPerWG;
+  L->S = sdtw::skew_steps(M);
+  const size_t cells = (size_t)B * (size_t)L->nbands * (size_t)L->S * 64;
   size_t off = 0;
   L->ctrl = off;
   L->ctrl_words = 1 + (size_t)B * (size_t)L->nseg;
@@ -58,10 +61,10 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   L->H = off;
   off += align_up((size_t)B * (size_t)L->nseg * (size_t)M * 8);
   L->R = off;
-  off += align_up((size_t)B * (size_t)N * (size_t)M * 8);
+  off += align_up(cells * 8);
   if (mode == SDTW_MODE_UNFUSED) {
     L->dist = off;
-    off += align_up((size_t)B * (size_t)N * (size_t)M * 4);
+    off += align_up(cells * 4);
   }
   L->total = off;
   return true;
@@ -79,8 +82,9 @@ DPArgs dp_args(const Layout& L, char* ws, const float* x, const float* y,
   a.loss64 = reinterpret_cast<double*>(ws + L.loss64);
   a.H = reinterpret_cast<double*>(ws + L.H);
   a.R = reinterpret_cast<double*>(ws + L.R);
-  a.dist = L.dist ? reinterpret_cast<const float*>(ws + L.dist) : nullptr;
+  a.dsk = L.dist ? reinterpret_cast<float*>(ws + L.dist) : nullptr;
   a.N = N;
+  a.S = L.S;
   a.M = M;
   a.D = D;
   a.B = (int)B;
@@ -142,8 +146,7 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
   DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma);
   a.loss = loss;
   hipError_t e = sdtw::launch_zero_u32(a.ctrl, (int64_t)L.ctrl_words, s);
-  if (e == hipSuccess)
-    e = sdtw::launch_dist(x, y, reinterpret_cast<float*>(ws + L.dist), B, N, M, D, s);
+  if (e == hipSuccess) e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, s);
   if (e == hipSuccess) e = sdtw::launch_dp(a, false, false, s);
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
 }
@@ -161,12 +164,11 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
   DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma);
-  float* E = align ? align : reinterpret_cast<float*>(ws + L.dist);
-  a.E = E;
   hipError_t e = sdtw::launch_zero_u32(a.ctrl, (int64_t)L.ctrl_words, s);
   if (e == hipSuccess) e = sdtw::launch_dp(a, true, false, s);
+  if (e == hipSuccess && align) e = sdtw::launch_unskew(a.dsk, align, B, N, M, L.S, s);
   if (e == hipSuccess && (grad_x || grad_y))
-    e = sdtw::launch_chain(E, x, y, grad_loss, grad_x, grad_y, B, N, M, D, s);
+    e = sdtw::launch_chain(a.dsk, x, y, grad_loss, grad_x, grad_y, B, N, M, D, L.S, s);
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
 }
 

@@ -6,122 +6,274 @@
 // i.e. two batched contractions E.Y and E^T.X (README "SoftDTW-CUDA (PyTorch +
 // Numba)", "Usage": gradients of loss_fn(x, y).mean() reach x and y).
 //
-// One wave owns 32 output rows and all of D (up to 256 columns per pass, as
-// 32x32 tiles of v_mfma_f32_32x32x2_f32 accumulated over the contraction
-// index K in steps of 2).  Operand lanes: A[r][k] in lane r + 32k, B[k][c] in
-// lane c + 32k; accumulator element (8*(e/4) + 4*(l/32) + e%4, l%32) in lane
-// l, register e.  Step s contracts k = s (lanes 0..31) and k = s + Kh (lanes
-// 32..63), Kh = ceil(K/2), so each lane walks one contiguous half of K.
+// E arrives in the band-step layout of the dynamic programme (see
+// sdtw_kernels.h).  A workgroup stages a window of band steps in an LDS ring
+// (coalesced: one step is 64 consecutive floats) and feeds
+// v_mfma_f32_32x32x2_f32 from it.  Operand lanes: A[r][k] in lane r + 32k,
+// B[k][c] in lane c + 32k; accumulator element (8*(e/4) + 4*(l/32) + e%4,
+// l%32) in lane l, register e.  Ring rows are padded to 65 floats so both
+// access patterns below hit distinct LDS banks.
 #include "sdtw_device.h"
 #include "sdtw_kernels.h"
 
 namespace sdtw {
 
-// ROLE 0: rows i, out = dx, own = x, other = y, A[r][k] = E[i0+r][k].
-// ROLE 1: rows j, out = dy, own = y, other = x, A[r][k] = E[k][j0+r].
-template <int ROLE, int NT>
-__device__ __forceinline__ void chain_wave(const float* __restrict__ Eb,
-                                           const float* __restrict__ own,
-                                           const float* __restrict__ other,
-                                           float* __restrict__ out, float g2,
-                                           int64_t rows, int64_t K, int64_t D,
-                                           int64_t ldE, int64_t r0, int64_t d0) {
-  const int l = lane_id();
-  const int rl = l & 31, hk = l >> 5;
-  const int64_t Kh = (K + 1) / 2;
-  const int64_t row = r0 + rl;
-  const bool row_ok = row < rows;
-  v16f acc[NT];
+constexpr int kRingSteps = 128;
+constexpr int kRingPitch = 65;
+
+// Copy band steps [s0, s0 + 32) (relative to the band's first column step)
+// between global memory, registers and the LDS ring; 256 threads x 8 floats.
+struct Stage32 {
+  float v[8];
+  __device__ __forceinline__ void load(const float* bandp, int64_t s0, int64_t smax) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+    for (int k = 0; k < 2; ++k) {
+      const int e = (int)threadIdx.x * 4 + 1024 * k;
+      int64_t st = s0 + e / 64;
+      st = st < smax ? st : smax - 1;
+      const v4f q = *reinterpret_cast<const v4f*>(bandp + st * 64 + (e & 63));
+      v[4 * k + 0] = q[0];
+      v[4 * k + 1] = q[1];
+      v[4 * k + 2] = q[2];
+      v[4 * k + 3] = q[3];
+    }
+  }
+  __device__ __forceinline__ void store(float* ring, int64_t s0) const {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = (int)threadIdx.x * 4 + 1024 * k;
+      const int slot = (int)((s0 + e / 64) & (kRingSteps - 1));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ring[slot * kRingPitch + (e & 63) + q] = v[4 * k + q];
+    }
+  }
+};
+
+// dx for one band (64 rows) of one pair, columns of D in [d0, d0 + 128).
+// Wave w: row tile w & 1, d tiles (w >> 1) + 2t.  Column blocks of 32 need
+// band steps [j0, j0 + 96); the next block's 32 new steps are fetched into
+// registers while the current block computes.
+template <int NTW>
+__global__ __launch_bounds__(256) void k_chain_rows(const float* __restrict__ esk,
+                                                    const float* __restrict__ x,
+                                                    const float* __restrict__ y,
+                                                    const float* __restrict__ gl,
+                                                    float* __restrict__ gx, int64_t N,
+                                                    int64_t M, int64_t D, int64_t S,
+                                                    int nbands, int64_t d0) {
+  __shared__ float ring[kRingSteps * kRingPitch];
+  const int64_t b = blockIdx.y, band = blockIdx.x;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int r = l & 31, h = l >> 5;
+  const int rt = w & 1, dsel = w >> 1;
+  const int lr = 32 * rt + r;
+  const int64_t row = band * 64 + lr;
+  const bool row_ok = row < N;
+  const float* bandp = esk + ((b * nbands + band) * S + kSkewOff) * 64;
+  const int64_t smax = S - kSkewOff;
+  const float* yb = y + b * M * D;
+  int64_t dcol[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int64_t dc = d0 + 32 * (dsel + 2 * t) + r;
+    dcol[t] = dc < D ? dc : D - 1;
+  }
+  v16f acc[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
   float rsum = 0.f;
-  int64_t dcol[NT];
-  bool dok[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    dcol[t] = d0 + 32 * t + rl;
-    dok[t] = dcol[t] < D;
+
+  const int64_t nblk = (M + 31) / 32;
+  Stage32 st;
+  for (int64_t s0 = 0; s0 < 96; s0 += 32) {
+    st.load(bandp, s0, smax);
+    st.store(ring, s0);
   }
-  for (int64_t s = 0; s < Kh; ++s) {
-    const int64_t k = s + hk * Kh;
-    const bool kok = k < K;
-    float av = 0.f;
-    if (kok && row_ok) av = (ROLE == 0) ? Eb[row * ldE + k] : Eb[k * ldE + row];
-    rsum += av;
-    const float* orow = other + (kok ? k : 0) * D;
+  float yv[16][NTW], yn[16][NTW];
+  auto load_y = [&](int64_t j0, float (&Y)[16][NTW]) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float bv = (kok && dok[t]) ? orow[dcol[t]] : 0.f;
-      acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[t], 0, 0, 0);
+    for (int s = 0; s < 16; ++s) {
+      int64_t j = j0 + 2 * s + h;
+      j = j < M ? j : M - 1;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) Y[s][t] = yb[j * D + dcol[t]];
     }
+  };
+  load_y(0, yv);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int64_t kb = 0; kb < nblk; ++kb) {
+    const int64_t j0 = kb * 32;
+    const bool more = kb + 1 < nblk;
+    if (more) {
+      st.load(bandp, j0 + 96, smax);
+      load_y(j0 + 32, yn);
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int64_t j = j0 + 2 * s + h;
+      const float a =
+          (row_ok && j < M) ? ring[(int)((j + lr) & (kRingSteps - 1)) * kRingPitch + lr] : 0.f;
+      rsum += a;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, yv[s][t], acc[t], 0, 0, 0);
+    }
+    __syncthreads();
+    if (more) {
+      st.store(ring, j0 + 96);
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) yv[s][t] = yn[s][t];
+    }
+    __syncthreads();
   }
+
   rsum += __shfl_xor(rsum, 32, 64);
-  // Row sums of the accumulator rows this lane holds (all lanes shuffle).
   float rs[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) rs[e] = __shfl(rsum, 8 * (e >> 2) + 4 * hk + (e & 3), 64);
+  for (int e = 0; e < 16; ++e) rs[e] = __shfl(rsum, 8 * (e >> 2) + 4 * h + (e & 3), 64);
+  const float g2 = 2.f * gl[b];
+  const float* xb = x + b * N * D;
+  float* ob = gx + b * N * D;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int t = 0; t < NTW; ++t) {
+    const int64_t dc = d0 + 32 * (dsel + 2 * t) + r;
+    if (dc >= D || dc >= d0 + 128) continue;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int64_t orw = r0 + 8 * (e >> 2) + 4 * hk + (e & 3);
-      if (dok[t] && orw < rows) {
-        const float ov = own[orw * D + dcol[t]];
-        out[orw * D + dcol[t]] = g2 * (rs[e] * ov - acc[t][e]);
-      }
+      const int64_t orow = band * 64 + 32 * rt + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (orow < N) ob[orow * D + dc] = g2 * (rs[e] * xb[orow * D + dc] - acc[t][e]);
     }
   }
 }
 
-template <int NT>
-__global__ __launch_bounds__(256) void k_chain(const float* __restrict__ E,
-                                               const float* __restrict__ x,
-                                               const float* __restrict__ y,
-                                               const float* __restrict__ gl,
-                                               float* __restrict__ gx,
-                                               float* __restrict__ gy,
-                                               int64_t N, int64_t M, int64_t D,
-                                               int xblocks, int64_t d0) {
-  const int w = threadIdx.x >> 6;
-  const int64_t b = blockIdx.y;
+// dy for 64 columns of one pair, columns of D in [d0, d0 + 128), summing over
+// every band.  Wave w: column tile w & 1, d tiles (w >> 1) + 2t.  The band's
+// window of steps [j0, j0 + 128) is fetched into registers one band ahead.
+template <int NTW>
+__global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ esk,
+                                                    const float* __restrict__ x,
+                                                    const float* __restrict__ y,
+                                                    const float* __restrict__ gl,
+                                                    float* __restrict__ gy, int64_t N,
+                                                    int64_t M, int64_t D, int64_t S,
+                                                    int nbands, int64_t d0) {
+  __shared__ float ring[kRingSteps * kRingPitch];
+  const int64_t b = blockIdx.y, j0 = (int64_t)blockIdx.x * 64;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int r = l & 31, h = l >> 5;
+  const int ct = w & 1, dsel = w >> 1;
+  const int jl = 32 * ct + r;
+  const bool col_ok = j0 + jl < M;
+  const int64_t smax = S - kSkewOff;
+  const float* xb = x + b * N * D;
+  int64_t dcol[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int64_t dc = d0 + 32 * (dsel + 2 * t) + r;
+    dcol[t] = dc < D ? dc : D - 1;
+  }
+  v16f acc[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+  float csum = 0.f;
+
+  Stage32 win[4], nxt[4];
+  float xv[32][NTW], xn[32][NTW];
+  auto load_band = [&](int64_t band, Stage32 (&Wn)[4], float (&X)[32][NTW]) {
+    const float* bandp = esk + ((b * nbands + band) * S + kSkewOff) * 64;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) Wn[k].load(bandp, j0 + 32 * k, smax);
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      int64_t rr = band * 64 + 2 * s + h;
+      rr = rr < N ? rr : N - 1;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) X[s][t] = xb[rr * D + dcol[t]];
+    }
+  };
+  load_band(0, win, xv);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  for (int64_t band = 0; band < nbands; ++band) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) win[k].store(ring, 32 * k);
+    __syncthreads();
+    const bool more = band + 1 < nbands;
+    if (more) load_band(band + 1, nxt, xn);
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const int lr = 2 * s + h;
+      const bool ok = col_ok && band * 64 + lr < N;
+      const float a = ok ? ring[(jl + lr) * kRingPitch + lr] : 0.f;
+      csum += a;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xv[s][t], acc[t], 0, 0, 0);
+    }
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) win[k] = nxt[k];
+#pragma unroll
+      for (int s = 0; s < 32; ++s)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) xv[s][t] = xn[s][t];
+    }
+  }
+
+  csum += __shfl_xor(csum, 32, 64);
+  float cs[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) cs[e] = __shfl(csum, 8 * (e >> 2) + 4 * h + (e & 3), 64);
   const float g2 = 2.f * gl[b];
-  const float* Eb = E + b * N * M;
-  if ((int)blockIdx.x < xblocks) {
-    if (!gx) return;
-    const int64_t r0 = ((int64_t)blockIdx.x * 4 + w) * 32;
-    if (r0 >= N) return;
-    chain_wave<0, NT>(Eb, x + b * N * D, y + b * M * D, gx + b * N * D, g2, N,
-                      M, D, M, r0, d0);
-  } else {
-    if (!gy) return;
-    const int64_t r0 = ((int64_t)(blockIdx.x - xblocks) * 4 + w) * 32;
-    if (r0 >= M) return;
-    chain_wave<1, NT>(Eb, y + b * M * D, x + b * N * D, gy + b * M * D, g2, M,
-                      N, D, M, r0, d0);
+  const float* yb = y + b * M * D;
+  float* ob = gy + b * M * D;
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int64_t dc = d0 + 32 * (dsel + 2 * t) + r;
+    if (dc >= D || dc >= d0 + 128) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t oj = j0 + 32 * ct + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (oj < M) ob[oj * D + dc] = g2 * (cs[e] * yb[oj * D + dc] - acc[t][e]);
+    }
   }
 }
 
-hipError_t launch_chain(const float* E, const float* x, const float* y,
+hipError_t launch_chain(const float* esk, const float* x, const float* y,
                         const float* gl, float* gx, float* gy, int64_t B,
-                        int64_t N, int64_t M, int64_t D, hipStream_t s) {
-  const int xblocks = (int)((N + 127) / 128);
-  const int yblocks = (int)((M + 127) / 128);
-  dim3 grid((unsigned)(xblocks + yblocks), (unsigned)B);
-  for (int64_t d0 = 0; d0 < D; d0 += 256) {
-    const int64_t dw = D - d0 < 256 ? D - d0 : 256;
-    const int nt = (int)((dw + 31) / 32);
-    if (nt <= 1)
-      hipLaunchKernelGGL(k_chain<1>, grid, dim3(256), 0, s, E, x, y, gl, gx, gy, N, M, D, xblocks, d0);
-    else if (nt <= 2)
-      hipLaunchKernelGGL(k_chain<2>, grid, dim3(256), 0, s, E, x, y, gl, gx, gy, N, M, D, xblocks, d0);
-    else if (nt <= 4)
-      hipLaunchKernelGGL(k_chain<4>, grid, dim3(256), 0, s, E, x, y, gl, gx, gy, N, M, D, xblocks, d0);
-    else
-      hipLaunchKernelGGL(k_chain<8>, grid, dim3(256), 0, s, E, x, y, gl, gx, gy, N, M, D, xblocks, d0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                        int64_t N, int64_t M, int64_t D, int64_t S,
+                        hipStream_t s) {
+  const int nb = (int)((N + 63) / 64);
+  for (int64_t d0 = 0; d0 < D; d0 += 128) {
+    const int64_t dw = D - d0 < 128 ? D - d0 : 128;
+    const bool two = dw > 64;  // more than two 32-wide d tiles
+    if (gx) {
+      dim3 grid((unsigned)nb, (unsigned)B);
+      if (two)
+        hipLaunchKernelGGL(k_chain_rows<2>, grid, dim3(256), 0, s, esk, x, y, gl, gx, N, M, D, S, nb, d0);
+      else
+        hipLaunchKernelGGL(k_chain_rows<1>, grid, dim3(256), 0, s, esk, x, y, gl, gx, N, M, D, S, nb, d0);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (gy) {
+      dim3 grid((unsigned)((M + 63) / 64), (unsigned)B);
+      if (two)
+        hipLaunchKernelGGL(k_chain_cols<2>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0);
+      else
+        hipLaunchKernelGGL(k_chain_cols<1>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

@@ -31,20 +31,33 @@ __device__ __forceinline__ double wave_shr1(double v, double fill) {
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// One soft-min step of the recurrence in fp64 state with fp32
-// transcendentals:  softmin_g(a,b,c) = m - g*ln(sum_k exp(-(a_k - m)/g)),
-// m = min(a,b,c).  `k2` = log2(e)/g, `g_ln2` = g*ln(2); returns d + softmin.
-// Infinite inputs contribute exp2(-inf) = 0; the result is garbage only when
-// all three are +inf, which callers mask.
-__device__ __forceinline__ double softmin_cell(double a, double b, double c,
-                                               double d, double k2,
-                                               double g_ln2) {
-  double m = fmin(fmin(a, c), b);
-  float ea = hw_exp2((float)((m - a) * k2));
-  float eb = hw_exp2((float)((m - b) * k2));
-  float ec = hw_exp2((float)((m - c) * k2));
-  float s = (ea + ec) + eb;
-  return fma(-g_ln2, (double)hw_log2(s), m + d);
+// Stand-in for +inf in the DP state: far above any reachable state value
+// (the state stays finite, so no inf - inf can ever produce a NaN) yet small
+// enough that sums of a few hundred of them stay finite.
+constexpr double kBig = 1e290;
+
+// v_min_f64 on values known to be non-NaN (the generic fmin would first
+// quiet possible signalling NaNs, which costs two extra instructions on the
+// dependency chain of every step).
+__device__ __forceinline__ double min_nonan(double a, double b) {
+  double r;
+  asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// One cell of the recurrence in base-2 units X = R * log2(e) / g:
+//   X = d + m - log2(2^(m-a) + 2^(m-b) + 2^(m-c)),  m = min(a, b, c),
+// which is R = D + softmin_g(...) scaled by log2(e)/g.  State and
+// differences are fp64; the exponentials and the logarithm are the fp32
+// hardware instructions applied to the (small) fp64 differences.
+__device__ __forceinline__ double softmin2_cell(double a, double b, double c,
+                                                double d) {
+  const double m = min_nonan(min_nonan(a, c), b);
+  const float ea = hw_exp2((float)(m - a));
+  const float eb = hw_exp2((float)(m - b));
+  const float ec = hw_exp2((float)(m - c));
+  const float s = (ea + ec) + eb;
+  return (m + d) - (double)hw_log2(s);
 }
 
 __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }

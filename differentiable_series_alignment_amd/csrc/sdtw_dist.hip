@@ -11,35 +11,47 @@
 // Work split: a 256-thread workgroup owns a 64x64 block of (i,j) for one
 // pair; each wave owns a 32x32 quarter as 2x2 tiles of
 // v_mfma_f64_16x16x4_f64.  Operand lanes: A[r][k] sits in lane r + 16k,
-// B[k][c] in lane c + 16k; the accumulator's element (4*(l/16)+e, l%16) sits
-// in lane l, register e.  The contraction index k of step s is d = 4s + k.
+// B[k][c] in lane c + 16k; the accumulator's element (4*e + l/16, l%16) sits
+// in lane l, register e (checked on the hardware).  The contraction index k of step s is d = 4s + k.
 #include "sdtw_device.h"
 #include "sdtw_kernels.h"
 
 namespace sdtw {
 
+// Finish one 16x16 accumulator tile: Dist = max(0, |x|^2 + |y|^2 - 2 x.y)
+// rounded once to fp32.  Plain output goes to out[row * ldo + col]; the
+// band-step output is staged in the workgroup's LDS tile first.
+template <bool SKEW>
 __device__ __forceinline__ void dist_tile_store(float* out, int64_t ldo,
                                                 int64_t i0, int64_t j0,
                                                 int64_t N, int64_t M,
                                                 const v4d& acc, double nx_l,
-                                                double ny_l) {
+                                                double ny_l, float* tile,
+                                                int ti, int tj) {
   const int l = lane_id();
   const int col = l & 15;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int row = 4 * (l >> 4) + e;
+    const int row = 4 * e + (l >> 4);
     const double nx_row = __shfl(nx_l, row, 64);
     double v = nx_row + ny_l - 2.0 * acc[e];
     v = v > 0.0 ? v : 0.0;
-    const int64_t gi = i0 + row, gj = j0 + col;
-    if (gi < N && gj < M) out[gi * ldo + gj] = (float)v;
+    if (SKEW) {
+      tile[(ti + row) * 64 + tj + col] = (float)v;
+    } else {
+      const int64_t gi = i0 + row, gj = j0 + col;
+      if (gi < N && gj < M) out[gi * ldo + gj] = (float)v;
+    }
   }
 }
 
+template <bool SKEW>
 __global__ __launch_bounds__(256) void k_dist(const float* __restrict__ x,
                                               const float* __restrict__ y,
                                               float* __restrict__ dist,
-                                              int64_t N, int64_t M, int64_t D) {
+                                              int64_t N, int64_t M, int64_t D,
+                                              int64_t S) {
+  __shared__ float tile[SKEW ? 64 * 64 : 1];
   const int l = lane_id();
   const int w = threadIdx.x >> 6;
   const int64_t b = blockIdx.z;
@@ -61,22 +73,58 @@ __global__ __launch_bounds__(256) void k_dist(const float* __restrict__ x,
   v4d acc00 = {0, 0, 0, 0}, acc01 = acc00, acc10 = acc00, acc11 = acc00;
   double nxa0 = 0, nxa1 = 0, nyb0 = 0, nyb1 = 0;
   const int64_t steps = (D + 3) / 4;
-#pragma unroll 4
-  for (int64_t s = 0; s < steps; ++s) {
-    const int64_t d = 4 * s + kk;
-    const bool vd = d < D;
-    const double a0 = (vd && va0) ? (double)pa0[d] : 0.0;
-    const double a1 = (vd && va1) ? (double)pa1[d] : 0.0;
-    const double b0 = (vd && vb0) ? (double)pb0[d] : 0.0;
-    const double b1 = (vd && vb1) ? (double)pb1[d] : 0.0;
-    nxa0 = fma(a0, a0, nxa0);
-    nxa1 = fma(a1, a1, nxa1);
-    nyb0 = fma(b0, b0, nyb0);
-    nyb1 = fma(b1, b1, nyb1);
-    acc00 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc00, 0, 0, 0);
-    acc01 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc01, 0, 0, 0);
-    acc10 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc10, 0, 0, 0);
-    acc11 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc11, 0, 0, 0);
+  // Operands are loaded unconditionally at clamped addresses one block of
+  // KB steps ahead of the MFMAs and zeroed at use where d >= D or the
+  // row/column is outside the grid.
+  constexpr int KB = 8;
+  float c_a0[KB], c_a1[KB], c_b0[KB], c_b1[KB];
+  float n_a0[KB], n_a1[KB], n_b0[KB], n_b1[KB];
+  const int64_t nblk = (steps + KB - 1) / KB;
+  auto load_block = [&](int64_t blk, float (&A0)[KB], float (&A1)[KB],
+                        float (&B0)[KB], float (&B1)[KB]) {
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      int64_t d = 4 * (blk * KB + j) + kk;
+      d = d < D ? d : D - 1;
+      A0[j] = pa0[d];
+      A1[j] = pa1[d];
+      B0[j] = pb0[d];
+      B1[j] = pb1[d];
+    }
+  };
+  load_block(0, c_a0, c_a1, c_b0, c_b1);
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const bool more = blk + 1 < nblk;
+    if (more) load_block(blk + 1, n_a0, n_a1, n_b0, n_b1);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int64_t s = blk * KB + j;
+      if (s < steps) {  // wave-uniform
+        const bool vd = 4 * s + kk < D;
+        const double a0 = (vd && va0) ? (double)c_a0[j] : 0.0;
+        const double a1 = (vd && va1) ? (double)c_a1[j] : 0.0;
+        const double b0 = (vd && vb0) ? (double)c_b0[j] : 0.0;
+        const double b1 = (vd && vb1) ? (double)c_b1[j] : 0.0;
+        nxa0 = fma(a0, a0, nxa0);
+        nxa1 = fma(a1, a1, nxa1);
+        nyb0 = fma(b0, b0, nyb0);
+        nyb1 = fma(b1, b1, nyb1);
+        acc00 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc00, 0, 0, 0);
+        acc01 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc01, 0, 0, 0);
+        acc10 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc10, 0, 0, 0);
+        acc11 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc11, 0, 0, 0);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        c_a0[j] = n_a0[j];
+        c_a1[j] = n_a1[j];
+        c_b0[j] = n_b0[j];
+        c_b1[j] = n_b1[j];
+      }
+    }
   }
   // Complete the norms over the four k lane groups (lanes r, r+16, r+32, r+48).
   nxa0 += __shfl_xor(nxa0, 16, 64);
@@ -88,17 +136,59 @@ __global__ __launch_bounds__(256) void k_dist(const float* __restrict__ x,
   nyb1 += __shfl_xor(nyb1, 16, 64);
   nyb1 += __shfl_xor(nyb1, 32, 64);
 
-  float* ob = dist + b * N * M;
-  dist_tile_store(ob, M, i0, j0, N, M, acc00, nxa0, nyb0);
-  dist_tile_store(ob, M, i0, j0 + 16, N, M, acc01, nxa0, nyb1);
-  dist_tile_store(ob, M, i0 + 16, j0, N, M, acc10, nxa1, nyb0);
-  dist_tile_store(ob, M, i0 + 16, j0 + 16, N, M, acc11, nxa1, nyb1);
+  float* ob = dist + (SKEW ? 0 : b * N * M);
+  const int ti = (w >> 1) * 32, tj = (w & 1) * 32;
+  dist_tile_store<SKEW>(ob, M, i0, j0, N, M, acc00, nxa0, nyb0, tile, ti, tj);
+  dist_tile_store<SKEW>(ob, M, i0, j0 + 16, N, M, acc01, nxa0, nyb1, tile, ti, tj + 16);
+  dist_tile_store<SKEW>(ob, M, i0 + 16, j0, N, M, acc10, nxa1, nyb0, tile, ti + 16, tj);
+  dist_tile_store<SKEW>(ob, M, i0 + 16, j0 + 16, N, M, acc11, nxa1, nyb1, tile, ti + 16, tj + 16);
+  if (SKEW) {
+    // The 64x64 block (one band, columns c0..c0+63) covers steps
+    // c0+p, p = 0..126, of the band; lane l of step p holds column
+    // c0 + p - l.  Each store writes one step's contiguous lane run.
+    __syncthreads();
+    const int64_t band = blockIdx.y, c0 = (int64_t)blockIdx.x * 64;
+    const int64_t nb = gridDim.y;
+    float* bandp = dist + ((b * nb + band) * S + c0 + kSkewOff) * 64;
+    for (int p = w; p < 127; p += 4) {
+      const int cl = p - l;
+      if (cl >= 0 && cl < 64 && c0 + cl < M) bandp[(int64_t)p * 64 + l] = tile[l * 64 + cl];
+    }
+  }
 }
 
 hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
                        int64_t N, int64_t M, int64_t D, hipStream_t stream) {
   dim3 grid((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)B);
-  hipLaunchKernelGGL(k_dist, grid, dim3(256), 0, stream, x, y, dist, N, M, D);
+  hipLaunchKernelGGL(k_dist<false>, grid, dim3(256), 0, stream, x, y, dist, N, M, D,
+                     (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t B,
+                            int64_t N, int64_t M, int64_t D, int64_t S,
+                            hipStream_t stream) {
+  dim3 grid((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)B);
+  hipLaunchKernelGGL(k_dist<true>, grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S);
+  return hipGetLastError();
+}
+
+// Band-step E -> plain [B,N,M] (the optional alignment-matrix output).
+__global__ __launch_bounds__(256) void k_unskew(const float* __restrict__ esk,
+                                                float* __restrict__ out, int64_t N,
+                                                int64_t M, int64_t S, int nbands) {
+  const int64_t b = blockIdx.z;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= M) return;
+  for (int64_t r = blockIdx.y; r < N; r += gridDim.y)
+    out[(b * N + r) * M + c] = esk[skew_index(b, r, c, nbands, S)];
+}
+
+hipError_t launch_unskew(const float* esk, float* out, int64_t B, int64_t N,
+                         int64_t M, int64_t S, hipStream_t s) {
+  dim3 grid((unsigned)((M + 255) / 256), (unsigned)(N < 4096 ? N : 4096), (unsigned)B);
+  hipLaunchKernelGGL(k_unskew, grid, dim3(256), 0, s, esk, out, N, M, S,
+                     (int)((N + 63) / 64));
   return hipGetLastError();
 }
 

@@ -41,18 +41,75 @@ constexpr int kCH = 16;                      // steps per chunk
 constexpr int kLag = 2 + 62 / kCH;           // chunks between adjacent bands
 constexpr int kRing = 128;                   // LDS ring columns per boundary
 constexpr int kPub = 4;                      // chunks between global publishes
-constexpr int kSlack = 64;                   // extra columns awaited at start
+constexpr int kSlack = 96;                   // extra columns awaited at start
 constexpr uint32_t kSpinCap = 1u << 25;      // polls before a wait gives up
 static_assert(kRing >= (kLag + 3) * kCH, "LDS ring too small");
+static_assert(kCH == 16, "band_chunk unrolls 16 steps");
 
 __global__ void k_zero_u32(unsigned* p, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
 }
 
-__global__ void k_zero_f32(float* p, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.f;
+// Per-lane view of one band of a band-step array: the element a sweep step t
+// touches is base[t * dir] (dir = +64 forward, -64 reverse).
+struct LaneCursor {
+  int64_t base;  // element index at t = 0
+  int64_t dir;
+};
+
+// Storage row of sweep row i: the forward sweep's rows are the original rows;
+// the reverse sweep's row i is original row N-1-i.  Sweep rows past the grid
+// (the padding of the last band) map onto the padding rows of storage, so
+// stores of padding cells never touch a real cell.
+__device__ __forceinline__ LaneCursor lane_cursor(bool rev, int64_t b, int64_t i,
+                                                  int lane, int64_t N, int64_t M,
+                                                  int nbands, int64_t S) {
+  LaneCursor c;
+  if (!rev) {
+    const int64_t r = i;  // lane == r % 64; cell (r, t - lane) is at step t + off
+    c.base = ((b * nbands + (r >> 6)) * S + kSkewOff) * 64 + (r & 63);
+    c.dir = 64;
+  } else {
+    const int64_t r = i < N ? N - 1 - i : i;
+    const int64_t l = r & 63;
+    // cell (r, M-1-(t-lane)) sits at step M-1-t+lane+l+off
+    c.base = ((b * nbands + (r >> 6)) * S + (M - 1 + lane + l + kSkewOff)) * 64 + l;
+    c.dir = -64;
+  }
+  return c;
+}
+
+// Sixteen steps of one band.  MASK: the chunk contains steps with column < 0
+// (only the first 64 steps do); those cells are the left boundary, +inf
+// except the corner R[-1,-1] = 0 handled through the initial state.
+template <bool REV, bool MASK>
+__device__ __forceinline__ void band_chunk(double& cur, double& up, const double (&top)[16],
+                                           const float (&dn)[16], const double (&rn)[16],
+                                           double (&bottom)[16], int64_t t0, int lane,
+                                           bool row_ok, double k2, double xnm,
+                                           float* __restrict__ dsk, double* __restrict__ rsk,
+                                           const LaneCursor& cu) {
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int64_t t = t0 + u;
+    const double d = row_ok ? (double)dn[u] * k2 : 0.0;
+    const double upn = wave_shr1(cur, top[u]);
+    const double diag = up;
+    up = upn;
+    double c = softmin2_cell(diag, upn, cur, d);
+    if (MASK) c = (t - lane < 0) ? kBig : c;
+    cur = c;
+    bottom[u] = c;
+    const int64_t e = cu.base + t * cu.dir;
+    if (!REV) {
+      rsk[e] = c;
+    } else {
+      // ln E = (R[N-1,M-1] + Dist - R - R') / g, i.e. in base-2 units
+      // log2 E = Xnm + d - X - X'; the exponential is taken last.
+      dsk[e] = hw_exp2((float)((xnm + d) - (rn[u] + c)));
+    }
+  }
 }
 
 template <bool REV>
@@ -69,15 +126,14 @@ __global__ __launch_bounds__(kBandsPerWG * 64) void k_dp_unfused(DPArgs a) {
   const int seg = (int)(ticket / (unsigned)a.B);
   const int b = (int)(ticket % (unsigned)a.B);
 
-  const int64_t N = a.N, M = a.M;
+  const int64_t N = a.N, M = a.M, S = a.S;
   const int band = seg * W + w;
   const int nb_seg = min(W, a.nbands - seg * W);
   const bool active = w < nb_seg;
-  const int64_t r0 = (int64_t)band * 64;
+  const int64_t r0 = (int64_t)(active ? band : 0) * 64;
   const int64_t i = r0 + lane;                        // sweep-space row
   const bool row_ok = active && i < N;
-  const int64_t orow = REV ? (N - 1 - (row_ok ? i : 0)) : (row_ok ? i : 0);
-  const int qcount = (int)((M + 63 + kCH - 1) / kCH);
+  const int qcount = (int)(sweep_steps(M) / kCH);
   const int qtot = qcount + kLag * (nb_seg - 1);
   const bool last_in_seg = (w == nb_seg - 1);
   const bool produce_global = active && last_in_seg && (seg + 1 < a.nseg);
@@ -88,85 +144,119 @@ __global__ __launch_bounds__(kBandsPerWG * 64) void k_dp_unfused(DPArgs a) {
   const double* Hin = a.H + ((int64_t)b * a.nseg + (seg > 0 ? seg - 1 : 0)) * M;
   double* Hout = a.H + ((int64_t)b * a.nseg + seg) * M;
 
-  const int64_t rowoff = ((int64_t)b * N + orow) * M;
-  const float* drow = a.dist + rowoff;
-  double* Rrow = a.R + rowoff;
-  float* Erow = REV ? a.E + rowoff : nullptr;
-  const double k2 = a.k2, g_ln2 = a.g_ln2;
-  const double rnm = REV ? a.loss64[b] : 0.0;
+  const LaneCursor cu = lane_cursor(REV, b, i, lane, N, M, a.nbands, S);
+  float* dsk = a.dsk;
+  double* rsk = a.R;
+  const double k2 = a.k2;
+  const double xnm = REV ? a.loss64[b] : 0.0;
 
-  double cur = kInf;
-  double up = (lane == 0 && r0 == 0) ? 0.0 : kInf;  // diagonal input of step 0
+  // Boundary: R[-1,-1] = 0 reaches the first row's first cell as the
+  // diagonal input of step 0 (lane 0 of band 0); all else is +inf.
+  double cur = kBig;
+  double up = (lane == 0 && r0 == 0) ? 0.0 : kBig;
   unsigned avail = 0;
+
+  // Position of the final cell (forward sweep): row N-1, column M-1.
+  const int64_t lastrow = N - 1;
+  const bool has_last = !REV && active && (lastrow >> 6) == band;
+  const int64_t tlast = M - 1 + (lastrow & 63);
+  const int qlast = (int)(tlast / kCH), ulast = (int)(tlast % kCH);
+
+  // Every global access below is unconditional (padding cells have storage)
+  // and the data of chunk q+1 is requested while chunk q computes, so memory
+  // latency stays off the per-step dependency chain.
+  float dn[kCH];
+  double rn[kCH];
+  double tn[kCH];  // raw top-row values from the segment above (masked at use)
+#define SDTW_LOAD_CHUNK(qq, D_, R_)                                       \
+  {                                                                       \
+    const int64_t t0n = (int64_t)(qq) * kCH;                              \
+    _Pragma("unroll") for (int u = 0; u < kCH; ++u) {                     \
+      const int64_t e = cu.base + (t0n + u) * cu.dir;                     \
+      D_[u] = dsk[e];                                                     \
+      if (REV) R_[u] = rsk[e];                                            \
+    }                                                                     \
+  }
+  // Wait (bounded) until the segment above has published `need` columns.
+  // The producer holds a smaller ticket and is running, so it publishes
+  // within one sweep; the cap only guarantees that every wave exits even if
+  // that ever failed (the result would be garbage, never a hang).
+#define SDTW_AWAIT(need_)                                                 \
+  {                                                                       \
+    const unsigned need = (unsigned)(need_);                              \
+    if (avail < need) {                                                   \
+      unsigned v = 0;                                                     \
+      for (uint32_t spin = 0; spin < kSpinCap; ++spin) {                  \
+        v = __hip_atomic_load(prog_in, __ATOMIC_ACQUIRE,                  \
+                              __HIP_MEMORY_SCOPE_AGENT);                  \
+        if (v >= need) break;                                             \
+        __builtin_amdgcn_s_sleep(2);                                      \
+      }                                                                   \
+      avail = v < need ? need : v;                                        \
+    }                                                                     \
+  }
+#define SDTW_LOAD_TOP(qq, T_)                                             \
+  {                                                                       \
+    const int64_t t0n = (int64_t)(qq) * kCH;                              \
+    _Pragma("unroll") for (int u = 0; u < kCH; ++u) {                     \
+      const int64_t col = t0n + u;                                        \
+      T_[u] = Hin[col < M ? col : M - 1];                                 \
+    }                                                                     \
+  }
+
+  if (active) SDTW_LOAD_CHUNK(0, dn, rn);
+  if (consume_global) {
+    SDTW_AWAIT(imin64(M, kCH + kSlack));
+    SDTW_LOAD_TOP(0, tn);
+  }
+  // Drain the first requests here, so that inside the loop the only loads
+  // in flight are the ones for the next chunk (the counter-based waits are
+  // then exact instead of covering those as well).
+  __builtin_amdgcn_s_waitcnt(0);
 
   for (int Q = 0; Q < qtot; ++Q) {
     const int q = Q - kLag * w;
     if (active && q >= 0 && q < qcount) {
       const int64_t t0 = (int64_t)q * kCH;
+      // Requests for chunk q+1 go out first, into fresh registers.
+      float dn2[kCH];
+      double rn2[kCH];
+      double tn2[kCH];
+      const bool more = q + 1 < qcount;
+      if (more) {
+        SDTW_LOAD_CHUNK(q + 1, dn2, rn2);
+        if (consume_global) {
+          SDTW_AWAIT(imin64(M, t0 + 2 * kCH));
+          SDTW_LOAD_TOP(q + 1, tn2);
+        }
+      }
       double top[kCH];
       if (r0 == 0) {
 #pragma unroll
-        for (int u = 0; u < kCH; ++u) top[u] = kInf;
+        for (int u = 0; u < kCH; ++u) top[u] = kBig;
       } else if (!consume_global) {
 #pragma unroll
         for (int u = 0; u < kCH; ++u) top[u] = ring[w - 1][(t0 + u) & (kRing - 1)];
       } else {
-        const unsigned need =
-            (unsigned)imin64(M, t0 + kCH + (q == 0 ? kSlack : 0));
-        if (avail < need) {
-          // Bounded wait: the producer holds a smaller ticket and is running,
-          // so it publishes within one segment's sweep; the cap only makes
-          // sure every wave exits even if that ever failed (the result would
-          // then be garbage, never a hang).
-          unsigned v = 0;
-          for (uint32_t spin = 0; spin < kSpinCap; ++spin) {
-            v = __hip_atomic_load(prog_in, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-            if (v >= need) break;
-            __builtin_amdgcn_s_sleep(2);
-          }
-          avail = v < need ? need : v;
-        }
 #pragma unroll
-        for (int u = 0; u < kCH; ++u) {
-          const int64_t col = t0 + u;
-          top[u] = col < M ? Hin[col] : kInf;
-        }
-      }
-
-      float dv[kCH];
-      double rv[kCH];
-#pragma unroll
-      for (int u = 0; u < kCH; ++u) {
-        const int64_t col = t0 + u - lane;
-        const bool ok = row_ok && col >= 0 && col < M;
-        const int64_t oc = REV ? (M - 1 - col) : col;
-        dv[u] = ok ? drow[oc] : 0.f;
-        if (REV) rv[u] = ok ? Rrow[oc] : 0.0;
+        for (int u = 0; u < kCH; ++u) top[u] = tn[u];
       }
 
       double bottom[kCH];
+      if (t0 < 64)
+        band_chunk<REV, true>(cur, up, top, dn, rn, bottom, t0, lane, row_ok, k2, xnm,
+                              dsk, rsk, cu);
+      else
+        band_chunk<REV, false>(cur, up, top, dn, rn, bottom, t0, lane, row_ok, k2, xnm,
+                               dsk, rsk, cu);
+
+      if (has_last && q == qlast) {
+        double v = 0.0;
 #pragma unroll
-      for (int u = 0; u < kCH; ++u) {
-        const int64_t col = t0 + u - lane;
-        const double upn = wave_shr1(cur, top[u]);
-        const double diag = up;
-        up = upn;
-        double c = softmin_cell(diag, upn, cur, (double)dv[u], k2, g_ln2);
-        c = col < 0 ? kInf : c;
-        cur = c;
-        bottom[u] = c;
-        const bool ok = row_ok && col >= 0 && col < M;
-        if (!REV) {
-          if (ok) {
-            Rrow[col] = c;
-            if (i == N - 1 && col == M - 1) {
-              a.loss64[b] = c;
-              a.loss[b] = (float)c;
-            }
-          }
-        } else if (ok) {
-          const double z = ((rnm + (double)dv[u]) - (rv[u] + c)) * k2;
-          Erow[M - 1 - col] = hw_exp2((float)z);
+        for (int u = 0; u < kCH; ++u) v = (u == ulast) ? bottom[u] : v;
+        if (lane == (int)(lastrow & 63)) {
+          a.loss64[b] = v;
+          a.loss[b] = (float)(v * a.g_ln2);
         }
       }
 
@@ -191,20 +281,26 @@ __global__ __launch_bounds__(kBandsPerWG * 64) void k_dp_unfused(DPArgs a) {
           }
         }
       }
+      // Rotate the prefetched chunk in; its loads were issued a chunk ago.
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < kCH; ++u) {
+          dn[u] = dn2[u];
+          if (REV) rn[u] = rn2[u];
+          if (consume_global) tn[u] = tn2[u];
+        }
+      }
     }
     __syncthreads();
   }
+#undef SDTW_LOAD_CHUNK
+#undef SDTW_AWAIT
+#undef SDTW_LOAD_TOP
 }
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

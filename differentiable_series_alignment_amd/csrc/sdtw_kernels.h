@@ -1,44 +1,75 @@
-// Launch wrappers of the gfx950 Soft-DTW kernels (host side, internal).
+// Launch wrappers and the private data layout of the gfx950 Soft-DTW kernels.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace sdtw {
 
-// Arguments of the wavefront dynamic-programme kernels.  Index spaces: the
-// forward sweep walks the grid from (0,0) to (N-1,M-1); the reverse sweep
-// walks it from (N-1,M-1) back to (0,0), i.e. the forward recurrence on both
-// sequences reversed.  "Rows" and "columns" below are in the sweep's own
-// space; arrays in memory are always in the original orientation.
+// ---------------------------------------------------------------------------
+// Band-step layout of the B x N x M cell arrays kept by the dynamic programme
+// (distances / alignment matrix in fp32, forward state in fp64).
+//
+// Rows are grouped in bands of 64 (the last one padded); inside a band the
+// cell (r, c) with lane l = r % 64 lives at step s = c + l + kSkewOff:
+//     index(b, r, c) = ((b * nbands + r / 64) * S + (c + l + kSkewOff)) * 64 + l
+// so the 64 cells one wavefront step touches (lane l at column t - l) are 64
+// consecutive elements.  The reverse sweep, whose lanes walk columns from the
+// right, reads the same steps with its lanes in reverse order.  S leaves room
+// for every step either sweep touches, padding included.
+// ---------------------------------------------------------------------------
+constexpr int64_t kSkewOff = 80;
+
+__host__ __device__ inline int64_t skew_steps(int64_t M) {
+  return ((M + 2 * kSkewOff + 46 + 15) / 16) * 16;   // >= M + 206
+}
+__host__ __device__ inline int64_t skew_index(int64_t b, int64_t r, int64_t c,
+                                              int64_t nbands, int64_t S) {
+  const int64_t l = r & 63;
+  return (((b * nbands + (r >> 6)) * S) + (c + l + kSkewOff)) * 64 + l;
+}
+// Steps a sweep runs per band: columns 0..M-1 for lanes 0..63, in chunks of 16.
+__host__ __device__ inline int64_t sweep_steps(int64_t M) {
+  return ((M + 63 + 15) / 16) * 16;
+}
+
+// Arguments of the wavefront dynamic-programme kernels.  The forward sweep
+// walks the grid from (0,0) to (N-1,M-1); the reverse sweep walks it from
+// (N-1,M-1) back to (0,0), i.e. the forward recurrence on both sequences
+// reversed.  All state is kept in base-2 units, X = R * log2(e) / gamma.
 struct DPArgs {
-  const float* dist;    // [B,N,M] fp32 distances (unfused) or nullptr
+  float* dsk;           // band-step distances (unfused); the reverse sweep
+                        // overwrites each cell with E
   const float* x;       // [B,N,D] (fused)
   const float* y;       // [B,M,D] (fused)
-  double* R;            // [B,N,M] fp64 forward state
-  float* E;             // reverse: [B,N,M] alignment output (may alias dist)
-  double* H;            // [B,nseg,M] fp64 bottom rows handed between segments
+  double* R;            // band-step forward state X
+  double* H;            // [B,nseg,M] X bottom rows handed between segments
   unsigned* ctrl;       // [0] ticket; [1 + b*nseg + s] columns published by segment s
-  double* loss64;       // [B] R[N,M] in fp64 (forward writes, reverse reads)
-  float* loss;          // [B] (forward)
+  double* loss64;       // [B] X[N-1,M-1] (forward writes, reverse reads)
+  float* loss;          // [B] loss in natural units (forward)
   const float* gl;      // [B] upstream gradients (fused reverse)
   float* gx;            // [B,N,D] (fused reverse)
-  float* gy;            // [B,M,D] (fused reverse, accumulated atomically)
-  int64_t N, M, D;
+  float* gy;            // [B,M,D] (fused reverse)
+  int64_t N, M, D, S;
   int B, nbands, nseg;
   double k2;            // log2(e) / gamma
-  double g_ln2;         // gamma * ln(2)
+  double g_ln2;         // gamma * ln(2) = 1 / k2
 };
 
 // Bands (64 rows each) per workgroup of the DP kernels.
 constexpr int kBandsPerWG = 4;
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
-hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
                        int64_t N, int64_t M, int64_t D, hipStream_t stream);
+hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t B,
+                            int64_t N, int64_t M, int64_t D, int64_t S,
+                            hipStream_t stream);
+hipError_t launch_unskew(const float* esk, float* out, int64_t B, int64_t N,
+                         int64_t M, int64_t S, hipStream_t s);
 hipError_t launch_dp(const DPArgs& a, bool reverse, bool fused, hipStream_t s);
-hipError_t launch_chain(const float* E, const float* x, const float* y,
+hipError_t launch_chain(const float* esk, const float* x, const float* y,
                         const float* gl, float* gx, float* gy, int64_t B,
-                        int64_t N, int64_t M, int64_t D, hipStream_t s);
+                        int64_t N, int64_t M, int64_t D, int64_t S,
+                        hipStream_t s);
 
 }  // namespace sdtw
