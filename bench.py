@@ -1,0 +1,193 @@
+"""Soft-DTW forward+backward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload (the headline configuration): B=32 pairs, N=M=512, D=64, gamma=1.0,
+x, y ~ N(0,1) fp32 from seed 0, unfused mode, loss = batch mean.  One step is
+one pass of the whole path through the C ABI on preallocated buffers:
+sdtw_forward (distances, forward sweep, loss) + sdtw_backward (reverse sweep,
+alignment matrix, chain rule to dx and dy).  Inputs are resident in HBM when
+the timed region starts.  Prints one JSON line.
+
+Metric: DP cells per second, B*N*M / (seconds per step), plus peak memory of
+the autograd path.  `roofline` describes the dominant kernel (the reverse
+sweep) timed alone with HIP events on the stream it runs on; `cpu_baseline`
+is the fp64 oracle on the host, timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+WORKLOAD = dict(B=32, N=512, M=512, D=64, gamma=1.0)
+PEAK_FP64_VECTOR_TFLOPS = 78.6   # MI355X datasheet
+# Algorithmic work of one cell of the reverse sweep (dominant kernel): the
+# soft-min (2 min, 3 sub, 3 exp2, 2 add, 1 log2, 2 add) plus the alignment
+# value (3 add/sub, 1 exp2): 17 floating-point operations, every one of them
+# necessary to produce R' and E for that cell.
+REV_FLOPS_PER_CELL = 17
+# Bytes the reverse sweep must move per cell: read Dist (4) and the forward
+# state (8), write E (4).
+REV_BYTES_PER_CELL = 16
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def cpu_baseline(x, y, gamma, budget_s):
+    """The fp64 oracle on the host cores, on a bounded sample (whole pairs of
+    the same workload) sized to about `budget_s` seconds of CPU work."""
+    from oracle import oracle as O
+    O.lib()
+    xs, ys = x.numpy(), y.numpy()
+    B, N, D = xs.shape
+    M = ys.shape[1]
+    O.value_and_grad(xs[:1], ys[:1], gamma, [1.0 / B])  # warm-up
+    threads = O.num_threads()
+    # Whole batches of the workload's pairs (spread over the OpenMP threads)
+    # until about budget_s seconds of wall time have passed.
+    npairs = B
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        O.value_and_grad(xs[:npairs], ys[:npairs], gamma, [1.0 / B] * npairs)
+        done += npairs
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done * N * M / dt, "unit": "cells/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} pairs of {N}x{M}, D={D} (fp64 distances, forward, "
+                      f"log-space backward, chain rule), {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the workload runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from differentiable_series_alignment_amd import _lib as L
+    from differentiable_series_alignment_amd import SoftDTW
+    from sdtw_inputs import pair_batch
+
+    L.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    W = WORKLOAD
+    B, N, M, D, gamma = W["B"], W["N"], W["M"], W["D"], W["gamma"]
+    xc, yc = pair_batch(B, N, M, D, seed=0)
+    x, y = xc.to(dev), yc.to(dev)
+    mode = L.SDTW_MODE_UNFUSED
+    nbytes = L.sdtw_workspace_bytes(B, N, M, D, mode)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    loss = torch.empty(B, dtype=torch.float32, device=dev)
+    gl = torch.full((B,), 1.0 / B, dtype=torch.float32, device=dev)
+    gx = torch.empty_like(x)
+    gy = torch.empty_like(y)
+    stream = torch.cuda.current_stream(dev)
+    s = int(stream.cuda_stream)
+
+    def fwd():
+        L.check(L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, gamma, mode,
+                               ws.data_ptr(), nbytes, loss.data_ptr(), s), "sdtw_forward")
+
+    def bwd(grads=True):
+        L.check(L.sdtw_backward(x.data_ptr(), y.data_ptr(), B, N, M, D, gamma, mode,
+                                ws.data_ptr(), nbytes, gl.data_ptr(),
+                                gx.data_ptr() if grads else None,
+                                gy.data_ptr() if grads else None, None, s),
+                "sdtw_backward")
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fwd()
+        bwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    cells = B * N * M
+    value = cells / (ms * 1e-3)
+
+    # Dominant kernel alone: sdtw_backward without gradient outputs launches
+    # exactly one kernel, the reverse sweep.  Events bracket it on its stream.
+    rev_ms = []
+    for it in range(args.warmup + args.steps):
+        fwd()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        bwd(grads=False)
+        a1.record(stream)
+        if it >= args.warmup:
+            rev_ms.append((a0, a1))
+    torch.cuda.synchronize()
+    rev = sum(a.elapsed_time(b) for a, b in rev_ms) / len(rev_ms)
+    achieved = REV_FLOPS_PER_CELL * cells / (rev * 1e-3) / 1e12
+
+    # Peak memory of the autograd path (what a user of SoftDTW sees).
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    xg = x.clone().requires_grad_(True)
+    yg = y.clone().requires_grad_(True)
+    resident = torch.cuda.memory_allocated(dev) - base
+    SoftDTW(gamma=gamma)(xg, yg).mean().backward()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev) - base
+
+    out = {
+        "metric": "SoftDTW fwd+bwd DP cells/s (B*N*M/s) at B=32,N=M=512,D=64; peak MB",
+        "value": value,
+        "unit": "cells/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64 DP state + f32 exp/log; f64-accumulated distances; f32 chain rule",
+        "data": "synthetic",
+        "config": {"workload": "B=32 N=M=512 D=64 gamma=1.0 unfused fwd+bwd, batch-mean loss",
+                   "B": B, "N": N, "M": M, "D": D, "gamma": gamma, "mode": "unfused"},
+        "peak_mib": peak / 2**20,
+        "peak_mib_over_inputs": (peak - resident) / 2**20,
+        "roofline": {"kernel": "reverse sweep (k_dp_unfused<true>)", "bound": "alu",
+                     "achieved": achieved, "peak": PEAK_FP64_VECTOR_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP64_VECTOR_TFLOPS,
+                     "traffic": None, "launch_us": rev * 1e3,
+                     "algorithmic_gbs": REV_BYTES_PER_CELL * cells / (rev * 1e-3) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(xc, yc, gamma, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // The cell arrays use the band-step layout of sdtw_kernels.h.
 struct Layout {
   int64_t nbands = 0, nseg = 0, S = 0;
-  size_t ctrl = 0, ctrl_words = 0;  // u32 ticket + per-segment progress
+  size_t ctrl = 0, ctrl_words = 0;  // two sweeps x (ticket, done, progress)
   size_t loss64 = 0;                // fp64 [B]
   size_t H = 0;                     // fp64 [B, nseg, M]
   size_t R = 0;                     // fp64 band-step forward state
@@ -54,7 +54,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   const size_t cells = (size_t)B * (size_t)L->nbands * (size_t)L->S * 64;
   size_t off = 0;
   L->ctrl = off;
-  L->ctrl_words = 1 + (size_t)B * (size_t)L->nseg;
+  L->ctrl_words = 2 * (2 + (size_t)B * (size_t)L->nseg);
   off += align_up(L->ctrl_words * 4);
   L->loss64 = off;
   off += align_up((size_t)B * 8);
@@ -72,13 +72,16 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
 
 bool gamma_ok(float g) { return isfinite(g) && g > 0.f; }
 
+// Control words: the forward sweep uses the first half, the reverse sweep the
+// second; each sweep's kernel leaves its half zeroed when it finishes.
 DPArgs dp_args(const Layout& L, char* ws, const float* x, const float* y,
-               int64_t B, int64_t N, int64_t M, int64_t D, float gamma) {
+               int64_t B, int64_t N, int64_t M, int64_t D, float gamma,
+               bool reverse) {
   DPArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
   a.y = y;
-  a.ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl);
+  a.ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl) + (reverse ? L.ctrl_words / 2 : 0);
   a.loss64 = reinterpret_cast<double*>(ws + L.loss64);
   a.H = reinterpret_cast<double*>(ws + L.H);
   a.R = reinterpret_cast<double*>(ws + L.R);
@@ -143,9 +146,12 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
   if (mode == SDTW_MODE_FUSED) return SDTW_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
-  DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma);
+  DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma, false);
   a.loss = loss;
-  hipError_t e = sdtw::launch_zero_u32(a.ctrl, (int64_t)L.ctrl_words, s);
+  // A fresh workspace holds garbage: clear both sweeps' control words once
+  // per forward (later launches find them cleared by the kernels).
+  hipError_t e = sdtw::launch_zero_u32(reinterpret_cast<unsigned*>(ws + L.ctrl),
+                                       (int64_t)L.ctrl_words, s);
   if (e == hipSuccess) e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, s);
   if (e == hipSuccess) e = sdtw::launch_dp(a, false, false, s);
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
@@ -163,9 +169,8 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
   if (mode == SDTW_MODE_FUSED) return SDTW_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
-  DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma);
-  hipError_t e = sdtw::launch_zero_u32(a.ctrl, (int64_t)L.ctrl_words, s);
-  if (e == hipSuccess) e = sdtw::launch_dp(a, true, false, s);
+  DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma, true);
+  hipError_t e = sdtw::launch_dp(a, true, false, s);
   if (e == hipSuccess && align) e = sdtw::launch_unskew(a.dsk, align, B, N, M, L.S, s);
   if (e == hipSuccess && (grad_x || grad_y))
     e = sdtw::launch_chain(a.dsk, x, y, grad_loss, grad_x, grad_y, B, N, M, D, L.S, s);

@@ -51,6 +51,25 @@ __global__ void k_zero_u32(unsigned* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
+// Control words of one sweep: [0] ticket, [1] finished workgroups,
+// [2 + b*nseg + s] columns published by segment s of pair b.  The last
+// workgroup to finish returns them to zero, so the next launch on the same
+// workspace starts clean without a separate clearing launch (every other
+// workgroup has stopped touching them once it has counted itself finished).
+__device__ __forceinline__ void release_ctrl(unsigned* ctrl, int64_t nprog) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned done = __hip_atomic_fetch_add(&ctrl[1], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (done == gridDim.x - 1) {
+      for (int64_t k = 0; k < nprog; ++k)
+        __hip_atomic_store(&ctrl[2 + k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ctrl[1], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Per-lane view of one band of a band-step array: the element a sweep step t
 // touches is base[t * dir] (dir = +64 forward, -64 reverse).
 struct LaneCursor {
@@ -139,8 +158,8 @@ __global__ __launch_bounds__(kBandsPerWG * 64) void k_dp_unfused(DPArgs a) {
   const bool produce_global = active && last_in_seg && (seg + 1 < a.nseg);
   const bool consume_global = active && (w == 0) && (seg > 0);
 
-  unsigned* prog_in = a.ctrl + 1 + (int64_t)b * a.nseg + (seg > 0 ? seg - 1 : 0);
-  unsigned* prog_out = a.ctrl + 1 + (int64_t)b * a.nseg + seg;
+  unsigned* prog_in = a.ctrl + 2 + (int64_t)b * a.nseg + (seg > 0 ? seg - 1 : 0);
+  unsigned* prog_out = a.ctrl + 2 + (int64_t)b * a.nseg + seg;
   const double* Hin = a.H + ((int64_t)b * a.nseg + (seg > 0 ? seg - 1 : 0)) * M;
   double* Hout = a.H + ((int64_t)b * a.nseg + seg) * M;
 
@@ -296,6 +315,7 @@ __global__ __launch_bounds__(kBandsPerWG * 64) void k_dp_unfused(DPArgs a) {
 #undef SDTW_LOAD_CHUNK
 #undef SDTW_AWAIT
 #undef SDTW_LOAD_TOP
+  release_ctrl(a.ctrl, (int64_t)a.B * a.nseg);
 }
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s) {
