@@ -45,11 +45,12 @@ bool sizes_ok(int64_t B, int64_t N, int64_t M, int64_t D) {
 }
 
 bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L) {
-  (void)D;
   if (!sizes_ok(B, N, M, D) || (mode != SDTW_MODE_UNFUSED && mode != SDTW_MODE_FUSED))
     return false;
   L->nbands = (N + 63) / 64;
-  L->nseg = (L->nbands + sdtw::kBandsPerWG - 1) / sdtw::kBandsPerWG;
+  const int bpw = mode == SDTW_MODE_FUSED ? sdtw::fused_bands_per_wg(D) : sdtw::kBandsPerWG;
+  if (bpw == 0) return false;  // fused mode: D beyond what the kernels hold on chip
+  L->nseg = (L->nbands + bpw - 1) / bpw;
   L->S = sdtw::skew_steps(M);
   const size_t cells = (size_t)B * (size_t)L->nbands * (size_t)L->S * 64;
   size_t off = 0;
@@ -143,17 +144,17 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
   if (!make_layout(B, N, M, D, mode, &L)) return SDTW_ERR_INVALID_ARG;
   int st = check_ws(L, workspace, workspace_bytes);
   if (st != SDTW_OK) return st;
-  if (mode == SDTW_MODE_FUSED) return SDTW_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
   DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma, false);
   a.loss = loss;
+  const bool fused = mode == SDTW_MODE_FUSED;
   // A fresh workspace holds garbage: clear both sweeps' control words once
   // per forward (later launches find them cleared by the kernels).
   hipError_t e = sdtw::launch_zero_u32(reinterpret_cast<unsigned*>(ws + L.ctrl),
                                        (int64_t)L.ctrl_words, s);
-  if (e == hipSuccess) e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, s);
-  if (e == hipSuccess) e = sdtw::launch_dp(a, false, false, s);
+  if (e == hipSuccess && !fused) e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, s);
+  if (e == hipSuccess) e = sdtw::launch_dp(a, false, fused, s);
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
 }
 
@@ -166,10 +167,22 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
   if (!make_layout(B, N, M, D, mode, &L)) return SDTW_ERR_INVALID_ARG;
   int st = check_ws(L, workspace, workspace_bytes);
   if (st != SDTW_OK) return st;
-  if (mode == SDTW_MODE_FUSED) return SDTW_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
   DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma, true);
+  if (mode == SDTW_MODE_FUSED) {
+    // One reverse sweep per slice of D; it writes dx, adds into dy and, if
+    // asked, writes E.  Nothing to compute when no output is requested.
+    if (!grad_x && !grad_y && !align) return SDTW_OK;
+    a.gl = grad_loss;
+    a.gx = grad_x;
+    a.gy = grad_y;
+    a.align = align;
+    hipError_t e = hipSuccess;
+    if (grad_y) e = sdtw::launch_zero_f32(grad_y, B * M * D, s);
+    if (e == hipSuccess) e = sdtw::launch_dp(a, true, true, s);
+    return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
+  }
   hipError_t e = sdtw::launch_dp(a, true, false, s);
   if (e == hipSuccess && align) e = sdtw::launch_unskew(a.dsk, align, B, N, M, L.S, s);
   if (e == hipSuccess && (grad_x || grad_y))

@@ -47,8 +47,9 @@ struct DPArgs {
   double* loss64;       // [B] X[N-1,M-1] (forward writes, reverse reads)
   float* loss;          // [B] loss in natural units (forward)
   const float* gl;      // [B] upstream gradients (fused reverse)
-  float* gx;            // [B,N,D] (fused reverse)
-  float* gy;            // [B,M,D] (fused reverse)
+  float* gx;            // [B,N,D] (fused reverse; written)
+  float* gy;            // [B,M,D] (fused reverse; accumulated, zeroed first)
+  float* align;         // [B,N,M] optional E output (fused reverse)
   int64_t N, M, D, S;
   int B, nbands, nseg;
   double k2;            // log2(e) / gamma
@@ -57,6 +58,11 @@ struct DPArgs {
 
 // Bands (64 rows each) per workgroup of the DP kernels.
 constexpr int kBandsPerWG = 4;
+// Largest feature dimension the fused kernels handle (x rows of a band and the
+// next distance block's y operand stay on chip).
+constexpr int64_t kFusedMaxD = 256;
+// Bands per workgroup of the fused kernels for this D (0: unsupported D).
+int fused_bands_per_wg(int64_t D);
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
@@ -66,7 +72,9 @@ hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t 
                             hipStream_t stream);
 hipError_t launch_unskew(const float* esk, float* out, int64_t B, int64_t N,
                          int64_t M, int64_t S, hipStream_t s);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_dp(const DPArgs& a, bool reverse, bool fused, hipStream_t s);
+hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s);
 hipError_t launch_chain(const float* esk, const float* x, const float* y,
                         const float* gl, float* gx, float* gy, int64_t B,
                         int64_t N, int64_t M, int64_t D, int64_t S,

@@ -49,6 +49,9 @@ def test_workspace_bytes():
     for bad in [(0, 4, 4, 1), (1, 0, 4, 1), (1, 4, 0, 1), (1, 4, 4, 0), (-1, 4, 4, 1)]:
         assert L.sdtw_workspace_bytes(*bad, L.SDTW_MODE_UNFUSED) == 0
     assert L.sdtw_workspace_bytes(1, 4, 4, 1, 7) == 0
+    # fused mode keeps a band's x rows on chip: D up to 256
+    assert L.sdtw_workspace_bytes(2, 100, 100, 256, L.SDTW_MODE_FUSED) > 0
+    assert L.sdtw_workspace_bytes(2, 100, 100, 257, L.SDTW_MODE_FUSED) == 0
 
 
 def _fwd(**kw):

@@ -89,19 +89,21 @@ def test_dist_matches_rounded_exact(O, S, B, N, M, D):
 
 # --- small and ragged shapes --------------------------------------------------------------
 
-def test_tiny_config(O, S):
-    """B=2, N=M=16, D=1, gamma=1, unfused, mean loss."""
+@pytest.mark.parametrize("fused", [False, True])
+def test_tiny_config(O, S, fused):
+    """B=2, N=M=16, D=1, gamma=1, mean loss."""
     x, y = pair_batch(2, 16, 16, 1, seed=0)
-    check_against_oracle(O, S, x, y, 1.0, what="tiny")
+    check_against_oracle(O, S, x, y, 1.0, fused=fused, what="tiny")
 
 
 @pytest.mark.parametrize("N,M", [(1, 1), (1, 9), (9, 1), (2, 2), (63, 65), (64, 64),
                                  (65, 63), (130, 257), (257, 130), (300, 300), (513, 77),
                                  (77, 513), (600, 333), (1100, 50), (5, 1500)])
 @pytest.mark.parametrize("gamma", [1.0, 0.1])
-def test_ragged_shapes(O, S, N, M, gamma):
+@pytest.mark.parametrize("fused", [False, True])
+def test_ragged_shapes(O, S, N, M, gamma, fused):
     x, y = pair_batch(3, N, M, 3, seed=N * 7 + M)
-    check_against_oracle(O, S, x, y, gamma, what=f"{N}x{M} g={gamma}")
+    check_against_oracle(O, S, x, y, gamma, fused=fused, what=f"{N}x{M} g={gamma}")
 
 
 @pytest.mark.parametrize("seed", [1, 2])
@@ -144,28 +146,31 @@ def test_zero_distance_marginals(S, N, M):
 
 # --- the workloads --------------------------------------------------------------------------
 
-def test_headline_config(O, S):
-    """B=32, N=M=512, D=64, gamma=1, unfused, loss = batch mean; all pairs."""
+@pytest.mark.parametrize("fused", [False, True])
+def test_headline_config(O, S, fused):
+    """B=32, N=M=512, D=64, gamma=1, loss = batch mean; all pairs."""
     x, y = pair_batch(32, 512, 512, 64, seed=0)
-    check_against_oracle(O, S, x, y, 1.0, what="headline")
+    check_against_oracle(O, S, x, y, 1.0, fused=fused, what="headline")
 
 
 @pytest.mark.parametrize("D", [1, 4, 16, 64, 128, 256])
-def test_feature_sweep(O, S, D):
+@pytest.mark.parametrize("fused", [False, True])
+def test_feature_sweep(O, S, D, fused):
     """B=32, N=M=256, D in {1,4,16,64,128,256}, gamma=1; all pairs."""
     x, y = pair_batch(32, 256, 256, D, seed=0)
-    check_against_oracle(O, S, x, y, 1.0, what=f"D={D}")
+    check_against_oracle(O, S, x, y, 1.0, fused=fused, what=f"D={D}")
 
 
 @pytest.mark.parametrize("N,M", [(1024, 1024), (2048, 2048), (4096, 1000), (4096, 4096)])
 @pytest.mark.parametrize("gamma", [1.0, 0.01])
-def test_long_sequences(O, S, N, M, gamma):
+@pytest.mark.parametrize("fused", [False, True])
+def test_long_sequences(O, S, N, M, gamma, fused):
     """B=32, D=128 at full size on the GPU; the oracle checks sampled pairs
     (first and last, or the first at 4096^2) and every pair must be finite
     with gradients summing to zero over both sequences."""
     x, y = pair_batch(32, N, M, 128, seed=0)
     pairs = [0] if N * M > 5_000_000 else [0, 31]
-    l, gx, gy = check_against_oracle(O, S, x, y, gamma, pairs=pairs,
+    l, gx, gy = check_against_oracle(O, S, x, y, gamma, fused=fused, pairs=pairs,
                                      what=f"{N}x{M} g={gamma}")
     s = gx.sum(axis=1) + gy.sum(axis=1)
     scale = np.abs(gx).sum(axis=1) + np.abs(gy).sum(axis=1) + 1e-30
@@ -208,6 +213,33 @@ def test_barycenter_api(S):
     z, hist = S.softdtw_barycenter(X, gamma=1.0, max_iter=30, lr=0.1, return_history=True)
     assert z.shape == (100, 3) and torch.isfinite(z).all()
     assert hist[-1] < hist[0]
+
+
+# --- fused mode against unfused mode ------------------------------------------------------
+
+@pytest.mark.parametrize("N,M,D", [(70, 45, 4), (300, 260, 64), (129, 700, 100), (257, 64, 200)])
+def test_fused_matches_unfused(S, N, M, D):
+    """Both modes see bit-identical distances and run the same recurrence, so
+    the loss and the alignment matrix agree bitwise; gradients are summed in
+    different orders (and dy through atomics in fused mode)."""
+    x, y = pair_batch(3, N, M, D, seed=N + M + D)
+    xd, yd = x.to(DEV), y.to(DEV)
+    lu, Eu = S.alignment(xd, yd, 0.7, fused=False)
+    lf, Ef = S.alignment(xd, yd, 0.7, fused=True)
+    torch.testing.assert_close(lf, lu, rtol=0, atol=0)
+    torch.testing.assert_close(Ef, Eu, rtol=0, atol=0)
+    _, gxu, gyu = gpu_value_and_grad(S, x, y, 0.7, fused=False)
+    _, gxf, gyf = gpu_value_and_grad(S, x, y, 0.7, fused=True)
+    np.testing.assert_allclose(gxf, gxu, rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(gyf, gyu, rtol=1e-4, atol=1e-6)
+
+
+def test_fused_rejects_large_D(S):
+    from differentiable_series_alignment_amd import _lib
+    assert _lib.sdtw_workspace_bytes(2, 10, 10, 300, _lib.SDTW_MODE_FUSED) == 0
+    x, y = pair_batch(2, 10, 10, 300, seed=0)
+    with pytest.raises(ValueError):
+        S.soft_dtw(x.to(DEV), y.to(DEV), 1.0, fused=True)
 
 
 # --- invariants (exact ones checked bitwise) ---------------------------------------------------
