@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--headline-only", action="store_true",
+                   help="skip the per-configuration table")
     return p.parse_args()
 
 
@@ -76,27 +78,12 @@ def cpu_baseline(x, y, gamma, budget_s):
                       f"log-space backward, chain rule), {dt:.1f} s wall"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the workload runs on a single MI355X)", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    from differentiable_series_alignment_amd import _lib as L
-    from differentiable_series_alignment_amd import SoftDTW
-    from sdtw_inputs import pair_batch
-
-    L.lib()
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    W = WORKLOAD
-    B, N, M, D, gamma = W["B"], W["N"], W["M"], W["D"], W["gamma"]
-    xc, yc = pair_batch(B, N, M, D, seed=0)
-    x, y = xc.to(dev), yc.to(dev)
-    mode = L.SDTW_MODE_UNFUSED
+def measure(L, torch, x, y, gamma, mode, steps, warmup):
+    """Milliseconds per fwd+bwd step through the C ABI on preallocated
+    buffers, timed with events on the launch stream."""
+    B, N, D = x.shape
+    M = y.shape[1]
+    dev = x.device
     nbytes = L.sdtw_workspace_bytes(B, N, M, D, mode)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     loss = torch.empty(B, dtype=torch.float32, device=dev)
@@ -117,25 +104,84 @@ def main():
                                 gy.data_ptr() if grads else None, None, s),
                 "sdtw_backward")
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         fwd()
         bwd()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         fwd()
         bwd()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    return e0.elapsed_time(e1) / steps, fwd, bwd, stream
+
+
+def peak_mib(torch, SoftDTW, x, y, gamma, fused):
+    """Peak device memory of one autograd fwd+bwd (SoftDTW(...)(x, y).mean()
+    .backward()) above what was allocated before, and the part of it taken
+    by x, y and their gradients."""
+    dev = x.device
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    xg = x.clone().requires_grad_(True)
+    yg = y.clone().requires_grad_(True)
+    SoftDTW(gamma=gamma, fused=fused)(xg, yg).mean().backward()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    io = 2 * (xg.numel() + yg.numel()) * 4
+    del xg, yg
+    return peak / 2**20, (peak - io) / 2**20
+
+
+def barycenter_rate(torch, softdtw_barycenter, block_waves):
+    """Block-wave barycenter: 10 sequences (100, 3), Adam lr 0.1, 100
+    iterations, gamma 1; each iteration is one batched fwd+bwd."""
+    X = block_waves(10, 100, 3, seed=0).to("cuda:0")
+    softdtw_barycenter(X, gamma=1.0, max_iter=5, lr=0.1)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    softdtw_barycenter(X, gamma=1.0, max_iter=100, lr=0.1)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    return {"workload": "barycenter K=10 N=M=100 D=3 gamma=1.0, 100 Adam iterations",
+            "ms_per_iteration": dt * 1e3 / 100,
+            "cells_per_s": 100 * 10 * 100 * 100 / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the workload runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from differentiable_series_alignment_amd import _lib as L
+    from differentiable_series_alignment_amd import SoftDTW, softdtw_barycenter
+    from sdtw_inputs import block_waves, pair_batch
+
+    L.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    W = WORKLOAD
+    B, N, M, D, gamma = W["B"], W["N"], W["M"], W["D"], W["gamma"]
+    xc, yc = pair_batch(B, N, M, D, seed=0)
+    x, y = xc.to(dev), yc.to(dev)
     cells = B * N * M
+
+    ms, fwd, bwd, stream = measure(L, torch, x, y, gamma, L.SDTW_MODE_UNFUSED,
+                                   args.steps, args.warmup)
     value = cells / (ms * 1e-3)
 
     # Dominant kernel alone: sdtw_backward without gradient outputs launches
     # exactly one kernel, the reverse sweep.  Events bracket it on its stream.
-    rev_ms = []
+    pairs = []
     for it in range(args.warmup + args.steps):
         fwd()
         a0 = torch.cuda.Event(enable_timing=True)
@@ -144,22 +190,36 @@ def main():
         bwd(grads=False)
         a1.record(stream)
         if it >= args.warmup:
-            rev_ms.append((a0, a1))
+            pairs.append((a0, a1))
     torch.cuda.synchronize()
-    rev = sum(a.elapsed_time(b) for a, b in rev_ms) / len(rev_ms)
+    rev = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
     achieved = REV_FLOPS_PER_CELL * cells / (rev * 1e-3) / 1e12
 
-    # Peak memory of the autograd path (what a user of SoftDTW sees).
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    base = torch.cuda.memory_allocated(dev)
-    torch.cuda.reset_peak_memory_stats(dev)
-    xg = x.clone().requires_grad_(True)
-    yg = y.clone().requires_grad_(True)
-    resident = torch.cuda.memory_allocated(dev) - base
-    SoftDTW(gamma=gamma)(xg, yg).mean().backward()
-    torch.cuda.synchronize()
-    peak = torch.cuda.max_memory_allocated(dev) - base
+    peak, peak_over = peak_mib(torch, SoftDTW, x, y, gamma, False)
+    ms_f, _, _, _ = measure(L, torch, x, y, gamma, L.SDTW_MODE_FUSED,
+                            max(5, args.steps // 5), 2)
+    peak_f, peak_over_f = peak_mib(torch, SoftDTW, x, y, gamma, True)
+
+    per_config = []
+    if not args.headline_only:
+        cfgs = [(2, 16, 16, 1, 1.0)]
+        cfgs += [(32, 256, 256, d, 1.0) for d in (1, 4, 16, 64, 128, 256)]
+        cfgs += [(32, n, m, 128, g) for (n, m) in ((1024, 1024), (2048, 2048),
+                                                   (4096, 4096), (4096, 1000))
+                 for g in (1.0, 0.01)]
+        for (b_, n_, m_, d_, g_) in cfgs:
+            xc2, yc2 = pair_batch(b_, n_, m_, d_, seed=0)
+            x2, y2 = xc2.to(dev), yc2.to(dev)
+            entry = {"workload": f"B={b_} N={n_} M={m_} D={d_} gamma={g_}"}
+            for mode, name in ((L.SDTW_MODE_UNFUSED, "unfused"), (L.SDTW_MODE_FUSED, "fused")):
+                t, _, _, _ = measure(L, torch, x2, y2, g_, mode, 5, 2)
+                pk, pko = peak_mib(torch, SoftDTW, x2, y2, g_, mode == L.SDTW_MODE_FUSED)
+                entry[name] = {"ms_per_step": t, "cells_per_s": b_ * n_ * m_ / (t * 1e-3),
+                               "peak_mib": pk, "peak_mib_over_io": pko}
+            per_config.append(entry)
+            del x2, y2
+            torch.cuda.empty_cache()
+        per_config.append(barycenter_rate(torch, softdtw_barycenter, block_waves))
 
     out = {
         "metric": "SoftDTW fwd+bwd DP cells/s (B*N*M/s) at B=32,N=M=512,D=64; peak MB",
@@ -176,13 +236,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": "B=32 N=M=512 D=64 gamma=1.0 unfused fwd+bwd, batch-mean loss",
                    "B": B, "N": N, "M": M, "D": D, "gamma": gamma, "mode": "unfused"},
-        "peak_mib": peak / 2**20,
-        "peak_mib_over_inputs": (peak - resident) / 2**20,
+        "peak_mib": peak,
+        "peak_mib_over_io": peak_over,
+        "fused": {"ms_per_step": ms_f, "cells_per_s": cells / (ms_f * 1e-3),
+                  "peak_mib": peak_f, "peak_mib_over_io": peak_over_f},
         "roofline": {"kernel": "reverse sweep (k_dp_unfused<true>)", "bound": "alu",
                      "achieved": achieved, "peak": PEAK_FP64_VECTOR_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP64_VECTOR_TFLOPS,
                      "traffic": None, "launch_us": rev * 1e3,
                      "algorithmic_gbs": REV_BYTES_PER_CELL * cells / (rev * 1e-3) / 1e9},
+        "per_config": per_config,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(xc, yc, gamma, args.cpu_seconds)

@@ -23,9 +23,12 @@
  *                      the backward overwrites it with E.
  *   SDTW_MODE_FUSED    recomputes distances from x and y inside the dynamic
  *                      programme; no B x N x M distance or E tensor exists.
+ *                      Supports D <= 256 (sdtw_workspace_bytes returns 0 and
+ *                      the calls return SDTW_ERR_INVALID_ARG beyond that).
  * Both modes keep the forward DP state (fp64, B x N x M) for the backward.
  * Distances are accumulated in fp64 and rounded once to fp32 in both modes,
- * so fused and unfused see identical distances.
+ * so fused and unfused see identical distances, losses and alignment
+ * matrices (gradients agree to rounding: they are summed in other orders).
  *
  * Conventions for every entry point:
  *  - x is [B,N,D], y is [B,M,D], fp32, row-major and contiguous, in device
@@ -96,11 +99,13 @@ int sdtw_forward(const float *x, const float *y, int64_t B, int64_t N,
  * workspace must be as sdtw_forward left it for the same arguments.
  * grad_x ([B,N,D]) and grad_y ([B,M,D]) are written (not accumulated); either
  * may be NULL to skip it.  align ([B,N,M] fp32), if not NULL, receives E
- * (unfused mode only; SDTW_ERR_UNSUPPORTED in fused mode).  In unfused mode
- * the distance tensor in the workspace is replaced by E, so a second
- * sdtw_backward on the same workspace needs sdtw_forward to run again first;
- * in fused mode the workspace is left unchanged and the backward may be
- * repeated. */
+ * (both modes; in fused mode it is the only B x N x M array written).  In
+ * unfused mode the distance tensor in the workspace is replaced by E, so a
+ * second sdtw_backward on the same workspace needs sdtw_forward to run again
+ * first; in fused mode the workspace is left unchanged and the backward may
+ * be repeated (a fused backward with every output NULL does nothing).  In
+ * fused mode grad_y is accumulated with atomic adds across row bands, so its
+ * last bits may differ from run to run. */
 int sdtw_backward(const float *x, const float *y, int64_t B, int64_t N,
                   int64_t M, int64_t D, float gamma, int mode, void *workspace,
                   size_t workspace_bytes, const float *grad_loss,
