@@ -51,79 +51,74 @@ __global__ __launch_bounds__(256) void k_dist(const float* __restrict__ x,
                                               float* __restrict__ dist,
                                               int64_t N, int64_t M, int64_t D,
                                               int64_t S) {
+  // The workgroup's 64 x rows and 64 y rows pass through LDS in slabs of
+  // KC feature columns (coalesced loads; the next slab is fetched into
+  // registers while the current one feeds the MFMAs).  Rows outside the
+  // grid and columns >= D are stored as zeros.
+  constexpr int KC = 64, PK = KC + 4;
+  __shared__ float xs[64 * PK], ys[64 * PK];
   __shared__ float tile[SKEW ? 64 * 64 : 1];
   const int l = lane_id();
   const int w = threadIdx.x >> 6;
   const int64_t b = blockIdx.z;
-  const int64_t i0 = (int64_t)blockIdx.y * 64 + (w >> 1) * 32;
-  const int64_t j0 = (int64_t)blockIdx.x * 64 + (w & 1) * 32;
+  const int64_t bi0 = (int64_t)blockIdx.y * 64, bj0 = (int64_t)blockIdx.x * 64;
+  const int64_t i0 = bi0 + (w >> 1) * 32;
+  const int64_t j0 = bj0 + (w & 1) * 32;
   const float* xb = x + b * N * D;
   const float* yb = y + b * M * D;
   const int r = l & 15, kk = l >> 4;
+  const int ra = (w >> 1) * 32 + r, rb = (w & 1) * 32 + r;  // slab rows of this lane
 
-  // Rows / columns this lane feeds into the A and B operands.
-  const int64_t ia0 = i0 + r, ia1 = i0 + 16 + r;
-  const int64_t jb0 = j0 + r, jb1 = j0 + 16 + r;
-  const bool va0 = ia0 < N, va1 = ia1 < N, vb0 = jb0 < M, vb1 = jb1 < M;
-  const float* pa0 = xb + (va0 ? ia0 : 0) * D;
-  const float* pa1 = xb + (va1 ? ia1 : 0) * D;
-  const float* pb0 = yb + (vb0 ? jb0 : 0) * D;
-  const float* pb1 = yb + (vb1 ? jb1 : 0) * D;
+  // Staging: thread t moves elements t + 256 q (q < 16) of each 64 x KC slab.
+  float sx[16], sy[16];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = (int)threadIdx.x + 256 * q;
+      const int row = e / KC, col = e % KC;
+      const int64_t d = k0 + col;
+      const int64_t gi = bi0 + row, gj = bj0 + row;
+      const bool dok = d < D;
+      const float vx = xb[(gi < N ? gi : 0) * D + (dok ? d : 0)];
+      const float vy = yb[(gj < M ? gj : 0) * D + (dok ? d : 0)];
+      sx[q] = (dok && gi < N) ? vx : 0.f;
+      sy[q] = (dok && gj < M) ? vy : 0.f;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = (int)threadIdx.x + 256 * q;
+      xs[(e / KC) * PK + e % KC] = sx[q];
+      ys[(e / KC) * PK + e % KC] = sy[q];
+    }
+  };
 
   v4d acc00 = {0, 0, 0, 0}, acc01 = acc00, acc10 = acc00, acc11 = acc00;
   double nxa0 = 0, nxa1 = 0, nyb0 = 0, nyb1 = 0;
   const int64_t steps = (D + 3) / 4;
-  // Operands are loaded unconditionally at clamped addresses one block of
-  // KB steps ahead of the MFMAs and zeroed at use where d >= D or the
-  // row/column is outside the grid.
-  constexpr int KB = 8;
-  float c_a0[KB], c_a1[KB], c_b0[KB], c_b1[KB];
-  float n_a0[KB], n_a1[KB], n_b0[KB], n_b1[KB];
-  const int64_t nblk = (steps + KB - 1) / KB;
-  auto load_block = [&](int64_t blk, float (&A0)[KB], float (&A1)[KB],
-                        float (&B0)[KB], float (&B1)[KB]) {
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      int64_t d = 4 * (blk * KB + j) + kk;
-      d = d < D ? d : D - 1;
-      A0[j] = pa0[d];
-      A1[j] = pa1[d];
-      B0[j] = pb0[d];
-      B1[j] = pb1[d];
-    }
-  };
-  load_block(0, c_a0, c_a1, c_b0, c_b1);
-  __builtin_amdgcn_s_waitcnt(0);
-  for (int64_t blk = 0; blk < nblk; ++blk) {
-    const bool more = blk + 1 < nblk;
-    if (more) load_block(blk + 1, n_a0, n_a1, n_b0, n_b1);
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const int64_t s = blk * KB + j;
-      if (s < steps) {  // wave-uniform
-        const bool vd = 4 * s + kk < D;
-        const double a0 = (vd && va0) ? (double)c_a0[j] : 0.0;
-        const double a1 = (vd && va1) ? (double)c_a1[j] : 0.0;
-        const double b0 = (vd && vb0) ? (double)c_b0[j] : 0.0;
-        const double b1 = (vd && vb1) ? (double)c_b1[j] : 0.0;
-        nxa0 = fma(a0, a0, nxa0);
-        nxa1 = fma(a1, a1, nxa1);
-        nyb0 = fma(b0, b0, nyb0);
-        nyb1 = fma(b1, b1, nyb1);
-        acc00 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc00, 0, 0, 0);
-        acc01 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc01, 0, 0, 0);
-        acc10 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc10, 0, 0, 0);
-        acc11 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc11, 0, 0, 0);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < KB; ++j) {
-        c_a0[j] = n_a0[j];
-        c_a1[j] = n_a1[j];
-        c_b0[j] = n_b0[j];
-        c_b1[j] = n_b1[j];
-      }
+  fetch(0);
+  for (int64_t k0 = 0; k0 < D; k0 += KC) {
+    __syncthreads();
+    stash();
+    __syncthreads();
+    if (k0 + KC < D) fetch(k0 + KC);
+    const int64_t s0 = k0 / 4;
+    const int ns = (int)(steps - s0 < KC / 4 ? steps - s0 : KC / 4);
+    for (int sl = 0; sl < ns; ++sl) {  // step s = s0 + sl, feature d = 4s + kk
+      const int c = 4 * sl + kk;
+      const double a0 = (double)xs[ra * PK + c];
+      const double a1 = (double)xs[(ra + 16) * PK + c];
+      const double b0 = (double)ys[rb * PK + c];
+      const double b1 = (double)ys[(rb + 16) * PK + c];
+      nxa0 = fma(a0, a0, nxa0);
+      nxa1 = fma(a1, a1, nxa1);
+      nyb0 = fma(b0, b0, nyb0);
+      nyb1 = fma(b1, b1, nyb1);
+      acc00 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc00, 0, 0, 0);
+      acc01 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc01, 0, 0, 0);
+      acc10 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc10, 0, 0, 0);
+      acc11 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc11, 0, 0, 0);
     }
   }
   // Complete the norms over the four k lane groups (lanes r, r+16, r+32, r+48).
