@@ -64,11 +64,11 @@ __device__ __forceinline__ void band_chunk(double& cur, double& up, const double
     bottom[u] = c;
     const int64_t e = cu.base + t * cu.dir;
     if (!REV) {
-      rsk[e] = c;
+      __builtin_nontemporal_store(c, rsk + e);
     } else {
       // ln E = (R[N-1,M-1] + Dist - R - R') / g, i.e. in base-2 units
       // log2 E = Xnm + d - X - X'; the exponential is taken last.
-      dsk[e] = hw_exp2((float)((xnm + d) - (rn[u] + c)));
+      __builtin_nontemporal_store(hw_exp2((float)((xnm + d) - (rn[u] + c))), dsk + e);
     }
   }
 }
@@ -139,22 +139,10 @@ __global__ __launch_bounds__(kBandsPerWG * 64) void k_dp_unfused(DPArgs a) {
     }                                                                     \
   }
   // Wait (bounded) until the segment above has published `need` columns.
-  // The producer holds a smaller ticket and is running, so it publishes
-  // within one sweep; the cap only guarantees that every wave exits even if
-  // that ever failed (the result would be garbage, never a hang).
 #define SDTW_AWAIT(need_)                                                 \
   {                                                                       \
     const unsigned need = (unsigned)(need_);                              \
-    if (avail < need) {                                                   \
-      unsigned v = 0;                                                     \
-      for (uint32_t spin = 0; spin < kSpinCap; ++spin) {                  \
-        v = __hip_atomic_load(prog_in, __ATOMIC_ACQUIRE,                  \
-                              __HIP_MEMORY_SCOPE_AGENT);                  \
-        if (v >= need) break;                                             \
-        __builtin_amdgcn_s_sleep(2);                                      \
-      }                                                                   \
-      avail = v < need ? need : v;                                        \
-    }                                                                     \
+    if (avail < need) avail = await_progress(prog_in, need);              \
   }
 #define SDTW_LOAD_TOP(qq, T_)                                             \
   {                                                                       \

@@ -34,6 +34,24 @@ __device__ __forceinline__ void release_ctrl(unsigned* ctrl, int64_t nprog) {
   }
 }
 
+// Bounded wait until *prog >= need (columns published by the segment above).
+// The polls are relaxed; one agent-scope acquire fence follows the poll that
+// succeeds, so waiting does not invalidate caches on every poll.  The producer
+// holds a smaller ticket and is running, so it publishes within one sweep; the
+// cap only guarantees that every wave exits even if that ever failed (the
+// result would be garbage, never a hang).  Returns the value to record as
+// available.
+__device__ __forceinline__ unsigned await_progress(const unsigned* prog, unsigned need) {
+  unsigned v = 0;
+  for (uint32_t spin = 0; spin < kSpinCap; ++spin) {
+    v = __hip_atomic_load(prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v >= need) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return v < need ? need : v;
+}
+
 // Per-lane view of one band of a band-step array: the element a sweep step t
 // touches is base[t * dir] (dir = +64 forward, -64 reverse).
 struct LaneCursor {

@@ -267,15 +267,7 @@ __global__ __launch_bounds__(W * 64) void k_dp_fused(DPArgs a, int64_t d0) {
   };
   auto await_cols = [&](int64_t need_) {
     const unsigned need = (unsigned)need_;
-    if (avail < need) {
-      unsigned v = 0;
-      for (uint32_t spin = 0; spin < kSpinCap; ++spin) {
-        v = __hip_atomic_load(prog_in, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-        if (v >= need) break;
-        __builtin_amdgcn_s_sleep(2);
-      }
-      avail = v < need ? need : v;
-    }
+    if (avail < need) avail = await_progress(prog_in, need);
   };
   auto load_top = [&](int qq, double (&T_)[kCH]) {
 #pragma unroll
@@ -337,7 +329,7 @@ __global__ __launch_bounds__(W * 64) void k_dp_fused(DPArgs a, int64_t d0) {
         cur = c;
         bottom[u] = c;
         if (!REV) {
-          rsk[cu.base + t * cu.dir] = c;
+          __builtin_nontemporal_store(c, rsk + cu.base + t * cu.dir);
         } else {
           const float ev = hw_exp2((float)((xnm + d) - (rn[u] + c)));
           *cellp = ev;
