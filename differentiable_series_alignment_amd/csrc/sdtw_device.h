@@ -36,28 +36,37 @@ __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf
 // enough that sums of a few hundred of them stay finite.
 constexpr double kBig = 1e290;
 
-// v_min_f64 on values known to be non-NaN (the generic fmin would first
-// quiet possible signalling NaNs, which costs two extra instructions on the
-// dependency chain of every step).
+// v_min_f64 / v_max_f64 on values known to be non-NaN (the generic fmin and
+// fmax would first quiet possible signalling NaNs, which costs two extra
+// instructions on the dependency chain of every step).
 __device__ __forceinline__ double min_nonan(double a, double b) {
   double r;
   asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+__device__ __forceinline__ double max_nonan(double a, double b) {
+  double r;
+  asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 // One cell of the recurrence in base-2 units X = R * log2(e) / g:
 //   X = d + m - log2(2^(m-a) + 2^(m-b) + 2^(m-c)),  m = min(a, b, c),
-// which is R = D + softmin_g(...) scaled by log2(e)/g.  State and
-// differences are fp64; the exponentials and the logarithm are the fp32
-// hardware instructions applied to the (small) fp64 differences.
+// which is R = D + softmin_g(...) scaled by log2(e)/g.  The term of the
+// minimum is exactly 1, so only the other two are exponentiated: with
+// m1 = min(a,c), p = max(a,c), m = min(m1,b), q = max(m1,b), the multiset
+// {a,b,c} is {m,p,q}.  State and differences are fp64; the exponentials and
+// the logarithm are the fp32 hardware instructions applied to the (small,
+// non-positive) fp64 differences.
 __device__ __forceinline__ double softmin2_cell(double a, double b, double c,
                                                 double d) {
-  const double m = min_nonan(min_nonan(a, c), b);
-  const float ea = hw_exp2((float)(m - a));
-  const float eb = hw_exp2((float)(m - b));
-  const float ec = hw_exp2((float)(m - c));
-  const float s = (ea + ec) + eb;
-  return (m + d) - (double)hw_log2(s);
+  const double m1 = min_nonan(a, c);
+  const double p = max_nonan(a, c);
+  const double m = min_nonan(m1, b);
+  const double q = max_nonan(m1, b);
+  const float ep = hw_exp2((float)(m - p));
+  const float eq = hw_exp2((float)(m - q));
+  return (m + d) - (double)hw_log2((1.0f + ep) + eq);
 }
 
 __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }

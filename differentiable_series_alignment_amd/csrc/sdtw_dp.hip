@@ -16,13 +16,15 @@
 //    it from the band above;
 //  - the state of a cell is fp64; exp/log are the fp32 hardware ones applied
 //    to fp64 differences (see softmin_cell);
-//  - the kBandsPerWG bands of a workgroup advance in lock step, chunk by
-//    chunk (CH steps), band w running LAG chunks behind band w-1 and reading
-//    its top row from an LDS ring that band w-1's lane 63 fills;
+//  - the kBandsPerWG band waves of a workgroup run decoupled, each at its own
+//    pace, chunk by chunk (16 steps); band w reads its top row from an LDS
+//    ring that band w-1's lane 63 fills, with written/released column
+//    counters instead of barriers;
 //  - consecutive workgroups of one pair ("segments") hand the bottom row of
-//    the segment over through global memory with agent-scope release/acquire
-//    counters; workgroups take tickets in arrival order and a segment only
-//    waits on a smaller ticket, so the wait always ends.
+//    the segment over through global memory; one extra wave per workgroup
+//    does that copying and signalling, so band waves only ever wait on LDS;
+//    workgroups take tickets in arrival order and a segment only waits on a
+//    smaller ticket, so the wait always ends.
 //
 // The reverse sweep runs the same recurrence on both sequences reversed,
 // which yields R'[i,j], the soft-DTW value of the suffix alignment from
@@ -42,209 +44,207 @@ __global__ void k_zero_u32(unsigned* p, int64_t n) {
 }
 
 // Sixteen steps of one band.  MASK: the chunk contains steps with column < 0
-// (only the first 64 steps do); those cells are the left boundary, +inf
-// except the corner R[-1,-1] = 0 handled through the initial state.
+// (only the first 64 steps do); those cells are the left boundary.  Giving
+// them the distance kBig makes every such state at least kBig (the +inf
+// stand-in) without touching the dependency chain; the corner R[-1,-1] = 0
+// enters through the initial state of lane 0 of the first band.  Cells past
+// the last column or below the last row compute unused values in padding
+// storage; no real cell depends on them.
 template <bool REV, bool MASK>
 __device__ __forceinline__ void band_chunk(double& cur, double& up, const double (&top)[16],
                                            const float (&dn)[16], const double (&rn)[16],
-                                           double (&bottom)[16], int64_t t0, int lane,
-                                           bool row_ok, double k2, double xnm,
-                                           float* __restrict__ dsk, double* __restrict__ rsk,
-                                           const LaneCursor& cu) {
+                                           double (&bottom)[16], int t0, int lane, double k2,
+                                           double xnm, float* __restrict__ dp,
+                                           double* __restrict__ rp) {
+  constexpr int dir = REV ? -64 : 64;
+  // Steps 8..15 address from a second base so every access of the chunk
+  // is base + immediate offset.
+  float* const dp8 = dp + 8 * dir;
+  double* const rp8 = rp + 8 * dir;
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
-    const int64_t t = t0 + u;
-    const double d = row_ok ? (double)dn[u] * k2 : 0.0;
+    double d = (double)dn[u] * k2;
+    if (MASK) d = (t0 + u < lane) ? kBig : d;
     const double upn = wave_shr1(cur, top[u]);
-    const double diag = up;
+    const double c = softmin2_cell(up, upn, cur, d);
     up = upn;
-    double c = softmin2_cell(diag, upn, cur, d);
-    if (MASK) c = (t - lane < 0) ? kBig : c;
     cur = c;
     bottom[u] = c;
-    const int64_t e = cu.base + t * cu.dir;
     if (!REV) {
-      __builtin_nontemporal_store(c, rsk + e);
+      __builtin_nontemporal_store(c, (u < 8 ? rp : rp8) + (u & 7) * dir);
     } else {
       // ln E = (R[N-1,M-1] + Dist - R - R') / g, i.e. in base-2 units
       // log2 E = Xnm + d - X - X'; the exponential is taken last.
-      __builtin_nontemporal_store(hw_exp2((float)((xnm + d) - (rn[u] + c))), dsk + e);
+      __builtin_nontemporal_store(hw_exp2((float)((xnm + d) - (rn[u] + c))),
+                                  (u < 8 ? dp : dp8) + (u & 7) * dir);
     }
   }
 }
 
+// s_waitcnt operand (gfx9 layout: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
+// vmcnt[5:4] in [15:14]) that waits until at most 16 vector-memory
+// operations are outstanding and does not wait on the other counters.
+constexpr int kWaitVm16 = (1 << 14) | (7 << 4) | (15 << 8);
+
+// Loads of one chunk's inputs (16 steps from `off`), two bases as above.
 template <bool REV>
-__global__ __launch_bounds__(kBandsPerWG * 64) void k_dp_unfused(DPArgs a) {
+__device__ __forceinline__ void load_chunk(const float* dbase, const double* rbase, int64_t off,
+                                           float (&dn)[16], double (&rn)[16]) {
+  constexpr int dir = REV ? -64 : 64;
+  const float* d0 = dbase + off;
+  const float* d8 = d0 + 8 * dir;
+  const double* r0 = rbase + off;
+  const double* r8 = r0 + 8 * dir;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    dn[u] = (u < 8 ? d0 : d8)[(u & 7) * dir];
+    if (REV) rn[u] = (u < 8 ? r0 : r8)[(u & 7) * dir];
+  }
+}
+
+// One band of one pair, swept column chunk by column chunk.  The band's top
+// row comes from LDS ring `w` (unless it is the first band of the pair); its
+// bottom row goes to LDS ring `w + 1` when a band or the segment's I/O wave
+// reads it.
+template <bool REV>
+__device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int w, int nb_seg,
+                                           double (*ring)[kRingC + kCH], unsigned* wr, unsigned* rd,
+                                           int lane) {
   constexpr int W = kBandsPerWG;
-  __shared__ double ring[W > 1 ? W - 1 : 1][kRing];
+  const int64_t N = a.N, M = a.M, S = a.S;
+  const int band = seg * W + w;
+  const int64_t r0 = (int64_t)band * 64;
+  const int64_t i = r0 + lane;                         // sweep-space row
+  const int qcount = (int)(sweep_steps(M) / kCH);
+  const bool top_ring = band > 0;
+  const bool out_used = (w + 1 < nb_seg) || (seg + 1 < a.nseg);
+  const unsigned Mu = (unsigned)M;
+
+  const LaneCursor cu = lane_cursor(REV, b, i, lane, N, M, a.nbands, S);
+  float* const dbase = a.dsk + cu.base;
+  double* const rbase = a.R + cu.base;
+  const double k2 = a.k2;
+  const double xnm = REV ? a.loss64[b] : 0.0;
+
+  // Final cell (forward sweep): row N-1, column M-1.
+  const int64_t lastrow = N - 1;
+  const bool has_last = !REV && (lastrow >> 6) == band;
+  const int64_t tlast = M - 1 + (lastrow & 63);
+  const int qlast = (int)(tlast / kCH), ulast = (int)(tlast % kCH);
+
+  double cur = kBig;
+  double up = (band == 0 && lane == 0) ? 0.0 : kBig;
+  unsigned seen_wr = 0, seen_rd = 0;
+
+  // Chunk inputs alternate between two register sets: chunk q computes from
+  // one while the requests for chunk q+1 fill the other, so the only wait
+  // on memory is the one for those loads at their first use (stores issued
+  // in between never have to complete).
+  float dnA[kCH], dnB[kCH];
+  double rnA[kCH], rnB[kCH];
+  load_chunk<REV>(dbase, rbase, 0, dnA, rnA);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  auto chunk = [&](int q, const float (&dn)[kCH], const double (&rn)[kCH], float (&dn2)[kCH],
+                   double (&rn2)[kCH]) {
+    const int t0 = q * kCH;
+    // This chunk's loads were issued before the previous chunk's 16 stores;
+    // the vector-memory counter retires in issue order, so allowing 16
+    // operations in flight completes the loads and leaves the stores going.
+    __builtin_amdgcn_s_waitcnt(kWaitVm16);
+    // Top row, columns t0 .. t0+15 (entries past M are never used).
+    double top[kCH];
+    if (top_ring) {
+      const unsigned need = (unsigned)t0 + kCH < Mu ? (unsigned)t0 + kCH : Mu;
+      if (seen_wr < need) seen_wr = lds_wait_ge(&wr[w], need);
+#pragma unroll
+      for (int u = 0; u < kCH; ++u) top[u] = ring[w][(t0 + u) & (kRingC - 1)];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kCH; ++u) top[u] = kBig;
+    }
+    // Unconditional (the last chunk re-reads its own cells), so the
+    // compiler's wait bookkeeping stays exact across the loop.
+    load_chunk<REV>(dbase, rbase, (int64_t)(q + 1 < qcount ? t0 + kCH : t0) * cu.dir, dn2, rn2);
+    double bottom[kCH];
+    float* dp = dbase + (int64_t)t0 * cu.dir;
+    double* rp = rbase + (int64_t)t0 * cu.dir;
+    if (t0 < 64)
+      band_chunk<REV, true>(cur, up, top, dn, rn, bottom, t0, lane, k2, xnm, dp, rp);
+    else
+      band_chunk<REV, false>(cur, up, top, dn, rn, bottom, t0, lane, k2, xnm, dp, rp);
+
+    if (has_last && q == qlast) {
+      double v = 0.0;
+#pragma unroll
+      for (int u = 0; u < kCH; ++u) v = (u == ulast) ? bottom[u] : v;
+      if (lane == (int)(lastrow & 63)) {
+        a.loss64[b] = v;
+        a.loss[b] = (float)(v * a.g_ln2);
+      }
+    }
+    // The top entries of this chunk have long been read: release them.
+    if (top_ring && lane == 0)
+      lds_publish(&rd[w], (unsigned)t0 + kCH < Mu ? (unsigned)t0 + kCH : Mu);
+    // Lane 63's cells (row r0+63, columns t0+u-63) go to the row below.
+    if (out_used) {
+      const int cmax = t0 + kCH - 1 - 63;          // newest column of this chunk
+      if (cmax >= kRingC) {
+        const unsigned need = (unsigned)(cmax - kRingC + 1);
+        if (seen_rd < need) seen_rd = lds_wait_ge(&rd[w + 1], need);
+      }
+      if (lane == 63) {
+        // Columns t0-63 .. t0-48 occupy slots s .. s+15 with s = 1 (mod 16),
+        // so the run is contiguous in the padded ring row and only s = 241
+        // spills into the pad, whose one slot (256) mirrors slot 0.  Slots
+        // of negative columns (first chunks) belong to columns not yet
+        // published, so writing them is harmless.
+        const int s0 = (t0 + kRingC - 63) & (kRingC - 1);
+        double* rw = &ring[w + 1][s0];
+#pragma unroll
+        for (int u = 0; u < kCH; ++u) rw[u] = bottom[u];
+        if (s0 + kCH > kRingC) ring[w + 1][0] = bottom[kRingC - s0];
+        const int done = t0 + kCH - 63;
+        lds_publish(&wr[w + 1], done <= 0 ? 0u : ((unsigned)done < Mu ? (unsigned)done : Mu));
+      }
+    }
+  };
+
+  for (int q = 0; q < qcount; q += 2) {
+    chunk(q, dnA, rnA, dnB, rnB);
+    if (q + 1 < qcount) chunk(q + 1, dnB, rnB, dnA, rnA);
+  }
+}
+
+template <bool REV>
+__global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a) {
+  constexpr int W = kBandsPerWG;
+  __shared__ double ring[W + 1][kRingC + kCH];   // + pad, see band_sweep
+  __shared__ unsigned wr[W + 1], rd[W + 1];
   __shared__ unsigned s_ticket;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   if (threadIdx.x == 0) s_ticket = atomicAdd(&a.ctrl[0], 1u);
+  if (threadIdx.x < W + 1) {
+    wr[threadIdx.x] = 0u;
+    rd[threadIdx.x] = 0u;
+  }
   __syncthreads();
   const unsigned ticket = s_ticket;
   const int seg = (int)(ticket / (unsigned)a.B);
   const int b = (int)(ticket % (unsigned)a.B);
-
-  const int64_t N = a.N, M = a.M, S = a.S;
-  const int band = seg * W + w;
   const int nb_seg = min(W, a.nbands - seg * W);
-  const bool active = w < nb_seg;
-  const int64_t r0 = (int64_t)(active ? band : 0) * 64;
-  const int64_t i = r0 + lane;                        // sweep-space row
-  const bool row_ok = active && i < N;
-  const int qcount = (int)(sweep_steps(M) / kCH);
-  const int qtot = qcount + kLag * (nb_seg - 1);
-  const bool last_in_seg = (w == nb_seg - 1);
-  const bool produce_global = active && last_in_seg && (seg + 1 < a.nseg);
-  const bool consume_global = active && (w == 0) && (seg > 0);
 
-  unsigned* prog_in = a.ctrl + 2 + (int64_t)b * a.nseg + (seg > 0 ? seg - 1 : 0);
-  unsigned* prog_out = a.ctrl + 2 + (int64_t)b * a.nseg + seg;
-  const double* Hin = a.H + ((int64_t)b * a.nseg + (seg > 0 ? seg - 1 : 0)) * M;
-  double* Hout = a.H + ((int64_t)b * a.nseg + seg) * M;
-
-  const LaneCursor cu = lane_cursor(REV, b, i, lane, N, M, a.nbands, S);
-  float* dsk = a.dsk;
-  double* rsk = a.R;
-  const double k2 = a.k2;
-  const double xnm = REV ? a.loss64[b] : 0.0;
-
-  // Boundary: R[-1,-1] = 0 reaches the first row's first cell as the
-  // diagonal input of step 0 (lane 0 of band 0); all else is +inf.
-  double cur = kBig;
-  double up = (lane == 0 && r0 == 0) ? 0.0 : kBig;
-  unsigned avail = 0;
-
-  // Position of the final cell (forward sweep): row N-1, column M-1.
-  const int64_t lastrow = N - 1;
-  const bool has_last = !REV && active && (lastrow >> 6) == band;
-  const int64_t tlast = M - 1 + (lastrow & 63);
-  const int qlast = (int)(tlast / kCH), ulast = (int)(tlast % kCH);
-
-  // Every global access below is unconditional (padding cells have storage)
-  // and the data of chunk q+1 is requested while chunk q computes, so memory
-  // latency stays off the per-step dependency chain.
-  float dn[kCH];
-  double rn[kCH];
-  double tn[kCH];  // raw top-row values from the segment above (masked at use)
-#define SDTW_LOAD_CHUNK(qq, D_, R_)                                       \
-  {                                                                       \
-    const int64_t t0n = (int64_t)(qq) * kCH;                              \
-    _Pragma("unroll") for (int u = 0; u < kCH; ++u) {                     \
-      const int64_t e = cu.base + (t0n + u) * cu.dir;                     \
-      D_[u] = dsk[e];                                                     \
-      if (REV) R_[u] = rsk[e];                                            \
-    }                                                                     \
+  if (w == W) {
+    const int64_t pb = (int64_t)b * a.nseg;
+    segment_io_wave(seg > 0, seg + 1 < a.nseg, a.ctrl + 2 + pb + (seg > 0 ? seg - 1 : 0),
+                    a.ctrl + 2 + pb + seg, a.H + (pb + (seg > 0 ? seg - 1 : 0)) * a.M,
+                    a.H + (pb + seg) * a.M, ring[0], &wr[0], &rd[0], ring[W], &wr[W],
+                    &rd[W], (unsigned)a.M, lane);
+  } else if (w < nb_seg) {
+    band_sweep<REV>(a, b, seg, w, nb_seg, ring, wr, rd, lane);
   }
-  // Wait (bounded) until the segment above has published `need` columns.
-#define SDTW_AWAIT(need_)                                                 \
-  {                                                                       \
-    const unsigned need = (unsigned)(need_);                              \
-    if (avail < need) avail = await_progress(prog_in, need);              \
-  }
-#define SDTW_LOAD_TOP(qq, T_)                                             \
-  {                                                                       \
-    const int64_t t0n = (int64_t)(qq) * kCH;                              \
-    _Pragma("unroll") for (int u = 0; u < kCH; ++u) {                     \
-      const int64_t col = t0n + u;                                        \
-      T_[u] = Hin[col < M ? col : M - 1];                                 \
-    }                                                                     \
-  }
-
-  if (active) SDTW_LOAD_CHUNK(0, dn, rn);
-  if (consume_global) {
-    SDTW_AWAIT(imin64(M, kCH + kSlack));
-    SDTW_LOAD_TOP(0, tn);
-  }
-  // Drain the first requests here, so that inside the loop the only loads
-  // in flight are the ones for the next chunk (the counter-based waits are
-  // then exact instead of covering those as well).
-  __builtin_amdgcn_s_waitcnt(0);
-
-  for (int Q = 0; Q < qtot; ++Q) {
-    const int q = Q - kLag * w;
-    if (active && q >= 0 && q < qcount) {
-      const int64_t t0 = (int64_t)q * kCH;
-      // Requests for chunk q+1 go out first, into fresh registers.
-      float dn2[kCH];
-      double rn2[kCH];
-      double tn2[kCH];
-      const bool more = q + 1 < qcount;
-      if (more) {
-        SDTW_LOAD_CHUNK(q + 1, dn2, rn2);
-        if (consume_global) {
-          SDTW_AWAIT(imin64(M, t0 + 2 * kCH));
-          SDTW_LOAD_TOP(q + 1, tn2);
-        }
-      }
-      double top[kCH];
-      if (r0 == 0) {
-#pragma unroll
-        for (int u = 0; u < kCH; ++u) top[u] = kBig;
-      } else if (!consume_global) {
-#pragma unroll
-        for (int u = 0; u < kCH; ++u) top[u] = ring[w - 1][(t0 + u) & (kRing - 1)];
-      } else {
-#pragma unroll
-        for (int u = 0; u < kCH; ++u) top[u] = tn[u];
-      }
-
-      double bottom[kCH];
-      if (t0 < 64)
-        band_chunk<REV, true>(cur, up, top, dn, rn, bottom, t0, lane, row_ok, k2, xnm,
-                              dsk, rsk, cu);
-      else
-        band_chunk<REV, false>(cur, up, top, dn, rn, bottom, t0, lane, row_ok, k2, xnm,
-                               dsk, rsk, cu);
-
-      if (has_last && q == qlast) {
-        double v = 0.0;
-#pragma unroll
-        for (int u = 0; u < kCH; ++u) v = (u == ulast) ? bottom[u] : v;
-        if (lane == (int)(lastrow & 63)) {
-          a.loss64[b] = v;
-          a.loss[b] = (float)(v * a.g_ln2);
-        }
-      }
-
-      // Hand lane 63's cells (row r0+63, columns t0+u-63) to the band below.
-      if (!last_in_seg) {
-        if (lane == 63) {
-#pragma unroll
-          for (int u = 0; u < kCH; ++u) ring[w][(t0 + u - 63) & (kRing - 1)] = bottom[u];
-        }
-      } else if (produce_global) {
-        if (lane == 63) {
-#pragma unroll
-          for (int u = 0; u < kCH; ++u) {
-            const int64_t col = t0 + u - 63;
-            if (col >= 0 && col < M) Hout[col] = bottom[u];
-          }
-          if (((q + 1) % kPub) == 0 || q == qcount - 1) {
-            int64_t done = t0 + kCH - 63;
-            done = done < 0 ? 0 : imin64(done, M);
-            __hip_atomic_store(prog_out, (unsigned)done, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
-      // Rotate the prefetched chunk in; its loads were issued a chunk ago.
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < kCH; ++u) {
-          dn[u] = dn2[u];
-          if (REV) rn[u] = rn2[u];
-          if (consume_global) tn[u] = tn2[u];
-        }
-      }
-    }
-    __syncthreads();
-  }
-#undef SDTW_LOAD_CHUNK
-#undef SDTW_AWAIT
-#undef SDTW_LOAD_TOP
   release_ctrl(a.ctrl, (int64_t)a.B * a.nseg);
 }
 
@@ -268,10 +268,11 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
 hipError_t launch_dp(const DPArgs& a, bool reverse, bool fused, hipStream_t s) {
   if (fused) return launch_dp_fused(a, reverse, s);
   const unsigned grid = (unsigned)a.B * (unsigned)a.nseg;
+  const dim3 block((kBandsPerWG + 1) * 64);
   if (reverse)
-    hipLaunchKernelGGL(k_dp_unfused<true>, dim3(grid), dim3(kBandsPerWG * 64), 0, s, a);
+    hipLaunchKernelGGL(k_dp_unfused<true>, dim3(grid), block, 0, s, a);
   else
-    hipLaunchKernelGGL(k_dp_unfused<false>, dim3(grid), dim3(kBandsPerWG * 64), 0, s, a);
+    hipLaunchKernelGGL(k_dp_unfused<false>, dim3(grid), block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ constexpr int kRing = 128;                   // LDS ring columns per boundary
 constexpr int kPub = 4;                      // chunks between global publishes
 constexpr int kSlack = 96;                   // extra columns awaited at start
 constexpr uint32_t kSpinCap = 1u << 25;      // polls before a wait gives up
+constexpr uint32_t kLdsSpinCap = 1u << 22;   // the same for waits on LDS counters
 static_assert(kRing >= (kLag + 3) * kCH, "LDS ring too small");
 static_assert(kCH == 16, "band_chunk unrolls 16 steps");
 
@@ -50,6 +51,101 @@ __device__ __forceinline__ unsigned await_progress(const unsigned* prog, unsigne
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return v < need ? need : v;
+}
+
+// ---------------------------------------------------------------------------
+// Decoupled bands.  Inside a workgroup every band wave runs at its own pace;
+// the row a band hands to the band below travels through an LDS ring of
+// kRingC columns with two counters: wr = columns written (all columns below
+// it are valid), rd = columns released by the reader (their slots may be
+// overwritten).  LDS operations of one wave are performed in issue order, so
+// a counter written after the ring entries never runs ahead of them, and a
+// read issued after the counter was seen never sees older entries.
+// ---------------------------------------------------------------------------
+constexpr int kRingC = 256;                  // columns per LDS ring (power of 2)
+
+// Bounded wait until *p >= need; returns the last value read (>= need unless
+// the cap was hit, in which case the caller proceeds on stale data rather
+// than hang).
+__device__ __forceinline__ unsigned lds_wait_ge(const unsigned* p, unsigned need) {
+  unsigned v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  for (uint32_t spin = 0; v < need && spin < kLdsSpinCap; ++spin) {
+    __builtin_amdgcn_s_sleep(1);
+    v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return v;
+}
+
+// Publish a counter after this wave's LDS writes.  The LDS unit performs one
+// wave's operations in issue order, so the counter can never become
+// visible before the data written ahead of it; only the compiler has to be
+// kept from reordering, and no wait for completion is needed.
+__device__ __forceinline__ void lds_publish(unsigned* p, unsigned v) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// The hand-off between consecutive workgroups of one pair ("segments") is
+// done by one extra wave per workgroup, so the band waves never wait on
+// global memory:
+//  - input: poll the previous segment's published column count, copy the
+//    new columns of its bottom row from global memory into ring_in (the top
+//    ring of band 0);
+//  - output: copy what the last band wrote into ring_out to global memory,
+//    wait for those stores, then publish the new column count.
+// Row values and counts are accessed with relaxed agent-scope atomics
+// (device-coherent loads and stores that bypass the per-XCD caches); the
+// explicit vmcnt(0) wait between the row stores and the count store orders
+// them, so no cache write-back or invalidation is needed.  A segment waits
+// only on a smaller ticket, which is running, so the loop ends; the poll cap
+// guarantees the wave exits regardless.
+__device__ __forceinline__ void segment_io_wave(
+    bool do_in, bool do_out, const unsigned* prog_in, unsigned* prog_out,
+    const double* Hin, double* Hout, double* ring_in, unsigned* wr_in,
+    const unsigned* rd_in, const double* ring_out, const unsigned* wr_out,
+    unsigned* rd_out, unsigned M, int lane) {
+  unsigned fetched = 0, known_in = 0, pub = 0;
+  for (uint32_t spin = 0; spin < kSpinCap; ++spin) {
+    const bool in_left = do_in && fetched < M;
+    const bool out_left = do_out && pub < M;
+    if (!in_left && !out_left) break;
+    bool moved = false;
+    if (in_left) {
+      if (known_in <= fetched)
+        known_in = __hip_atomic_load(prog_in, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned room =
+          __hip_atomic_load(rd_in, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + kRingC;
+      const unsigned lim = known_in < room ? known_in : room;
+      if (lim > fetched) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        for (unsigned c = fetched + lane; c < lim; c += 64)
+          ring_in[c & (kRingC - 1)] =
+              __hip_atomic_load(Hin + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) lds_publish(wr_in, lim);
+        fetched = lim;
+        moved = true;
+      }
+    }
+    if (out_left) {
+      const unsigned avail = lds_wait_ge(wr_out, 0);
+      if (avail > pub) {
+        for (unsigned c = pub + lane; c < avail; c += 64)
+          __hip_atomic_store(Hout + c, ring_out[c & (kRingC - 1)], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) lds_publish(rd_out, avail);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0)
+          __hip_atomic_store(prog_out, avail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pub = avail;
+        moved = true;
+      }
+    }
+    if (!moved) __builtin_amdgcn_s_sleep(2);
+  }
 }
 
 // Per-lane view of one band of a band-step array: the element a sweep step t
