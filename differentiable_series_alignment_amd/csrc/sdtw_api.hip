@@ -18,11 +18,12 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // The cell arrays use the band-step layout of sdtw_kernels.h.
 struct Layout {
   int64_t nbands = 0, nseg = 0, S = 0;
-  size_t ctrl = 0, ctrl_words = 0;  // two sweeps x (ticket, done, progress)
+  size_t ctrl = 0, ctrl_words = 0;  // ticket, done, per-segment progress
   size_t loss64 = 0;                // fp64 [B]
-  size_t H = 0;                     // fp64 [B, nseg, M]
+  size_t H = 0;                     // fp64 [2, B, nseg, M] segment hand-off rows
   size_t R = 0;                     // fp64 band-step forward state
-  size_t dist = 0;                  // fp32 band-step distances / E (unfused)
+  size_t R2 = 0;                    // fp64 band-step reverse soft-min parts (unfused)
+  size_t dist = 0;                  // fp32 band-step distances, then E (unfused)
   size_t total = 0;
 };
 
@@ -60,10 +61,12 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   L->loss64 = off;
   off += align_up((size_t)B * 8);
   L->H = off;
-  off += align_up((size_t)B * (size_t)L->nseg * (size_t)M * 8);
+  off += align_up(2 * (size_t)B * (size_t)L->nseg * (size_t)M * 8);
   L->R = off;
   off += align_up(cells * 8);
   if (mode == SDTW_MODE_UNFUSED) {
+    L->R2 = off;
+    off += align_up(cells * 8);
     L->dist = off;
     off += align_up(cells * 4);
   }
@@ -73,8 +76,10 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
 
 bool gamma_ok(float g) { return isfinite(g) && g > 0.f; }
 
-// Control words: the forward sweep uses the first half, the reverse sweep the
-// second; each sweep's kernel leaves its half zeroed when it finishes.
+// Control words: the unfused launch (both sweeps) uses them from the start;
+// the fused sweeps run as separate launches, the forward one on the first
+// half and the reverse one on the second.  Every launch leaves its words
+// zeroed when it finishes.
 DPArgs dp_args(const Layout& L, char* ws, const float* x, const float* y,
                int64_t B, int64_t N, int64_t M, int64_t D, float gamma,
                bool reverse) {
@@ -86,6 +91,7 @@ DPArgs dp_args(const Layout& L, char* ws, const float* x, const float* y,
   a.loss64 = reinterpret_cast<double*>(ws + L.loss64);
   a.H = reinterpret_cast<double*>(ws + L.H);
   a.R = reinterpret_cast<double*>(ws + L.R);
+  a.R2 = L.R2 ? reinterpret_cast<double*>(ws + L.R2) : nullptr;
   a.dsk = L.dist ? reinterpret_cast<float*>(ws + L.dist) : nullptr;
   a.N = N;
   a.S = L.S;
@@ -153,8 +159,14 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
   // per forward (later launches find them cleared by the kernels).
   hipError_t e = sdtw::launch_zero_u32(reinterpret_cast<unsigned*>(ws + L.ctrl),
                                        (int64_t)L.ctrl_words, s);
-  if (e == hipSuccess && !fused) e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, s);
-  if (e == hipSuccess) e = sdtw::launch_dp(a, false, fused, s);
+  if (fused) {
+    if (e == hipSuccess) e = sdtw::launch_dp_fused(a, false, s);
+  } else {
+    // Both sweeps at once: the loss comes from the forward one, and the
+    // reverse one leaves what the backward needs besides the forward state.
+    if (e == hipSuccess) e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, s);
+    if (e == hipSuccess) e = sdtw::launch_dp_both(a, s);
+  }
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
 }
 
@@ -169,7 +181,7 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
   if (st != SDTW_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
-  DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma, true);
+  DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma, mode == SDTW_MODE_FUSED);
   if (mode == SDTW_MODE_FUSED) {
     // One reverse sweep per slice of D; it writes dx, adds into dy and, if
     // asked, writes E.  Nothing to compute when no output is requested.
@@ -180,13 +192,16 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
     a.align = align;
     hipError_t e = hipSuccess;
     if (grad_y) e = sdtw::launch_zero_f32(grad_y, B * M * D, s);
-    if (e == hipSuccess) e = sdtw::launch_dp(a, true, true, s);
+    if (e == hipSuccess) e = sdtw::launch_dp_fused(a, true, s);
     return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
   }
-  hipError_t e = sdtw::launch_dp(a, true, false, s);
+  // Unfused: both sweeps ran in the forward; the chain rule forms E from
+  // their states (the distances are not read again), so repeated backward
+  // calls on one forward are all valid.
+  if (!grad_x && !grad_y && !align) return SDTW_OK;
+  hipError_t e = sdtw::launch_chain(a.dsk, a.R, a.R2, a.loss64, x, y, grad_loss, grad_x,
+                                    grad_y, B, N, M, D, L.S, s);
   if (e == hipSuccess && align) e = sdtw::launch_unskew(a.dsk, align, B, N, M, L.S, s);
-  if (e == hipSuccess && (grad_x || grad_y))
-    e = sdtw::launch_chain(a.dsk, x, y, grad_loss, grad_x, grad_y, B, N, M, D, L.S, s);
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
 }
 

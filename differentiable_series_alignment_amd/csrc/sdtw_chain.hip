@@ -49,12 +49,60 @@ struct Stage32 {
   }
 };
 
+// The same 32-step window, formed from the two sweeps' states instead:
+// E = 2^(Xnm - X - T') for each cell, written both to the LDS ring and to
+// the band-step E array (the distance array, no longer needed) for the
+// column pass and the optional alignment output.
+typedef double v2d __attribute__((ext_vector_type(2)));
+struct StageXT {
+  double xv[8], tv[8];
+  int64_t off[2];
+  __device__ __forceinline__ void load(const double* xbp, const double* tbp, int64_t s0,
+                                       int64_t smax) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = (int)threadIdx.x * 4 + 1024 * k;
+      int64_t st = s0 + e / 64;
+      st = st < smax ? st : smax - 1;
+      off[k] = st * 64 + (e & 63);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v2d a = *reinterpret_cast<const v2d*>(xbp + off[k] + 2 * h);
+        const v2d c = *reinterpret_cast<const v2d*>(tbp + off[k] + 2 * h);
+        xv[4 * k + 2 * h] = a[0];
+        xv[4 * k + 2 * h + 1] = a[1];
+        tv[4 * k + 2 * h] = c[0];
+        tv[4 * k + 2 * h + 1] = c[1];
+      }
+    }
+  }
+  __device__ __forceinline__ void store(float* ring, float* ebp, int64_t s0, double xnm) const {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = (int)threadIdx.x * 4 + 1024 * k;
+      const int slot = (int)((s0 + e / 64) & (kRingSteps - 1));
+      v4f q;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        q[j] = align_entry(xnm, xv[4 * k + j], tv[4 * k + j]);
+        ring[slot * kRingPitch + (e & 63) + j] = q[j];
+      }
+      __builtin_nontemporal_store(q, reinterpret_cast<v4f*>(ebp + off[k]));
+    }
+  }
+};
+
 // dx for one band (64 rows) of one pair, columns of D in [d0, d0 + 128).
 // Wave w: row tile w & 1, d tiles (w >> 1) + 2t.  Column blocks of 32 need
 // band steps [j0, j0 + 96); the next block's 32 new steps are fetched into
-// registers while the current block computes.
-template <int NTW>
-__global__ __launch_bounds__(256) void k_chain_rows(const float* __restrict__ esk,
+// registers while the current block computes.  FORM: the window comes from
+// the sweeps' states and E is formed (and stored) on the way; otherwise it
+// is read from the stored E.  GX = false forms E only.
+template <int NTW, bool GX, bool FORM>
+__global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
+                                                    const double* __restrict__ R,
+                                                    const double* __restrict__ R2,
+                                                    const double* __restrict__ loss64,
                                                     const float* __restrict__ x,
                                                     const float* __restrict__ y,
                                                     const float* __restrict__ gl,
@@ -69,7 +117,11 @@ __global__ __launch_bounds__(256) void k_chain_rows(const float* __restrict__ es
   const int lr = 32 * rt + r;
   const int64_t row = band * 64 + lr;
   const bool row_ok = row < N;
-  const float* bandp = esk + ((b * nbands + band) * S + kSkewOff) * 64;
+  const int64_t boff = ((b * nbands + band) * S + kSkewOff) * 64;
+  float* bandp = esk + boff;
+  const double* xbp = R + boff;
+  const double* tbp = R2 + boff;
+  const double xnm = FORM ? loss64[b] : 0.0;
   const int64_t smax = S - kSkewOff;
   const float* yb = y + b * M * D;
   int64_t dcol[NTW];
@@ -87,9 +139,15 @@ __global__ __launch_bounds__(256) void k_chain_rows(const float* __restrict__ es
 
   const int64_t nblk = (M + 31) / 32;
   Stage32 st;
+  StageXT sx;
   for (int64_t s0 = 0; s0 < 96; s0 += 32) {
-    st.load(bandp, s0, smax);
-    st.store(ring, s0);
+    if (FORM) {
+      sx.load(xbp, tbp, s0, smax);
+      sx.store(ring, bandp, s0, xnm);
+    } else {
+      st.load(bandp, s0, smax);
+      st.store(ring, s0);
+    }
   }
   float yv[16][NTW], yn[16][NTW];
   auto load_y = [&](int64_t j0, float (&Y)[16][NTW]) {
@@ -101,7 +159,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(const float* __restrict__ es
       for (int t = 0; t < NTW; ++t) Y[s][t] = yb[j * D + dcol[t]];
     }
   };
-  load_y(0, yv);
+  if (GX) load_y(0, yv);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -109,29 +167,40 @@ __global__ __launch_bounds__(256) void k_chain_rows(const float* __restrict__ es
     const int64_t j0 = kb * 32;
     const bool more = kb + 1 < nblk;
     if (more) {
-      st.load(bandp, j0 + 96, smax);
-      load_y(j0 + 32, yn);
+      if (FORM)
+        sx.load(xbp, tbp, j0 + 96, smax);
+      else
+        st.load(bandp, j0 + 96, smax);
+      if (GX) load_y(j0 + 32, yn);
     }
+    if (GX) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int64_t j = j0 + 2 * s + h;
-      const float a =
-          (row_ok && j < M) ? ring[(int)((j + lr) & (kRingSteps - 1)) * kRingPitch + lr] : 0.f;
-      rsum += a;
+      for (int s = 0; s < 16; ++s) {
+        const int64_t j = j0 + 2 * s + h;
+        const float a =
+            (row_ok && j < M) ? ring[(int)((j + lr) & (kRingSteps - 1)) * kRingPitch + lr] : 0.f;
+        rsum += a;
 #pragma unroll
-      for (int t = 0; t < NTW; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, yv[s][t], acc[t], 0, 0, 0);
+        for (int t = 0; t < NTW; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, yv[s][t], acc[t], 0, 0, 0);
+      }
     }
     __syncthreads();
     if (more) {
-      st.store(ring, j0 + 96);
+      if (FORM)
+        sx.store(ring, bandp, j0 + 96, xnm);
+      else
+        st.store(ring, j0 + 96);
+      if (GX) {
 #pragma unroll
-      for (int s = 0; s < 16; ++s)
+        for (int s = 0; s < 16; ++s)
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) yv[s][t] = yn[s][t];
+          for (int t = 0; t < NTW; ++t) yv[s][t] = yn[s][t];
+      }
     }
     __syncthreads();
   }
+  if (!GX) return;
 
   rsum += __shfl_xor(rsum, 32, 64);
   float rs[16];
@@ -248,32 +317,54 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
   }
 }
 
-hipError_t launch_chain(const float* esk, const float* x, const float* y,
-                        const float* gl, float* gx, float* gy, int64_t B,
-                        int64_t N, int64_t M, int64_t D, int64_t S,
-                        hipStream_t s) {
+template <int NTW, bool FORM>
+static void launch_rows(dim3 grid, hipStream_t s, float* esk, const double* R,
+                        const double* R2, const double* loss64, const float* x,
+                        const float* y, const float* gl, float* gx, int64_t N, int64_t M,
+                        int64_t D, int64_t S, int nb, int64_t d0) {
+  if (gx)
+    hipLaunchKernelGGL((k_chain_rows<NTW, true, FORM>), grid, dim3(256), 0, s, esk, R, R2,
+                       loss64, x, y, gl, gx, N, M, D, S, nb, d0);
+  else
+    hipLaunchKernelGGL((k_chain_rows<1, false, FORM>), grid, dim3(256), 0, s, esk, R, R2,
+                       loss64, x, y, gl, gx, N, M, D, S, nb, d0);
+}
+
+hipError_t launch_chain(float* esk, const double* R, const double* R2,
+                        const double* loss64, const float* x, const float* y,
+                        const float* gl, float* gx, float* gy, int64_t B, int64_t N,
+                        int64_t M, int64_t D, int64_t S, hipStream_t s) {
   const int nb = (int)((N + 63) / 64);
+  // Row pass(es): the first forms E; later D slices read it back.
   for (int64_t d0 = 0; d0 < D; d0 += 128) {
+    if (d0 > 0 && !gx) break;
     const int64_t dw = D - d0 < 128 ? D - d0 : 128;
     const bool two = dw > 64;  // more than two 32-wide d tiles
-    if (gx) {
-      dim3 grid((unsigned)nb, (unsigned)B);
+    const dim3 grid((unsigned)nb, (unsigned)B);
+    if (d0 == 0) {
       if (two)
-        hipLaunchKernelGGL(k_chain_rows<2>, grid, dim3(256), 0, s, esk, x, y, gl, gx, N, M, D, S, nb, d0);
+        launch_rows<2, true>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0);
       else
-        hipLaunchKernelGGL(k_chain_rows<1>, grid, dim3(256), 0, s, esk, x, y, gl, gx, N, M, D, S, nb, d0);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    if (gy) {
-      dim3 grid((unsigned)((M + 63) / 64), (unsigned)B);
+        launch_rows<1, true>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0);
+    } else {
       if (two)
-        hipLaunchKernelGGL(k_chain_cols<2>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0);
+        launch_rows<2, false>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0);
       else
-        hipLaunchKernelGGL(k_chain_cols<1>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+        launch_rows<1, false>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!gy) return hipSuccess;
+  for (int64_t d0 = 0; d0 < D; d0 += 128) {
+    const int64_t dw = D - d0 < 128 ? D - d0 : 128;
+    const dim3 grid((unsigned)((M + 63) / 64), (unsigned)B);
+    if (dw > 64)
+      hipLaunchKernelGGL(k_chain_cols<2>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0);
+    else
+      hipLaunchKernelGGL(k_chain_cols<1>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }

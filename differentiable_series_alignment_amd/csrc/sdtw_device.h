@@ -50,23 +50,31 @@ __device__ __forceinline__ double max_nonan(double a, double b) {
   return r;
 }
 
-// One cell of the recurrence in base-2 units X = R * log2(e) / g:
-//   X = d + m - log2(2^(m-a) + 2^(m-b) + 2^(m-c)),  m = min(a, b, c),
-// which is R = D + softmin_g(...) scaled by log2(e)/g.  The term of the
-// minimum is exactly 1, so only the other two are exponentiated: with
-// m1 = min(a,c), p = max(a,c), m = min(m1,b), q = max(m1,b), the multiset
-// {a,b,c} is {m,p,q}.  State and differences are fp64; the exponentials and
-// the logarithm are the fp32 hardware instructions applied to the (small,
-// non-positive) fp64 differences.
-__device__ __forceinline__ double softmin2_cell(double a, double b, double c,
-                                                double d) {
+// Soft-minimum part of one cell of the recurrence in base-2 units
+// X = R * log2(e) / g:
+//   X = d + T,  T = m - log2(2^(m-a) + 2^(m-b) + 2^(m-c)),  m = min(a, b, c),
+// which is R = D + softmin_g(...) scaled by log2(e)/g; this returns T.  The
+// term of the minimum is exactly 1, so only the other two are
+// exponentiated: with m1 = min(a,c), p = max(a,c), m = min(m1,b),
+// q = max(m1,b), the multiset {a,b,c} is {m,p,q}.  State and differences
+// are fp64; the exponentials and the logarithm are the fp32 hardware
+// instructions applied to the (small, non-positive) fp64 differences.
+__device__ __forceinline__ double softmin2_part(double a, double b, double c) {
   const double m1 = min_nonan(a, c);
   const double p = max_nonan(a, c);
   const double m = min_nonan(m1, b);
   const double q = max_nonan(m1, b);
   const float ep = hw_exp2((float)(m - p));
   const float eq = hw_exp2((float)(m - q));
-  return (m + d) - (double)hw_log2((1.0f + ep) + eq);
+  return m - (double)hw_log2((1.0f + ep) + eq);
+}
+
+// Alignment-matrix entry from the two sweeps: with X the forward state of
+// the cell, T' the soft-minimum part of the reverse state (the reverse
+// state without the cell's own distance) and Xnm the final forward state,
+//   log2 E = Xnm + d - X - X' = Xnm - X - T'.
+__device__ __forceinline__ float align_entry(double xnm, double x, double tr) {
+  return hw_exp2((float)((xnm - x) - tr));
 }
 
 __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }

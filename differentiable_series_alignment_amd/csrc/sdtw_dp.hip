@@ -28,12 +28,15 @@
 //
 // The reverse sweep runs the same recurrence on both sequences reversed,
 // which yields R'[i,j], the soft-DTW value of the suffix alignment from
-// (i,j) to (N-1,M-1) that includes Dist[i,j].  In log space the alignment
-// matrix is then
+// (i,j) to (N-1,M-1) that includes Dist[i,j].  Splitting every alignment
+// path at (i,j) gives the alignment matrix in log space,
 //   ln E[i,j] = (R[N-1,M-1] + Dist[i,j] - R[i,j] - R'[i,j]) / g,
-// and E is exponentiated only at the end, cell by cell (the log-space
-// backward with a final exp of the review page, section "Proposed method";
-// the identity follows from splitting every alignment path at (i,j)).
+// exponentiated only at the end (the log-space backward with a final exp of
+// the review page "SoftDTW-CUDA-Torch", section "Proposed method").  The two
+// sweeps are independent, so one launch runs both at once: the forward
+// sweep keeps X = R log2(e)/g, the reverse sweep keeps T' = (R' - Dist)
+// log2(e)/g, its soft-minimum part, and E = 2^(Xnm - X - T') is formed
+// later, by the chain-rule kernel.
 #include "sdtw_dp_common.h"
 
 namespace sdtw {
@@ -49,35 +52,28 @@ __global__ void k_zero_u32(unsigned* p, int64_t n) {
 // stand-in) without touching the dependency chain; the corner R[-1,-1] = 0
 // enters through the initial state of lane 0 of the first band.  Cells past
 // the last column or below the last row compute unused values in padding
-// storage; no real cell depends on them.
+// storage; no real cell depends on them.  The forward sweep stores X, the
+// reverse sweep its soft-minimum part T'.
 template <bool REV, bool MASK>
 __device__ __forceinline__ void band_chunk(double& cur, double& up, const double (&top)[16],
-                                           const float (&dn)[16], const double (&rn)[16],
-                                           double (&bottom)[16], int t0, int lane, double k2,
-                                           double xnm, float* __restrict__ dp,
-                                           double* __restrict__ rp) {
+                                           const float (&dn)[16], double (&bottom)[16],
+                                           int t0, int lane, double k2,
+                                           double* __restrict__ sp) {
   constexpr int dir = REV ? -64 : 64;
-  // Steps 8..15 address from a second base so every access of the chunk
-  // is base + immediate offset.
-  float* const dp8 = dp + 8 * dir;
-  double* const rp8 = rp + 8 * dir;
+  // Steps 8..15 address from a second base so every store of the chunk is
+  // base + immediate offset.
+  double* const sp8 = sp + 8 * dir;
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     double d = (double)dn[u] * k2;
     if (MASK) d = (t0 + u < lane) ? kBig : d;
     const double upn = wave_shr1(cur, top[u]);
-    const double c = softmin2_cell(up, upn, cur, d);
+    const double t = softmin2_part(up, upn, cur);
+    const double c = t + d;
     up = upn;
     cur = c;
     bottom[u] = c;
-    if (!REV) {
-      __builtin_nontemporal_store(c, (u < 8 ? rp : rp8) + (u & 7) * dir);
-    } else {
-      // ln E = (R[N-1,M-1] + Dist - R - R') / g, i.e. in base-2 units
-      // log2 E = Xnm + d - X - X'; the exponential is taken last.
-      __builtin_nontemporal_store(hw_exp2((float)((xnm + d) - (rn[u] + c))),
-                                  (u < 8 ? dp : dp8) + (u & 7) * dir);
-    }
+    __builtin_nontemporal_store(REV ? t : c, (u < 8 ? sp : sp8) + (u & 7) * dir);
   }
 }
 
@@ -86,20 +82,14 @@ __device__ __forceinline__ void band_chunk(double& cur, double& up, const double
 // operations are outstanding and does not wait on the other counters.
 constexpr int kWaitVm16 = (1 << 14) | (7 << 4) | (15 << 8);
 
-// Loads of one chunk's inputs (16 steps from `off`), two bases as above.
+// Loads of one chunk's distances (16 steps from `off`), two bases as above.
 template <bool REV>
-__device__ __forceinline__ void load_chunk(const float* dbase, const double* rbase, int64_t off,
-                                           float (&dn)[16], double (&rn)[16]) {
+__device__ __forceinline__ void load_chunk(const float* dbase, int64_t off, float (&dn)[16]) {
   constexpr int dir = REV ? -64 : 64;
   const float* d0 = dbase + off;
   const float* d8 = d0 + 8 * dir;
-  const double* r0 = rbase + off;
-  const double* r8 = r0 + 8 * dir;
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    dn[u] = (u < 8 ? d0 : d8)[(u & 7) * dir];
-    if (REV) rn[u] = (u < 8 ? r0 : r8)[(u & 7) * dir];
-  }
+  for (int u = 0; u < 16; ++u) dn[u] = (u < 8 ? d0 : d8)[(u & 7) * dir];
 }
 
 // One band of one pair, swept column chunk by column chunk.  The band's top
@@ -108,8 +98,8 @@ __device__ __forceinline__ void load_chunk(const float* dbase, const double* rba
 // reads it.
 template <bool REV>
 __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int w, int nb_seg,
-                                           double (*ring)[kRingC + kCH], unsigned* wr, unsigned* rd,
-                                           int lane) {
+                                           double (*ring)[kRingC + kCH], unsigned* wr,
+                                           unsigned* rd, int lane) {
   constexpr int W = kBandsPerWG;
   const int64_t N = a.N, M = a.M, S = a.S;
   const int band = seg * W + w;
@@ -121,10 +111,9 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
   const unsigned Mu = (unsigned)M;
 
   const LaneCursor cu = lane_cursor(REV, b, i, lane, N, M, a.nbands, S);
-  float* const dbase = a.dsk + cu.base;
-  double* const rbase = a.R + cu.base;
+  const float* const dbase = a.dsk + cu.base;
+  double* const sbase = (REV ? a.R2 : a.R) + cu.base;
   const double k2 = a.k2;
-  const double xnm = REV ? a.loss64[b] : 0.0;
 
   // Final cell (forward sweep): row N-1, column M-1.
   const int64_t lastrow = N - 1;
@@ -137,16 +126,12 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
   unsigned seen_wr = 0, seen_rd = 0;
 
   // Chunk inputs alternate between two register sets: chunk q computes from
-  // one while the requests for chunk q+1 fill the other, so the only wait
-  // on memory is the one for those loads at their first use (stores issued
-  // in between never have to complete).
+  // one while the requests for chunk q+1 fill the other.
   float dnA[kCH], dnB[kCH];
-  double rnA[kCH], rnB[kCH];
-  load_chunk<REV>(dbase, rbase, 0, dnA, rnA);
+  load_chunk<REV>(dbase, 0, dnA);
   __builtin_amdgcn_s_waitcnt(0);
 
-  auto chunk = [&](int q, const float (&dn)[kCH], const double (&rn)[kCH], float (&dn2)[kCH],
-                   double (&rn2)[kCH]) {
+  auto chunk = [&](int q, const float (&dn)[kCH], float (&dn2)[kCH]) {
     const int t0 = q * kCH;
     // This chunk's loads were issued before the previous chunk's 16 stores;
     // the vector-memory counter retires in issue order, so allowing 16
@@ -165,14 +150,13 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
     }
     // Unconditional (the last chunk re-reads its own cells), so the
     // compiler's wait bookkeeping stays exact across the loop.
-    load_chunk<REV>(dbase, rbase, (int64_t)(q + 1 < qcount ? t0 + kCH : t0) * cu.dir, dn2, rn2);
+    load_chunk<REV>(dbase, (int64_t)(q + 1 < qcount ? t0 + kCH : t0) * cu.dir, dn2);
     double bottom[kCH];
-    float* dp = dbase + (int64_t)t0 * cu.dir;
-    double* rp = rbase + (int64_t)t0 * cu.dir;
+    double* sp = sbase + (int64_t)t0 * cu.dir;
     if (t0 < 64)
-      band_chunk<REV, true>(cur, up, top, dn, rn, bottom, t0, lane, k2, xnm, dp, rp);
+      band_chunk<REV, true>(cur, up, top, dn, bottom, t0, lane, k2, sp);
     else
-      band_chunk<REV, false>(cur, up, top, dn, rn, bottom, t0, lane, k2, xnm, dp, rp);
+      band_chunk<REV, false>(cur, up, top, dn, bottom, t0, lane, k2, sp);
 
     if (has_last && q == qlast) {
       double v = 0.0;
@@ -211,12 +195,17 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
   };
 
   for (int q = 0; q < qcount; q += 2) {
-    chunk(q, dnA, rnA, dnB, rnB);
-    if (q + 1 < qcount) chunk(q + 1, dnB, rnB, dnA, rnA);
+    chunk(q, dnA, dnB);
+    if (q + 1 < qcount) chunk(q + 1, dnB, dnA);
   }
 }
 
-template <bool REV>
+// Both sweeps in one launch.  Tickets alternate between the sweeps, so the
+// forward and reverse workgroups of a pair start together; within a sweep a
+// segment waits only on the previous segment, which holds a smaller ticket.
+// Control words: [0] ticket, [1] finished workgroups, [2 + sweep*B*nseg +
+// b*nseg + s] columns published by segment s of pair b; H holds one bottom
+// row per (sweep, pair, segment).
 __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a) {
   constexpr int W = kBandsPerWG;
   __shared__ double ring[W + 1][kRingC + kCH];   // + pad, see band_sweep
@@ -232,20 +221,26 @@ __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a)
   }
   __syncthreads();
   const unsigned ticket = s_ticket;
-  const int seg = (int)(ticket / (unsigned)a.B);
-  const int b = (int)(ticket % (unsigned)a.B);
+  const int rev = (int)(ticket & 1u);
+  const unsigned rest = ticket >> 1;
+  const int seg = (int)(rest / (unsigned)a.B);
+  const int b = (int)(rest % (unsigned)a.B);
   const int nb_seg = min(W, a.nbands - seg * W);
+  const int64_t per_sweep = (int64_t)a.B * a.nseg;
 
   if (w == W) {
-    const int64_t pb = (int64_t)b * a.nseg;
-    segment_io_wave(seg > 0, seg + 1 < a.nseg, a.ctrl + 2 + pb + (seg > 0 ? seg - 1 : 0),
-                    a.ctrl + 2 + pb + seg, a.H + (pb + (seg > 0 ? seg - 1 : 0)) * a.M,
-                    a.H + (pb + seg) * a.M, ring[0], &wr[0], &rd[0], ring[W], &wr[W],
-                    &rd[W], (unsigned)a.M, lane);
+    const int64_t pb = rev * per_sweep + (int64_t)b * a.nseg;
+    const int64_t sin = pb + (seg > 0 ? seg - 1 : 0), sout = pb + seg;
+    segment_io_wave(seg > 0, seg + 1 < a.nseg, a.ctrl + 2 + sin, a.ctrl + 2 + sout,
+                    a.H + sin * a.M, a.H + sout * a.M, ring[0], &wr[0], &rd[0], ring[W],
+                    &wr[W], &rd[W], (unsigned)a.M, lane);
   } else if (w < nb_seg) {
-    band_sweep<REV>(a, b, seg, w, nb_seg, ring, wr, rd, lane);
+    if (rev)
+      band_sweep<true>(a, b, seg, w, nb_seg, ring, wr, rd, lane);
+    else
+      band_sweep<false>(a, b, seg, w, nb_seg, ring, wr, rd, lane);
   }
-  release_ctrl(a.ctrl, (int64_t)a.B * a.nseg);
+  release_ctrl(a.ctrl, 2 * per_sweep);
 }
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s) {
@@ -265,14 +260,9 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_dp(const DPArgs& a, bool reverse, bool fused, hipStream_t s) {
-  if (fused) return launch_dp_fused(a, reverse, s);
-  const unsigned grid = (unsigned)a.B * (unsigned)a.nseg;
-  const dim3 block((kBandsPerWG + 1) * 64);
-  if (reverse)
-    hipLaunchKernelGGL(k_dp_unfused<true>, dim3(grid), block, 0, s, a);
-  else
-    hipLaunchKernelGGL(k_dp_unfused<false>, dim3(grid), block, 0, s, a);
+hipError_t launch_dp_both(const DPArgs& a, hipStream_t s) {
+  const unsigned grid = 2u * (unsigned)a.B * (unsigned)a.nseg;
+  hipLaunchKernelGGL(k_dp_unfused, dim3(grid), dim3((kBandsPerWG + 1) * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -324,14 +324,15 @@ __global__ __launch_bounds__(W * 64) void k_dp_fused(DPArgs a, int64_t d0) {
         const double upn = wave_shr1(cur, top[u]);
         const double diag = up;
         up = upn;
-        double c = softmin2_cell(diag, upn, cur, d);
+        const double tpart = softmin2_part(diag, upn, cur);
+        double c = tpart + d;
         c = (t - lane < 0) ? kBig : c;
         cur = c;
         bottom[u] = c;
         if (!REV) {
           __builtin_nontemporal_store(c, rsk + cu.base + t * cu.dir);
         } else {
-          const float ev = hw_exp2((float)((xnm + d) - (rn[u] + c)));
+          const float ev = align_entry(xnm, rn[u], tpart);
           *cellp = ev;
           const int64_t col = t - lane;
           if (alignp && col >= 0 && col < M) alignp[M - 1 - col] = ev;

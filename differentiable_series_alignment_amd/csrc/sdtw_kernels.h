@@ -37,13 +37,13 @@ __host__ __device__ inline int64_t sweep_steps(int64_t M) {
 // (N-1,M-1) back to (0,0), i.e. the forward recurrence on both sequences
 // reversed.  All state is kept in base-2 units, X = R * log2(e) / gamma.
 struct DPArgs {
-  float* dsk;           // band-step distances (unfused); the reverse sweep
-                        // overwrites each cell with E
+  float* dsk;           // band-step distances (unfused)
   const float* x;       // [B,N,D] (fused)
   const float* y;       // [B,M,D] (fused)
   double* R;            // band-step forward state X
-  double* H;            // [B,nseg,M] X bottom rows handed between segments
-  unsigned* ctrl;       // [0] ticket; [1 + b*nseg + s] columns published by segment s
+  double* R2;           // band-step reverse soft-minimum parts T' (unfused)
+  double* H;            // bottom rows handed between segments
+  unsigned* ctrl;       // ticket, finished count, per-segment progress
   double* loss64;       // [B] X[N-1,M-1] (forward writes, reverse reads)
   float* loss;          // [B] loss in natural units (forward)
   const float* gl;      // [B] upstream gradients (fused reverse)
@@ -73,11 +73,16 @@ hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t 
 hipError_t launch_unskew(const float* esk, float* out, int64_t B, int64_t N,
                          int64_t M, int64_t S, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
-hipError_t launch_dp(const DPArgs& a, bool reverse, bool fused, hipStream_t s);
+// Unfused: both sweeps of every pair in one launch (X into R, T' into R2).
+hipError_t launch_dp_both(const DPArgs& a, hipStream_t s);
+// Fused: one sweep per launch (the reverse one with the chain rule inside).
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s);
-hipError_t launch_chain(const float* esk, const float* x, const float* y,
-                        const float* gl, float* gx, float* gy, int64_t B,
-                        int64_t N, int64_t M, int64_t D, int64_t S,
-                        hipStream_t s);
+// Chain rule of the unfused backward.  The row pass forms E = 2^(Xnm-X-T')
+// from R and R2 into `esk` (the distance array, no longer needed) and, if
+// gx is given, writes dx; the column pass reads E from `esk` and writes dy.
+hipError_t launch_chain(float* esk, const double* R, const double* R2,
+                        const double* loss64, const float* x, const float* y,
+                        const float* gl, float* gx, float* gy, int64_t B, int64_t N,
+                        int64_t M, int64_t D, int64_t S, hipStream_t s);
 
 }  // namespace sdtw

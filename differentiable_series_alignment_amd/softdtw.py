@@ -71,7 +71,6 @@ class _SoftDTWFunction(torch.autograd.Function):
         ctx.ws = ws
         ctx.gamma = gamma
         ctx.mode = mode
-        ctx.consumed = False
         return loss
 
     @staticmethod
@@ -86,19 +85,13 @@ class _SoftDTWFunction(torch.autograd.Function):
         ws = ctx.ws
         s = _stream(x.device)
         with torch.cuda.device(x.device):
-            if ctx.consumed and ctx.mode == L.SDTW_MODE_UNFUSED:
-                # A second backward (retain_graph): the unfused backward
-                # replaced the distances in the workspace, so rebuild them.
-                scratch = torch.empty(B, dtype=torch.float32, device=x.device)
-                L.check(L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, ctx.gamma,
-                                       ctx.mode, ws.data_ptr(), ws.numel(),
-                                       scratch.data_ptr(), s), "sdtw_forward")
+            # The backward leaves the workspace valid for another backward
+            # (retain_graph) in both modes.
             L.check(L.sdtw_backward(x.data_ptr(), y.data_ptr(), B, N, M, D, ctx.gamma,
                                     ctx.mode, ws.data_ptr(), ws.numel(), gl.data_ptr(),
                                     gx.data_ptr() if gx is not None else None,
                                     gy.data_ptr() if gy is not None else None,
                                     None, s), "sdtw_backward")
-        ctx.consumed = True
         return gx, gy, None, None
 
 

@@ -298,6 +298,38 @@ def test_retain_graph_twice(S):
     torch.testing.assert_close(xd.grad, g1, rtol=0, atol=0)
 
 
+def test_abi_backward_repeatable(S):
+    """Through the C ABI: two backward calls on one unfused forward give
+    bitwise the same dx, dy and E (the backward forms E from the sweep
+    states and never reads the distances it overwrites); a backward with
+    every output NULL is a successful no-op."""
+    from differentiable_series_alignment_amd import _lib as L
+    B, N, M, D = 3, 130, 97, 5
+    x, y = pair_batch(B, N, M, D, seed=11)
+    x, y = x.to(DEV), y.to(DEV)
+    nb = L.sdtw_workspace_bytes(B, N, M, D, L.SDTW_MODE_UNFUSED)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    loss = torch.empty(B, device=DEV)
+    gl = torch.full((B,), 0.5, device=DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    L.check(L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, 1.0, L.SDTW_MODE_UNFUSED,
+                           ws.data_ptr(), nb, loss.data_ptr(), s), "sdtw_forward")
+    outs = []
+    for _ in range(2):
+        gx, gy = torch.empty_like(x), torch.empty_like(y)
+        E = torch.empty(B, N, M, device=DEV)
+        L.check(L.sdtw_backward(x.data_ptr(), y.data_ptr(), B, N, M, D, 1.0,
+                                L.SDTW_MODE_UNFUSED, ws.data_ptr(), nb, gl.data_ptr(),
+                                gx.data_ptr(), gy.data_ptr(), E.data_ptr(), s), "sdtw_backward")
+        outs.append((gx, gy, E))
+    assert L.sdtw_backward(x.data_ptr(), y.data_ptr(), B, N, M, D, 1.0, L.SDTW_MODE_UNFUSED,
+                           ws.data_ptr(), nb, gl.data_ptr(), None, None, None, s) == L.SDTW_OK
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        torch.testing.assert_close(a, b, rtol=0, atol=0)
+    assert torch.isfinite(outs[0][2]).all()
+
+
 def test_small_gamma_finite(S):
     x, y = pair_batch(4, 700, 650, 32, seed=8)
     l, gx, gy = gpu_value_and_grad(S, x, y, 0.01)
