@@ -5,15 +5,17 @@
 Workload (the headline configuration): B=32 pairs, N=M=512, D=64, gamma=1.0,
 x, y ~ N(0,1) fp32 from seed 0, unfused mode, loss = batch mean.  One step is
 one pass of the whole path through the C ABI on preallocated buffers:
-sdtw_forward (distances, forward sweep, loss) + sdtw_backward (reverse sweep,
-alignment matrix, chain rule to dx and dy).  Inputs are resident in HBM when
-the timed region starts.  Prints one JSON line.
+sdtw_forward (distances; forward and reverse sweeps of the dynamic programme
+in one launch; loss) + sdtw_backward (alignment matrix from the two sweeps,
+chain rule to dx and dy).  Inputs are resident in HBM when the timed region
+starts.  Prints one JSON line.
 
 Metric: DP cells per second, B*N*M / (seconds per step), plus peak memory of
-the autograd path.  `roofline` describes the dominant kernel (the reverse
-sweep) timed alone with HIP events on the stream it runs on; `cpu_baseline`
-is the fp64 oracle on the host, timed on a bounded sample of the same
-workload.
+the autograd path.  `roofline` describes the dominant kernel (the launch that
+runs both sweeps), its duration taken from HIP events that the library
+records on the launch stream (sdtw_timing); `kernels` lists every launch of
+a step the same way.  `cpu_baseline` is the fp64 oracle on the host, timed
+on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -28,15 +30,48 @@ if HERE not in sys.path:
     sys.path.insert(0, HERE)
 
 WORKLOAD = dict(B=32, N=512, M=512, D=64, gamma=1.0)
-PEAK_FP64_VECTOR_TFLOPS = 78.6   # MI355X datasheet
-# Algorithmic work of one cell of the reverse sweep (dominant kernel): the
-# soft-min (2 min, 3 sub, 3 exp2, 2 add, 1 log2, 2 add) plus the alignment
-# value (3 add/sub, 1 exp2): 17 floating-point operations, every one of them
-# necessary to produce R' and E for that cell.
-REV_FLOPS_PER_CELL = 17
-# Bytes the reverse sweep must move per cell: read Dist (4) and the forward
-# state (8), write E (4).
-REV_BYTES_PER_CELL = 16
+# Plain ALU peak of the MI355X: 256 CUs x 4 SIMDs x 16 lanes, one operation
+# per lane per clock at 2.4 GHz (the datasheet's 78.6 TFLOP/s fp64 counts an
+# FMA as two), i.e. 39.3 T operations/s.
+PEAK_ALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Algorithmic work of one cell in one sweep: d = Dist*log2(e)/g (1 mul), the
+# two minima and two maxima that order the three predecessors (4), the two
+# differences to the minimum (2), two exp2 (2), their sum with 1 (2), log2
+# (1), the soft-minimum m - log2 (1) and the state t + d (1): 14 operations.
+# The dominant launch runs both sweeps over every cell.
+DP_OPS_PER_CELL = 2 * 14
+# Bytes the two sweeps must move per cell: each reads Dist (4) and writes
+# its fp64 state (8).
+DP_BYTES_PER_CELL = 2 * (4 + 8)
+DOMINANT = "dp_both"
+# HBM traffic of one launch of the dominant kernel, from two rocprofv3 --pmc
+# runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) on the headline workload,
+# each scaled by what the same counter reads for a 256 MiB copy (FETCH_SIZE
+# reads half the bytes moved, WRITE_SIZE all of them).  Valid only for the
+# kernel sources it was taken on, identified by their SHA-256.
+TRAFFIC_RECORD = {
+    "sources": ["differentiable_series_alignment_amd/csrc/sdtw_dp.hip",
+                "differentiable_series_alignment_amd/csrc/sdtw_dp_common.h",
+                "differentiable_series_alignment_amd/csrc/sdtw_device.h",
+                "differentiable_series_alignment_amd/csrc/sdtw_kernels.h"],
+    "sha256": "fac6c14e11c9dbc79fe6043c4edca8e44f479798173aca1a2e122cfb2e6b213f",
+    "fetch_kib": 37418, "fetch_scale": 2.0,
+    "write_kib": 147856, "write_scale": 1.0,
+}
+
+
+def recorded_traffic():
+    """Bytes per launch of the dominant kernel, or None once its sources
+    differ from those the counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_RECORD["sources"]:
+        with open(os.path.join(HERE, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != TRAFFIC_RECORD["sha256"]:
+        return None
+    r = TRAFFIC_RECORD
+    return 1024 * (r["fetch_kib"] * r["fetch_scale"] + r["write_kib"] * r["write_scale"])
 
 
 def parse():
@@ -48,7 +83,21 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--headline-only", action="store_true",
                    help="skip the per-configuration table")
+    p.add_argument("--counter-pass", action="store_true",
+                   help="for rocprofv3 --pmc runs: three headline steps and three "
+                        "copies of 256 MiB (the counters' calibration), no output")
     return p.parse_args()
+
+
+def counter_pass(torch, L, x, y, gamma):
+    """Three unfused headline steps, then three copies of a 256 MiB fp32
+    tensor whose bytes are known, for scaling the traffic counters."""
+    measure(L, torch, x, y, gamma, L.SDTW_MODE_UNFUSED, 3, 0)
+    src = torch.ones(64 * 2**20, dtype=torch.float32, device=x.device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(x, y, gamma, budget_s):
@@ -174,26 +223,30 @@ def main():
     xc, yc = pair_batch(B, N, M, D, seed=0)
     x, y = xc.to(dev), yc.to(dev)
     cells = B * N * M
+    if args.counter_pass:
+        counter_pass(torch, L, x, y, gamma)
+        return
 
     ms, fwd, bwd, stream = measure(L, torch, x, y, gamma, L.SDTW_MODE_UNFUSED,
                                    args.steps, args.warmup)
     value = cells / (ms * 1e-3)
 
-    # Dominant kernel alone: sdtw_backward without gradient outputs launches
-    # exactly one kernel, the reverse sweep.  Events bracket it on its stream.
-    pairs = []
+    # Per-launch durations: HIP events that the library records around each
+    # of its launches, on the stream it launches on.
+    L.sdtw_timing(True)
+    per_kernel = {}
     for it in range(args.warmup + args.steps):
         fwd()
-        a0 = torch.cuda.Event(enable_timing=True)
-        a1 = torch.cuda.Event(enable_timing=True)
-        a0.record(stream)
-        bwd(grads=False)
-        a1.record(stream)
+        bwd()
+        recs = L.sdtw_timing_collect()
         if it >= args.warmup:
-            pairs.append((a0, a1))
-    torch.cuda.synchronize()
-    rev = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
-    achieved = REV_FLOPS_PER_CELL * cells / (rev * 1e-3) / 1e12
+            for name, t in recs:
+                per_kernel.setdefault(name, []).append(t)
+    L.sdtw_timing(False)
+    kernels = {k: {"launches_per_step": len(v) / args.steps, "avg_us": 1e3 * sum(v) / len(v)}
+               for k, v in per_kernel.items()}
+    dom_ms = sum(per_kernel[DOMINANT]) / len(per_kernel[DOMINANT])
+    achieved = DP_OPS_PER_CELL * cells / (dom_ms * 1e-3) / 1e12
 
     peak, peak_over = peak_mib(torch, SoftDTW, x, y, gamma, False)
     ms_f, _, _, _ = measure(L, torch, x, y, gamma, L.SDTW_MODE_FUSED,
@@ -240,11 +293,13 @@ def main():
         "peak_mib_over_io": peak_over,
         "fused": {"ms_per_step": ms_f, "cells_per_s": cells / (ms_f * 1e-3),
                   "peak_mib": peak_f, "peak_mib_over_io": peak_over_f},
-        "roofline": {"kernel": "reverse sweep (k_dp_unfused<true>)", "bound": "alu",
-                     "achieved": achieved, "peak": PEAK_FP64_VECTOR_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP64_VECTOR_TFLOPS,
-                     "traffic": None, "launch_us": rev * 1e3,
-                     "algorithmic_gbs": REV_BYTES_PER_CELL * cells / (rev * 1e-3) / 1e9},
+        "roofline": {"kernel": "both sweeps of the dynamic programme (k_dp_unfused)",
+                     "bound": "alu", "achieved": achieved, "peak": PEAK_ALU_TOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_ALU_TOPS,
+                     "traffic": recorded_traffic(), "traffic_unit": "bytes per launch",
+                     "launch_us": dom_ms * 1e3,
+                     "algorithmic_gbs": DP_BYTES_PER_CELL * cells / (dom_ms * 1e-3) / 1e9},
+        "kernels": kernels,
         "per_config": per_config,
     }
     if not args.no_cpu_baseline:

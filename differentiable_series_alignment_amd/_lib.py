@@ -37,6 +37,9 @@ SIGNATURES = {
                           ctypes.c_size_t, _P, _P]),
     "sdtw_backward": (_I, [_P, _P, _I64, _I64, _I64, _I64, _F, _I, _P,
                            ctypes.c_size_t, _P, _P, _P, _P, _P]),
+    "sdtw_timing": (_I, [_I]),
+    "sdtw_timing_collect": (_I, [ctypes.POINTER(ctypes.c_char_p),
+                                 ctypes.POINTER(ctypes.c_float), _I]),
 }
 
 _lib = None
@@ -95,6 +98,21 @@ def sdtw_backward(x: int, y: int, B: int, N: int, M: int, D: int, gamma: float,
     return lib().sdtw_backward(x, y, B, N, M, D, gamma, mode, workspace,
                                workspace_bytes, grad_loss, grad_x, grad_y, align,
                                stream)
+
+
+def sdtw_timing(on: bool) -> int:
+    return lib().sdtw_timing(1 if on else 0)
+
+
+def sdtw_timing_collect(cap: int = 4096) -> list[tuple[str, float]]:
+    """(kernel name, milliseconds) of the launches recorded since the last
+    collect on this thread, in launch order."""
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = lib().sdtw_timing_collect(names, ms, cap)
+    if n < 0:
+        raise SdtwError(-n, "sdtw_timing_collect")
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]
 
 
 def check(status: int, where: str) -> None:

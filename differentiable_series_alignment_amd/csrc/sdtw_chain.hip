@@ -322,6 +322,7 @@ static void launch_rows(dim3 grid, hipStream_t s, float* esk, const double* R,
                         const double* R2, const double* loss64, const float* x,
                         const float* y, const float* gl, float* gx, int64_t N, int64_t M,
                         int64_t D, int64_t S, int nb, int64_t d0) {
+  TimedLaunch timed_("chain_rows", s);
   if (gx)
     hipLaunchKernelGGL((k_chain_rows<NTW, true, FORM>), grid, dim3(256), 0, s, esk, R, R2,
                        loss64, x, y, gl, gx, N, M, D, S, nb, d0);
@@ -359,6 +360,7 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
   for (int64_t d0 = 0; d0 < D; d0 += 128) {
     const int64_t dw = D - d0 < 128 ? D - d0 : 128;
     const dim3 grid((unsigned)((M + 63) / 64), (unsigned)B);
+    TimedLaunch timed_("chain_cols", s);
     if (dw > 64)
       hipLaunchKernelGGL(k_chain_cols<2>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0);
     else

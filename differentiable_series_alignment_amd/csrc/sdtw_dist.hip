@@ -165,8 +165,11 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
 hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
                        int64_t N, int64_t M, int64_t D, hipStream_t stream) {
   dim3 grid((unsigned)((M + kDT - 1) / kDT), (unsigned)((N + kDT - 1) / kDT), (unsigned)B);
-  hipLaunchKernelGGL(k_dist<false>, grid, dim3(256), 0, stream, x, y, dist, N, M, D,
-                     (int64_t)0, 0);
+  {
+    TimedLaunch timed_("dist", stream);
+    hipLaunchKernelGGL(k_dist<false>, grid, dim3(256), 0, stream, x, y, dist, N, M, D,
+                       (int64_t)0, 0);
+  }
   return hipGetLastError();
 }
 
@@ -174,8 +177,11 @@ hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t 
                             int64_t N, int64_t M, int64_t D, int64_t S,
                             hipStream_t stream) {
   dim3 grid((unsigned)((M + kDT - 1) / kDT), (unsigned)((N + kDT - 1) / kDT), (unsigned)B);
-  hipLaunchKernelGGL(k_dist<true>, grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S,
-                     (int)((N + 63) / 64));
+  {
+    TimedLaunch timed_("dist_skew", stream);
+    hipLaunchKernelGGL(k_dist<true>, grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S,
+                       (int)((N + 63) / 64));
+  }
   return hipGetLastError();
 }
 
@@ -193,8 +199,11 @@ __global__ __launch_bounds__(256) void k_unskew(const float* __restrict__ esk,
 hipError_t launch_unskew(const float* esk, float* out, int64_t B, int64_t N,
                          int64_t M, int64_t S, hipStream_t s) {
   dim3 grid((unsigned)((M + 255) / 256), (unsigned)(N < 4096 ? N : 4096), (unsigned)B);
-  hipLaunchKernelGGL(k_unskew, grid, dim3(256), 0, s, esk, out, N, M, S,
-                     (int)((N + 63) / 64));
+  {
+    TimedLaunch timed_("unskew", s);
+    hipLaunchKernelGGL(k_unskew, grid, dim3(256), 0, s, esk, out, N, M, S,
+                       (int)((N + 63) / 64));
+  }
   return hipGetLastError();
 }
 

@@ -245,6 +245,7 @@ __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a)
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  TimedLaunch timed_("zero_u32", s);
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
@@ -256,12 +257,14 @@ __global__ void k_zero_f32(float* p, int64_t n) {
 
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  TimedLaunch timed_("zero_f32", s);
   hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 
 hipError_t launch_dp_both(const DPArgs& a, hipStream_t s) {
   const unsigned grid = 2u * (unsigned)a.B * (unsigned)a.nseg;
+  TimedLaunch timed_("dp_both", s);
   hipLaunchKernelGGL(k_dp_unfused, dim3(grid), dim3((kBandsPerWG + 1) * 64), 0, s, a);
   return hipGetLastError();
 }

@@ -422,6 +422,7 @@ static hipError_t launch_fused_one(const DPArgs& a, int64_t d0, hipStream_t s) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)a.B * (unsigned)a.nseg;
+  TimedLaunch timed_(REV ? "dp_fused_rev" : "dp_fused_fwd", s);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(W * 64), lds, s, a, d0);
   return hipGetLastError();
 }

@@ -64,6 +64,21 @@ constexpr int64_t kFusedMaxD = 256;
 // Bands per workgroup of the fused kernels for this D (0: unsupported D).
 int fused_bands_per_wg(int64_t D);
 
+// Scope around one kernel launch: when launch timing is on, HIP events on
+// `s` bracket the launch (see sdtw_timing).
+class TimedLaunch {
+ public:
+  TimedLaunch(const char* name, hipStream_t s);
+  ~TimedLaunch();
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+
+ private:
+  hipStream_t stream_;
+  long index_;
+  hipEvent_t end_ = nullptr;
+};
+
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
                        int64_t N, int64_t M, int64_t D, hipStream_t stream);

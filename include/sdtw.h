@@ -113,6 +113,23 @@ int sdtw_backward(const float *x, const float *y, int64_t B, int64_t N,
                   size_t workspace_bytes, const float *grad_loss,
                   float *grad_x, float *grad_y, float *align, void *stream);
 
+/* Launch timing, off by default.  sdtw_timing(1) makes every kernel that
+ * later sdtw_* calls (from any host thread of the process) enqueue be
+ * bracketed by a pair of HIP events recorded on that call's stream;
+ * sdtw_timing(0) stops recording.  Returns SDTW_OK.  Recording costs two
+ * event creations per launch, so it is meant for measurement runs, not for
+ * production loops. */
+int sdtw_timing(int on);
+
+/* Waits for the launches recorded since the previous collect (launches still
+ * being enqueued by another thread are left for the next collect), writes
+ * the names (static strings) and durations in milliseconds of the first
+ * `cap` of them, in launch order, into names[] and ms[] (both
+ * may be NULL when cap is 0), releases the events and returns how many
+ * launches were recorded; -SDTW_ERR_HIP if an event could not be read (its
+ * duration is then reported as -1). */
+int sdtw_timing_collect(const char **names, float *ms, int cap);
+
 #ifdef __cplusplus
 }
 #endif

@@ -124,3 +124,12 @@ def test_python_layer_validation_on_cpu():
         SoftDTW(normalize=True)(x, y)
     with pytest.raises(ValueError):
         soft_dtw(x[0], y[0])                            # not 3-D
+
+
+def test_timing_switch_without_launches():
+    """Launch timing can be switched and collected with nothing recorded (no
+    HIP call is made then)."""
+    assert L.sdtw_timing(True) == L.SDTW_OK
+    assert L.sdtw_timing_collect() == []
+    assert L.sdtw_timing(False) == L.SDTW_OK
+    assert L.lib().sdtw_timing_collect(None, None, 0) == 0

@@ -330,6 +330,24 @@ def test_abi_backward_repeatable(S):
     assert torch.isfinite(outs[0][2]).all()
 
 
+def test_launch_timing_records_each_kernel(S):
+    """sdtw_timing brackets every launch of a forward+backward with events on
+    the call's stream and reports them by name, in launch order."""
+    from differentiable_series_alignment_amd import _lib as L
+    x, y = pair_batch(2, 100, 90, 8, seed=12)
+    xd = x.to(DEV).requires_grad_(True)
+    yd = y.to(DEV).requires_grad_(True)
+    L.sdtw_timing(True)
+    try:
+        S.soft_dtw(xd, yd, 1.0).sum().backward()
+        recs = L.sdtw_timing_collect()
+    finally:
+        L.sdtw_timing(False)
+    names = [n for n, _ in recs]
+    assert names == ["zero_u32", "dist_skew", "dp_both", "chain_rows", "chain_cols"], names
+    assert all(t > 0 for _, t in recs)
+
+
 def test_small_gamma_finite(S):
     x, y = pair_batch(4, 700, 650, 32, seed=8)
     l, gx, gy = gpu_value_and_grad(S, x, y, 0.01)
