@@ -23,6 +23,8 @@ struct Layout {
   size_t H = 0;                     // fp64 [2, B, nseg, M] segment hand-off rows
   size_t R = 0;                     // fp64 band-step forward state
   size_t R2 = 0;                    // fp64 band-step reverse soft-min parts (unfused)
+  size_t part = 0;                  // fp32 split partial sums of the chain rule (unfused)
+  size_t cnt_rows = 0, cnt_cols = 0;  // word offsets of the chain split counters
   size_t dist = 0;                  // fp32 band-step distances, then E (unfused)
   size_t total = 0;
 };
@@ -56,7 +58,11 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   const size_t cells = (size_t)B * (size_t)L->nbands * (size_t)L->S * 64;
   size_t off = 0;
   L->ctrl = off;
-  L->ctrl_words = 2 * (2 + (size_t)B * (size_t)L->nseg);
+  // DP words (two halves of ticket, done, progress), then the counters of
+  // the chain rule's split sums (one per band, one per 64-column block).
+  L->cnt_rows = 2 * (2 + (size_t)B * (size_t)L->nseg);
+  L->cnt_cols = L->cnt_rows + (size_t)B * (size_t)L->nbands;
+  L->ctrl_words = L->cnt_cols + (size_t)B * (size_t)((M + 63) / 64);
   off += align_up(L->ctrl_words * 4);
   L->loss64 = off;
   off += align_up((size_t)B * 8);
@@ -67,6 +73,8 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   if (mode == SDTW_MODE_UNFUSED) {
     L->R2 = off;
     off += align_up(cells * 8);
+    L->part = off;
+    off += align_up(sdtw::chain_part_floats(B, N, M) * 4);
     L->dist = off;
     off += align_up(cells * 4);
   }
@@ -87,7 +95,7 @@ DPArgs dp_args(const Layout& L, char* ws, const float* x, const float* y,
   memset(&a, 0, sizeof(a));
   a.x = x;
   a.y = y;
-  a.ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl) + (reverse ? L.ctrl_words / 2 : 0);
+  a.ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl) + (reverse ? 2 + B * L.nseg : 0);
   a.loss64 = reinterpret_cast<double*>(ws + L.loss64);
   a.H = reinterpret_cast<double*>(ws + L.H);
   a.R = reinterpret_cast<double*>(ws + L.R);
@@ -199,8 +207,11 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
   // their states (the distances are not read again), so repeated backward
   // calls on one forward are all valid.
   if (!grad_x && !grad_y && !align) return SDTW_OK;
+  unsigned* ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl);
   hipError_t e = sdtw::launch_chain(a.dsk, a.R, a.R2, a.loss64, x, y, grad_loss, grad_x,
-                                    grad_y, B, N, M, D, L.S, s);
+                                    grad_y, B, N, M, D, L.S,
+                                    reinterpret_cast<float*>(ws + L.part),
+                                    ctrl + L.cnt_rows, ctrl + L.cnt_cols, s);
   if (e == hipSuccess && align) e = sdtw::launch_unskew(a.dsk, align, B, N, M, L.S, s);
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
 }

@@ -92,12 +92,68 @@ struct StageXT {
   }
 };
 
+// Split sums.  When the columns (dx) or the bands (dy) of one workgroup's sum
+// are spread over `nsplit` workgroups, each writes its partial (the NTW
+// accumulator tiles and the row or column sum, per thread) to `part`
+// ([nsplit][16*NTW+1][256] floats for its group), and the last workgroup to
+// arrive adds the partials in split order, so the result does not depend on
+// the order of arrival.  Returns true in that last workgroup, which then
+// holds the full sums and clears the group's counter for the next launch.
+template <int NTW>
+__device__ __forceinline__ bool split_reduce(v16f (&acc)[NTW], float& sum, float* part,
+                                             unsigned* cnt, int p, int nsplit) {
+  constexpr int K = 16 * NTW + 1;
+  __shared__ unsigned s_last;
+  const int tid = (int)threadIdx.x;
+  // Partials go out as device-coherent stores (they bypass the per-XCD
+  // caches); each thread waits for its own, the barrier makes that all of
+  // them, and only then is the arrival counted.  The last workgroup reads
+  // them back with device-coherent loads.  No cache write-back or
+  // invalidation is needed for either side.
+  float* mine = part + (int64_t)p * K * 256;
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      __hip_atomic_store(mine + (t * 16 + e) * 256 + tid, acc[t][e], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(mine + 16 * NTW * 256 + tid, sum, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(nsplit - 1);
+  __syncthreads();
+  if (!s_last) return false;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+  sum = 0.f;
+  for (int q = 0; q < nsplit; ++q) {
+    const float* src = part + (int64_t)q * K * 256;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][e] += __hip_atomic_load(
+          src + (t * 16 + e) * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sum += __hip_atomic_load(src + 16 * NTW * 256 + tid, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 // dx for one band (64 rows) of one pair, columns of D in [d0, d0 + 128).
 // Wave w: row tile w & 1, d tiles (w >> 1) + 2t.  Column blocks of 32 need
 // band steps [j0, j0 + 96); the next block's 32 new steps are fetched into
 // registers while the current block computes.  FORM: the window comes from
 // the sweeps' states and E is formed (and stored) on the way; otherwise it
-// is read from the stored E.  GX = false forms E only.
+// is read from the stored E.  GX = false forms E only.  The band's column
+// blocks are split over gridDim.z workgroups (split sums, above).
 template <int NTW, bool GX, bool FORM>
 __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
                                                     const double* __restrict__ R,
@@ -108,9 +164,12 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
                                                     const float* __restrict__ gl,
                                                     float* __restrict__ gx, int64_t N,
                                                     int64_t M, int64_t D, int64_t S,
-                                                    int nbands, int64_t d0) {
+                                                    int nbands, int64_t d0,
+                                                    float* __restrict__ part,
+                                                    unsigned* __restrict__ cnt) {
   __shared__ float ring[kRingSteps * kRingPitch];
   const int64_t b = blockIdx.y, band = blockIdx.x;
+  const int p = blockIdx.z, nsplit = gridDim.z;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int r = l & 31, h = l >> 5;
   const int rt = w & 1, dsel = w >> 1;
@@ -138,9 +197,10 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
   float rsum = 0.f;
 
   const int64_t nblk = (M + 31) / 32;
+  const int64_t kb0 = p * nblk / nsplit, kb1 = (p + 1) * nblk / nsplit;
   Stage32 st;
   StageXT sx;
-  for (int64_t s0 = 0; s0 < 96; s0 += 32) {
+  for (int64_t s0 = kb0 * 32; s0 < kb0 * 32 + 96; s0 += 32) {
     if (FORM) {
       sx.load(xbp, tbp, s0, smax);
       sx.store(ring, bandp, s0, xnm);
@@ -159,13 +219,13 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
       for (int t = 0; t < NTW; ++t) Y[s][t] = yb[j * D + dcol[t]];
     }
   };
-  if (GX) load_y(0, yv);
+  if (GX) load_y(kb0 * 32, yv);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int64_t kb = 0; kb < nblk; ++kb) {
+  for (int64_t kb = kb0; kb < kb1; ++kb) {
     const int64_t j0 = kb * 32;
-    const bool more = kb + 1 < nblk;
+    const bool more = kb + 1 < kb1;
     if (more) {
       if (FORM)
         sx.load(xbp, tbp, j0 + 96, smax);
@@ -201,6 +261,10 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
     __syncthreads();
   }
   if (!GX) return;
+  if (nsplit > 1 &&
+      !split_reduce<NTW>(acc, rsum, part + (b * nbands + band) * (int64_t)nsplit * (16 * NTW + 1) * 256,
+                         cnt + b * nbands + band, p, nsplit))
+    return;
 
   rsum += __shfl_xor(rsum, 32, 64);
   float rs[16];
@@ -224,6 +288,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
 // dy for 64 columns of one pair, columns of D in [d0, d0 + 128), summing over
 // every band.  Wave w: column tile w & 1, d tiles (w >> 1) + 2t.  The band's
 // window of steps [j0, j0 + 128) is fetched into registers one band ahead.
+// The bands are split over gridDim.z workgroups (split sums, above).
 template <int NTW>
 __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ esk,
                                                     const float* __restrict__ x,
@@ -231,9 +296,13 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
                                                     const float* __restrict__ gl,
                                                     float* __restrict__ gy, int64_t N,
                                                     int64_t M, int64_t D, int64_t S,
-                                                    int nbands, int64_t d0) {
+                                                    int nbands, int64_t d0,
+                                                    float* __restrict__ part,
+                                                    unsigned* __restrict__ cnt) {
   __shared__ float ring[kRingSteps * kRingPitch];
   const int64_t b = blockIdx.y, j0 = (int64_t)blockIdx.x * 64;
+  const int p = blockIdx.z, nsplit = gridDim.z;
+  const int64_t bb0 = (int64_t)p * nbands / nsplit, bb1 = (int64_t)(p + 1) * nbands / nsplit;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int r = l & 31, h = l >> 5;
   const int ct = w & 1, dsel = w >> 1;
@@ -268,14 +337,14 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
       for (int t = 0; t < NTW; ++t) X[s][t] = xb[rr * D + dcol[t]];
     }
   };
-  load_band(0, win, xv);
+  load_band(bb0, win, xv);
   __builtin_amdgcn_s_waitcnt(0);
 
-  for (int64_t band = 0; band < nbands; ++band) {
+  for (int64_t band = bb0; band < bb1; ++band) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) win[k].store(ring, 32 * k);
     __syncthreads();
-    const bool more = band + 1 < nbands;
+    const bool more = band + 1 < bb1;
     if (more) load_band(band + 1, nxt, xn);
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
@@ -298,6 +367,11 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
     }
   }
 
+  if (nsplit > 1 &&
+      !split_reduce<NTW>(acc, csum, part + (b * gridDim.x + blockIdx.x) * (int64_t)nsplit * (16 * NTW + 1) * 256,
+                         cnt + b * gridDim.x + blockIdx.x, p, nsplit))
+    return;
+
   csum += __shfl_xor(csum, 32, 64);
   float cs[16];
 #pragma unroll
@@ -317,41 +391,67 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
   }
 }
 
+// Workgroups per band (dx) or per 64-column block (dy): enough splits of the
+// reduction range to give the launch about 1024 workgroups, keeping at least
+// two column blocks (or bands) per workgroup.
+int chain_splits_rows(int64_t B, int64_t N, int64_t M) {
+  const int64_t groups = B * ((N + 63) / 64), nblk = (M + 31) / 32;
+  int64_t p = (1024 + groups - 1) / groups;
+  p = p < nblk / 2 ? p : nblk / 2;
+  return (int)(p < 1 ? 1 : (p > 16 ? 16 : p));
+}
+int chain_splits_cols(int64_t B, int64_t N, int64_t M) {
+  const int64_t groups = B * ((M + 63) / 64), nb = (N + 63) / 64;
+  int64_t p = (1024 + groups - 1) / groups;
+  p = p < nb / 2 ? p : nb / 2;
+  return (int)(p < 1 ? 1 : (p > 16 ? 16 : p));
+}
+size_t chain_part_floats(int64_t B, int64_t N, int64_t M) {
+  const int64_t pr = chain_splits_rows(B, N, M), pc = chain_splits_cols(B, N, M);
+  const int64_t rows = pr > 1 ? B * ((N + 63) / 64) * pr : 0;
+  const int64_t cols = pc > 1 ? B * ((M + 63) / 64) * pc : 0;
+  return (size_t)(rows > cols ? rows : cols) * 33 * 256;
+}
+
 template <int NTW, bool FORM>
 static void launch_rows(dim3 grid, hipStream_t s, float* esk, const double* R,
                         const double* R2, const double* loss64, const float* x,
                         const float* y, const float* gl, float* gx, int64_t N, int64_t M,
-                        int64_t D, int64_t S, int nb, int64_t d0) {
+                        int64_t D, int64_t S, int nb, int64_t d0, float* part,
+                        unsigned* cnt) {
   TimedLaunch timed_("chain_rows", s);
   if (gx)
     hipLaunchKernelGGL((k_chain_rows<NTW, true, FORM>), grid, dim3(256), 0, s, esk, R, R2,
-                       loss64, x, y, gl, gx, N, M, D, S, nb, d0);
+                       loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt);
   else
     hipLaunchKernelGGL((k_chain_rows<1, false, FORM>), grid, dim3(256), 0, s, esk, R, R2,
-                       loss64, x, y, gl, gx, N, M, D, S, nb, d0);
+                       loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt);
 }
 
 hipError_t launch_chain(float* esk, const double* R, const double* R2,
                         const double* loss64, const float* x, const float* y,
                         const float* gl, float* gx, float* gy, int64_t B, int64_t N,
-                        int64_t M, int64_t D, int64_t S, hipStream_t s) {
+                        int64_t M, int64_t D, int64_t S, float* part, unsigned* cnt_rows,
+                        unsigned* cnt_cols, hipStream_t s) {
   const int nb = (int)((N + 63) / 64);
+  const unsigned pr = (unsigned)chain_splits_rows(B, N, M);
+  const unsigned pc = (unsigned)chain_splits_cols(B, N, M);
   // Row pass(es): the first forms E; later D slices read it back.
   for (int64_t d0 = 0; d0 < D; d0 += 128) {
     if (d0 > 0 && !gx) break;
     const int64_t dw = D - d0 < 128 ? D - d0 : 128;
     const bool two = dw > 64;  // more than two 32-wide d tiles
-    const dim3 grid((unsigned)nb, (unsigned)B);
+    const dim3 grid((unsigned)nb, (unsigned)B, pr);
     if (d0 == 0) {
       if (two)
-        launch_rows<2, true>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0);
+        launch_rows<2, true>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
       else
-        launch_rows<1, true>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0);
+        launch_rows<1, true>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
     } else {
       if (two)
-        launch_rows<2, false>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0);
+        launch_rows<2, false>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
       else
-        launch_rows<1, false>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0);
+        launch_rows<1, false>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -359,12 +459,12 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
   if (!gy) return hipSuccess;
   for (int64_t d0 = 0; d0 < D; d0 += 128) {
     const int64_t dw = D - d0 < 128 ? D - d0 : 128;
-    const dim3 grid((unsigned)((M + 63) / 64), (unsigned)B);
+    const dim3 grid((unsigned)((M + 63) / 64), (unsigned)B, pc);
     TimedLaunch timed_("chain_cols", s);
     if (dw > 64)
-      hipLaunchKernelGGL(k_chain_cols<2>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0);
+      hipLaunchKernelGGL(k_chain_cols<2>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0, part, cnt_cols);
     else
-      hipLaunchKernelGGL(k_chain_cols<1>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0);
+      hipLaunchKernelGGL(k_chain_cols<1>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0, part, cnt_cols);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
