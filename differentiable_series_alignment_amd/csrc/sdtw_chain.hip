@@ -391,20 +391,23 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
   }
 }
 
-// Workgroups per band (dx) or per 64-column block (dy): enough splits of the
-// reduction range to give the launch about 1024 workgroups, keeping at least
-// two column blocks (or bands) per workgroup.
+// Workgroups per band (dx) or per 64-column block (dy): a launch with fewer
+// groups than the GPU has CUs splits each group's reduction range so that it
+// fills them, keeping at least two column blocks (or bands) per workgroup.
+// Larger launches do not split (at C2 a split gains nothing and its partial
+// sums would cost memory).
+constexpr int64_t kChainFill = 256;
 int chain_splits_rows(int64_t B, int64_t N, int64_t M) {
   const int64_t groups = B * ((N + 63) / 64), nblk = (M + 31) / 32;
-  int64_t p = (1024 + groups - 1) / groups;
+  int64_t p = (kChainFill + groups - 1) / groups;
   p = p < nblk / 2 ? p : nblk / 2;
-  return (int)(p < 1 ? 1 : (p > 16 ? 16 : p));
+  return (int)(p < 1 ? 1 : (p > 8 ? 8 : p));
 }
 int chain_splits_cols(int64_t B, int64_t N, int64_t M) {
   const int64_t groups = B * ((M + 63) / 64), nb = (N + 63) / 64;
-  int64_t p = (1024 + groups - 1) / groups;
+  int64_t p = (kChainFill + groups - 1) / groups;
   p = p < nb / 2 ? p : nb / 2;
-  return (int)(p < 1 ? 1 : (p > 16 ? 16 : p));
+  return (int)(p < 1 ? 1 : (p > 8 ? 8 : p));
 }
 size_t chain_part_floats(int64_t B, int64_t N, int64_t M) {
   const int64_t pr = chain_splits_rows(B, N, M), pc = chain_splits_cols(B, N, M);
