@@ -3,105 +3,191 @@
 // The README "SoftDTW-CUDA (PyTorch + Numba)" ("Fused Mode": no distance
 // tensor; "Limitations": squared Euclidean only) and the review page
 // "SoftDTW-CUDA-Torch" ("Proposed method": distances recomputed on the fly)
-// describe a mode that never materialises Dist.  Here each band (64 rows)
-// keeps its x rows in LDS and, at every chunk of 16 steps, recomputes the
-// 64 x 16 block of distances the wavefront is about to enter with fp64 MFMA
-// (the same operations, in the same order, as the distance kernel, so fused
-// and unfused distances are bit-identical) into an 80-column LDS ring that
-// the steps read.
-//
-// The reverse sweep replaces every ring entry by its alignment value E once
-// the cell is done; when a 16-column block of the band is complete (four
-// chunks later) it contributes, on fp32 MFMA,
-//   dx[rows of the band] += 2g (rowsum(E) x - E . Y)    (kept in registers),
-//   dy[16 columns]       += 2g (colsum(E) y - E^T . X)  (atomic adds, the
-//                                                       bands share columns),
-// so neither Dist nor E ever reaches global memory.  The gradient columns of
-// D are covered in slices of 32*NT per launch.
+// describe a mode that never materialises Dist.  Here one workgroup owns one
+// 64-row band of one pair, and its waves split the work so that the
+// dependency chain of the sweep never waits on a matrix instruction:
+//  - the band wave runs the recurrence (lane = row, as in the unfused
+//    kernel) and reads each cell's distance from an LDS ring;
+//  - distance helper waves compute the ring's 64 x 16 blocks ahead of it on
+//    fp64 MFMA, from the band's x rows (resident in LDS) and the y rows of
+//    the block, with the same operations in the same order as the distance
+//    kernel, so fused and unfused distances are bit-identical;
+//  - in the reverse sweep the band wave replaces each ring entry by its
+//    alignment value E = 2^(Xnm - X - T') once the cell is done, and
+//    chain-rule helper waves consume every completed 16-column block on
+//    fp32 MFMA: dx of the band's rows (kept in registers; each helper owns a
+//    slice of the columns of D) and dy of the block's columns (atomic adds:
+//    the bands share columns);
+//  - one wave hands the band's bottom row to the next band's workgroup and
+//    receives the row above from the previous one (segment_io_wave).
+// All coordination inside a workgroup goes through LDS counters.
 #include "sdtw_dp_common.h"
 
 namespace sdtw {
 
-constexpr int kDRing = 80;   // distance/E ring columns per band (79 are live)
-constexpr int kDPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
+constexpr int kFR = 128;     // distance/E ring columns per band (8 blocks of 16)
+constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
+constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
+constexpr int kRevHelpD = 2; // distance helpers, reverse sweep
+constexpr int kRevHelpC = 2; // chain-rule helpers, reverse sweep
 
 __host__ __device__ inline int fused_pitch(int64_t D) { return (int)(((D + 3) / 4) * 4 + 4); }
 
-size_t fused_lds_bytes(int W, int64_t D) {
-  return (size_t)W * (64 * (size_t)fused_pitch(D) + (size_t)kDRing * kDPitch) * 4;
+// Dynamic LDS of one workgroup: the band's x rows and the distance/E ring.
+size_t fused_lds_bytes(int64_t D) {
+  return (size_t)64 * fused_pitch(D) * 4 + (size_t)kFR * kFPitch * 4;
 }
 
-// Bands per workgroup for the fused kernels: as many as the LDS holds (the
-// x rows of each band plus its ring), 0 when D is beyond what they support.
-int fused_bands_per_wg(int64_t D) {
-  if (D < 1 || D > kFusedMaxD) return 0;
-  const size_t static_lds = 3 * kRing * 8 + 64;
-  for (int W : {4, 2, 1})
-    if (fused_lds_bytes(W, D) + static_lds <= 163840) return W;
-  return 0;
-}
+// One band per workgroup; 0 when D is beyond what the kernels hold on chip.
+int fused_bands_per_wg(int64_t D) { return (D >= 1 && D <= kFusedMaxD) ? 1 : 0; }
 
-template <int NT>
-struct GradAcc {
-  v16f x[2][NT];
-  float rsum[2];
+struct FusedShared {
+  double ring_in[kRingC + kCH];   // row above the band (from the previous band)
+  double ring_out[kRingC + kCH];  // the band's bottom row (to the next band)
+  unsigned wr_in, rd_in, wr_out, rd_out;
+  unsigned d_ready;               // distance blocks published, in order
+  unsigned dp_done;               // chunks completed by the band wave
+  unsigned e_free[kRevHelpC];     // blocks released by each chain-rule helper
+  unsigned ticket;
 };
 
-template <bool REV, int W, int KD, int NT>
-__global__ __launch_bounds__(W * 64) void k_dp_fused(DPArgs a, int64_t d0) {
-  extern __shared__ float smem[];
-  __shared__ double ring[W > 1 ? W - 1 : 1][kRing];
-  __shared__ unsigned s_ticket;
+__device__ __forceinline__ unsigned umin_u(unsigned a, unsigned b) { return a < b ? a : b; }
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  if (threadIdx.x == 0) s_ticket = atomicAdd(&a.ctrl[0], 1u);
-  __syncthreads();
-  const unsigned ticket = s_ticket;
-  const int seg = (int)(ticket / (unsigned)a.B);
-  const int b = (int)(ticket % (unsigned)a.B);
-
-  const int64_t N = a.N, M = a.M, D = a.D, S = a.S;
-  const int P = fused_pitch(D);
-  const int band = seg * W + w;
-  const int nb_seg = min(W, a.nbands - seg * W);
-  const bool active = w < nb_seg;
-  const int64_t r0 = (int64_t)(active ? band : 0) * 64;
+// ---------------------------------------------------------------------------
+// Band wave.
+// ---------------------------------------------------------------------------
+template <bool REV>
+__device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, float* dr, int b,
+                                           int band, int lane) {
+  const int64_t N = a.N, M = a.M, S = a.S;
+  const int64_t r0 = (int64_t)band * 64;
   const int64_t i = r0 + lane;
-  const bool row_ok = active && i < N;
   const int qcount = (int)(sweep_steps(M) / kCH);
-  const int qtot = qcount + kLag * (nb_seg - 1);
-  const bool last_in_seg = (w == nb_seg - 1);
-  const bool produce_global = active && last_in_seg && (seg + 1 < a.nseg);
-  const bool consume_global = active && (w == 0) && (seg > 0);
-
-  unsigned* prog_in = a.ctrl + 2 + (int64_t)b * a.nseg + (seg > 0 ? seg - 1 : 0);
-  unsigned* prog_out = a.ctrl + 2 + (int64_t)b * a.nseg + seg;
-  const double* Hin = a.H + ((int64_t)b * a.nseg + (seg > 0 ? seg - 1 : 0)) * M;
-  double* Hout = a.H + ((int64_t)b * a.nseg + seg) * M;
-
+  const bool top_ring = band > 0;
+  const bool out_used = band + 1 < a.nbands;
+  const unsigned Mu = (unsigned)M;
   const LaneCursor cu = lane_cursor(REV, b, i, lane, N, M, a.nbands, S);
-  double* rsk = a.R;
+  double* const rbase = a.R + cu.base;
   const double k2 = a.k2;
   const double xnm = REV ? a.loss64[b] : 0.0;
-  float* xs = smem + w * 64 * P;
-  float* dr = smem + W * 64 * P + w * kDRing * kDPitch;
-  const float* xb = a.x + (int64_t)b * N * D;
-  const float* yb = a.y + (int64_t)b * M * D;
+  const int64_t lastrow = N - 1;
+  const bool has_last = !REV && (lastrow >> 6) == band;
+  const int64_t tlast = M - 1 + (lastrow & 63);
+  const int qlast = (int)(tlast / kCH), ulast = (int)(tlast % kCH);
+  float* alignp = (REV && a.align && i < N) ? a.align + ((int64_t)b * N + (N - 1 - i)) * M
+                                            : nullptr;
+  constexpr int dir = REV ? -64 : 64;
 
-  // x rows of this band in sweep order, zero-padded to P columns.
-  if (active) {
-    for (int rr = 0; rr < 64; ++rr) {
-      const int64_t si = r0 + rr;
-      const bool ok = si < N;
-      const int64_t orr = ok ? (REV ? N - 1 - si : si) : 0;
-      for (int d = lane; d < P; d += 64) xs[rr * P + d] = (ok && d < D) ? xb[orr * D + d] : 0.f;
+  double cur = kBig;
+  double up = (band == 0 && lane == 0) ? 0.0 : kBig;
+  unsigned seen_wr = 0, seen_rd = 0, seen_d = 0;
+
+  // Reverse sweep: the forward state of the chunk's cells, requested one
+  // chunk ahead into alternating register sets.
+  double rnA[kCH], rnB[kCH];
+  auto load_x = [&](int q, double (&R_)[kCH]) {
+    const double* p0 = rbase + (int64_t)q * kCH * dir;
+    const double* p8 = p0 + 8 * dir;
+#pragma unroll
+    for (int u = 0; u < kCH; ++u) R_[u] = (u < 8 ? p0 : p8)[(u & 7) * dir];
+  };
+  if (REV) load_x(0, rnA);
+
+  auto chunk = [&](int q, const double (&rn)[kCH], double (&rn2)[kCH]) {
+    const int t0 = q * kCH;
+    double top[kCH];
+    if (top_ring) {
+      const unsigned need = umin_u((unsigned)t0 + kCH, Mu);
+      if (seen_wr < need) seen_wr = lds_wait_ge(&sh.wr_in, need);
+#pragma unroll
+      for (int u = 0; u < kCH; ++u) top[u] = sh.ring_in[(t0 + u) & (kRingC - 1)];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kCH; ++u) top[u] = kBig;
     }
+    if (REV) load_x(q + 1 < qcount ? q + 1 : q, rn2);
+    // Distances of the chunk's cells: blocks 0..q must be in the ring.
+    if (seen_d < (unsigned)q + 1) seen_d = lds_wait_ge(&sh.d_ready, (unsigned)q + 1);
+    float dn[kCH];
+#pragma unroll
+    for (int u = 0; u < kCH; ++u) dn[u] = dr[((t0 + u - lane) & (kFR - 1)) * kFPitch + lane];
+
+    double bottom[kCH];
+    double* sp = rbase + (int64_t)t0 * dir;
+    double* sp8 = sp + 8 * dir;
+    const bool mask = t0 < 64;
+#pragma unroll
+    for (int u = 0; u < kCH; ++u) {
+      const int t = t0 + u;
+      const bool boundary = mask && t < lane;   // column < 0
+      double d = (double)dn[u] * k2;
+      d = boundary ? kBig : d;
+      const double upn = wave_shr1(cur, top[u]);
+      const double tp = softmin2_part(up, upn, cur);
+      const double c = tp + d;
+      up = upn;
+      cur = c;
+      bottom[u] = c;
+      if (!REV) {
+        __builtin_nontemporal_store(c, (u < 8 ? sp : sp8) + (u & 7) * dir);
+      } else if (!boundary) {
+        const float ev = align_entry(xnm, rn[u], tp);
+        dr[((t - lane) & (kFR - 1)) * kFPitch + lane] = ev;
+        const int col = t - lane;
+        if (alignp && col < M) alignp[M - 1 - col] = ev;
+      }
+    }
+    if (lane == 0) lds_publish(&sh.dp_done, (unsigned)q + 1);
+
+    if (has_last && q == qlast) {
+      double v = 0.0;
+#pragma unroll
+      for (int u = 0; u < kCH; ++u) v = (u == ulast) ? bottom[u] : v;
+      if (lane == (int)(lastrow & 63)) {
+        a.loss64[b] = v;
+        a.loss[b] = (float)(v * a.g_ln2);
+      }
+    }
+    if (top_ring && lane == 0) lds_publish(&sh.rd_in, umin_u((unsigned)t0 + kCH, Mu));
+    if (out_used) {
+      const int cmax = t0 + kCH - 1 - 63;
+      if (cmax >= kRingC) {
+        const unsigned need = (unsigned)(cmax - kRingC + 1);
+        if (seen_rd < need) seen_rd = lds_wait_ge(&sh.rd_out, need);
+      }
+      if (lane == 63) {
+        // Same slot arithmetic as the unfused band waves (padded ring row).
+        const int s0 = (t0 + kRingC - 63) & (kRingC - 1);
+        double* rw = &sh.ring_out[s0];
+#pragma unroll
+        for (int u = 0; u < kCH; ++u) rw[u] = bottom[u];
+        if (s0 + kCH > kRingC) sh.ring_out[0] = bottom[kRingC - s0];
+        const int done = t0 + kCH - 63;
+        lds_publish(&sh.wr_out, done <= 0 ? 0u : umin_u((unsigned)done, Mu));
+      }
+    }
+  };
+  for (int q = 0; q < qcount; q += 2) {
+    chunk(q, rnA, rnB);
+    if (q + 1 < qcount) chunk(q + 1, rnB, rnA);
   }
-  // Row norms of the four 16-row tiles, accumulated exactly as the distance
-  // kernel does (per lane over d = 4s + k, then across the four k lanes).
+}
+
+// ---------------------------------------------------------------------------
+// Distance helper h of nh: blocks p = h, h+nh, ... (sweep columns [16p, 16p+16)).
+// ---------------------------------------------------------------------------
+template <bool REV, int NHC>
+__device__ __forceinline__ void fused_dist_helper(const DPArgs& a, FusedShared& sh,
+                                                  const float* xs, float* dr, int b, int h,
+                                                  int nh, int lane) {
+  const int64_t M = a.M, D = a.D;
+  const int P = fused_pitch(D);
+  const int qcount = (int)(sweep_steps(M) / kCH);
   const int r16 = lane & 15, kk = lane >> 4;
   const int steps4 = (int)((D + 3) / 4);
+  const float* yb = a.y + (int64_t)b * M * D;
+  // Row norms of the four 16-row tiles, accumulated exactly as the distance
+  // kernel does (per lane over d = 4s + k, then across the four k lanes).
   double nxt[4];
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
@@ -114,44 +200,42 @@ __global__ __launch_bounds__(W * 64) void k_dp_fused(DPArgs a, int64_t d0) {
     p += __shfl_xor(p, 32, 64);
     nxt[ti] = p;
   }
-
-  // y operand of the next distance block, fetched one chunk ahead.
-  float yq[KD];
-  auto fetch_y = [&](int q) {
-    const int64_t sc = (int64_t)q * kCH + r16;
+  unsigned seen_dp = 0, seen_e = 0;
+  for (int p = h; p < qcount; p += nh) {
+    // Block p takes the slots of block p-8: the band wave must be past it
+    // (chunk p-4 done) and, in the reverse sweep, the chain-rule helpers
+    // must have released it.
+    if (p >= kFR / kCH) {
+      const unsigned need = (unsigned)(p - 3);
+      if (seen_dp < need) seen_dp = lds_wait_ge(&sh.dp_done, need);
+      if (REV && seen_e < (unsigned)(p - 7)) {
+        unsigned m = ~0u;
+        for (int c = 0; c < NHC; ++c) m = umin_u(m, lds_wait_ge(&sh.e_free[c], (unsigned)(p - 7)));
+        seen_e = m;
+      }
+    }
+    const int64_t sc = (int64_t)p * kCH + r16;      // sweep column of this lane
     const bool cok = sc < M;
     const int64_t oc = cok ? (REV ? M - 1 - sc : sc) : 0;
     const float* yr = yb + oc * D;
-#pragma unroll
-    for (int s = 0; s < KD; ++s) {
-      const int d = 4 * s + kk;
-      yq[s] = yr[d < D ? d : D - 1];
-    }
-  };
-  // Distances of sweep columns [16q, 16q+16) for the band's 64 rows.
-  auto dist_block = [&](int q) {
-    const int64_t c0 = (int64_t)q * kCH;
-    const bool cok = c0 + r16 < M;
     v4d acc[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) acc[ti] = (v4d){0.0, 0.0, 0.0, 0.0};
     double ny = 0.0;
+    for (int s = 0; s < steps4; ++s) {
+      const int d = 4 * s + kk;
+      const float yv = yr[d < D ? d : D - 1];
+      const double bv = (d < D && cok) ? (double)yv : 0.0;
+      ny = fma(bv, bv, ny);
 #pragma unroll
-    for (int s = 0; s < KD; ++s) {
-      if (s < steps4) {
-        const bool vd = 4 * s + kk < D;
-        const double bv = (vd && cok) ? (double)yq[s] : 0.0;
-        ny = fma(bv, bv, ny);
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          const double av = (double)xs[(16 * ti + r16) * P + 4 * s + kk];
-          acc[ti] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[ti], 0, 0, 0);
-        }
+      for (int ti = 0; ti < 4; ++ti) {
+        const double av = (double)xs[(16 * ti + r16) * P + 4 * s + kk];
+        acc[ti] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[ti], 0, 0, 0);
       }
     }
     ny += __shfl_xor(ny, 16, 64);
     ny += __shfl_xor(ny, 32, 64);
-    const int slot = (int)((c0 + r16) % kDRing);
+    float* col = dr + (int)(sc & (kFR - 1)) * kFPitch;
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -160,73 +244,98 @@ __global__ __launch_bounds__(W * 64) void k_dp_fused(DPArgs a, int64_t d0) {
         const double nxr = __shfl(nxt[ti], rl, 64);
         double v = nxr + ny - 2.0 * acc[ti][e];
         v = v > 0.0 ? v : 0.0;
-        dr[slot * kDPitch + 16 * ti + rl] = (float)v;
+        col[16 * ti + rl] = (float)v;
       }
-  };
-
-  GradAcc<NT> g;
-  if (REV) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      g.rsum[rt] = 0.f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) g.x[rt][t][e] = 0.f;
-    }
+    // Publish in block order.
+    (void)lds_wait_ge(&sh.d_ready, (unsigned)p);
+    if (lane == 0) lds_publish(&sh.d_ready, (unsigned)p + 1);
   }
-  const float g2 = REV ? 2.f * a.gl[b] : 0.f;
-  const bool want_gx = REV && a.gx != nullptr;
-  const bool want_gy = REV && a.gy != nullptr;
-  const int64_t dlim = d0 + 32 * NT < D ? d0 + 32 * NT : D;
+}
 
-  // Contributions of the completed sweep columns [16p, 16p+16).
-  auto grad_block = [&](int p) {
+// ---------------------------------------------------------------------------
+// Chain-rule helper c (reverse sweep): columns [c*DC, (c+1)*DC) of D.
+// ---------------------------------------------------------------------------
+template <int DC>
+__device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared& sh,
+                                                   const float* xs, const float* dr, int b,
+                                                   int band, int c, int lane) {
+  constexpr int NT = DC / 32;
+  const int64_t N = a.N, M = a.M, D = a.D;
+  const int P = fused_pitch(D);
+  const int qcount = (int)(sweep_steps(M) / kCH);
+  const int64_t r0 = (int64_t)band * 64;
+  const int64_t dbeg = (int64_t)c * DC;
+  const bool want_gx = a.gx != nullptr, want_gy = a.gy != nullptr;
+  if ((!want_gx && !want_gy) || dbeg >= D) {
+    if (lane == 0) lds_publish(&sh.e_free[c], (unsigned)qcount);
+    return;
+  }
+  const int64_t dend = dbeg + DC < D ? dbeg + DC : D;
+  const float g2 = 2.f * a.gl[b];
+  const float* yb = a.y + (int64_t)b * M * D;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int r16 = lane & 15, kk = lane >> 4;
+  v16f gxa[2][NT];
+  float rsum[2] = {0.f, 0.f};
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) gxa[rt][t][e] = 0.f;
+
+  const int nreal = (int)((M + kCH - 1) / kCH);
+  unsigned seen_dp = 0;
+  for (int p = 0; p < nreal; ++p) {
+    // Block p is complete once the band wave has finished chunk p+4 (the
+    // last chunk completes every remaining block).
+    const unsigned need = umin_u((unsigned)p + 5, (unsigned)qcount);
+    if (seen_dp < need) seen_dp = lds_wait_ge(&sh.dp_done, need);
     const int64_t c0 = (int64_t)p * kCH;
     if (want_gx) {
-      const int c = lane & 31, h = lane >> 5;
+      // dx += E[64 x 16] . Y[16 x DC] on v_mfma_f32_32x32x2_f32.
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int64_t sc = c0 + 2 * s + h;
         const bool cok = sc < M;
-        const int64_t oc = cok ? (REV ? M - 1 - sc : sc) : 0;
-        const int slot = (int)(sc % kDRing);
+        const int64_t oc = cok ? M - 1 - sc : 0;
+        const float* ecol = dr + (int)(sc & (kFR - 1)) * kFPitch;
         float av[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          const int row = 32 * rt + c;
-          const bool ok = cok && (r0 + row < N);
-          av[rt] = ok ? dr[slot * kDPitch + row] : 0.f;
-          g.rsum[rt] += av[rt];
+          const int row = 32 * rt + r32;
+          av[rt] = (cok && r0 + row < N) ? ecol[row] : 0.f;
+          rsum[rt] += av[rt];
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const int64_t dc = d0 + 32 * t + c;
+          const int64_t dc = dbeg + 32 * t + r32;
           const float bv = yb[oc * D + (dc < D ? dc : D - 1)];
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt)
-            g.x[rt][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[rt], bv, g.x[rt][t], 0, 0, 0);
+            gxa[rt][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[rt], bv, gxa[rt][t], 0, 0, 0);
         }
       }
     }
     if (want_gy) {
+      // dy[16 columns] += 2g (colsum(E) y - E^T . X[64 x DC]) on
+      // v_mfma_f32_16x16x4_f32, added atomically (other bands add too).
       v4f acc[2 * NT];
 #pragma unroll
       for (int t = 0; t < 2 * NT; ++t) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
       const int64_t sc = c0 + r16;
       const bool cok = sc < M;
-      const int slot = (int)(sc % kDRing);
+      const float* ecol = dr + (int)(sc & (kFR - 1)) * kFPitch;
       float cs = 0.f;
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const int row = 4 * s + kk;
-        const bool ok = cok && (r0 + row < N);
-        const float av = ok ? dr[slot * kDPitch + row] : 0.f;
+        const float av = (cok && r0 + row < N) ? ecol[row] : 0.f;
         cs += av;
 #pragma unroll
         for (int t = 0; t < 2 * NT; ++t) {
-          const int64_t dc = d0 + 16 * t + r16;
-          const float bv = dc < D ? xs[row * P + dc] : 0.f;
+          const int64_t dc = dbeg + 16 * t + r16;
+          const float bv = dc < dend ? xs[row * P + dc] : 0.f;
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[t], 0, 0, 0);
         }
       }
@@ -238,162 +347,25 @@ __global__ __launch_bounds__(W * 64) void k_dp_fused(DPArgs a, int64_t d0) {
         const float csum = __shfl(cs, ci, 64);
         const int64_t scol = c0 + ci;
         if (scol < M) {
-          const int64_t oc = REV ? M - 1 - scol : scol;
+          const int64_t oc = M - 1 - scol;
           float* gyr = a.gy + ((int64_t)b * M + oc) * D;
           const float* yr = yb + oc * D;
 #pragma unroll
           for (int t = 0; t < 2 * NT; ++t) {
-            const int64_t dc = d0 + 16 * t + r16;
-            if (dc < dlim) atomicAdd(gyr + dc, g2 * (csum * yr[dc] - acc[t][e]));
+            const int64_t dc = dbeg + 16 * t + r16;
+            if (dc < dend) atomicAdd(gyr + dc, g2 * (csum * yr[dc] - acc[t][e]));
           }
         }
       }
     }
-  };
-
-  double cur = kBig;
-  double up = (lane == 0 && r0 == 0) ? 0.0 : kBig;
-  unsigned avail = 0;
-  const int64_t lastrow = N - 1;
-  const bool has_last = !REV && active && (lastrow >> 6) == band;
-  const int64_t tlast = M - 1 + (lastrow & 63);
-  const int qlast = (int)(tlast / kCH), ulast = (int)(tlast % kCH);
-  float* alignp = (REV && a.align && row_ok) ? a.align + ((int64_t)b * N + (N - 1 - i)) * M : nullptr;
-
-  double rn[kCH], tn[kCH];
-  auto load_x = [&](int qq, double (&R_)[kCH]) {
-#pragma unroll
-    for (int u = 0; u < kCH; ++u) R_[u] = rsk[cu.base + ((int64_t)qq * kCH + u) * cu.dir];
-  };
-  auto await_cols = [&](int64_t need_) {
-    const unsigned need = (unsigned)need_;
-    if (avail < need) avail = await_progress(prog_in, need);
-  };
-  auto load_top = [&](int qq, double (&T_)[kCH]) {
-#pragma unroll
-    for (int u = 0; u < kCH; ++u) {
-      const int64_t col = (int64_t)qq * kCH + u;
-      T_[u] = Hin[col < M ? col : M - 1];
-    }
-  };
-
-  if (active) {
-    if (REV) load_x(0, rn);
-    fetch_y(0);
+    if (lane == 0) lds_publish(&sh.e_free[c], (unsigned)p + 1);
   }
-  if (consume_global) {
-    await_cols(imin64(M, kCH + kSlack));
-    load_top(0, tn);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
+  if (lane == 0) lds_publish(&sh.e_free[c], (unsigned)qcount);
 
-  for (int Q = 0; Q < qtot; ++Q) {
-    const int q = Q - kLag * w;
-    if (active && q >= 0 && q < qcount) {
-      const int64_t t0 = (int64_t)q * kCH;
-      dist_block(q);
-      const bool more = q + 1 < qcount;
-      double rn2[kCH], tn2[kCH];
-      if (more) {
-        fetch_y(q + 1);
-        if (REV) load_x(q + 1, rn2);
-        if (consume_global) {
-          await_cols(imin64(M, t0 + 2 * kCH));
-          load_top(q + 1, tn2);
-        }
-      }
-      double top[kCH];
-      if (r0 == 0) {
-#pragma unroll
-        for (int u = 0; u < kCH; ++u) top[u] = kBig;
-      } else if (!consume_global) {
-#pragma unroll
-        for (int u = 0; u < kCH; ++u) top[u] = ring[w - 1][(t0 + u) & (kRing - 1)];
-      } else {
-#pragma unroll
-        for (int u = 0; u < kCH; ++u) top[u] = tn[u];
-      }
-
-      double bottom[kCH];
-      int slot = (int)((t0 - lane + 64 * kDRing) % kDRing);
-#pragma unroll
-      for (int u = 0; u < kCH; ++u) {
-        const int64_t t = t0 + u;
-        float* cellp = dr + slot * kDPitch + lane;
-        const double d = row_ok ? (double)(*cellp) * k2 : 0.0;
-        const double upn = wave_shr1(cur, top[u]);
-        const double diag = up;
-        up = upn;
-        const double tpart = softmin2_part(diag, upn, cur);
-        double c = tpart + d;
-        c = (t - lane < 0) ? kBig : c;
-        cur = c;
-        bottom[u] = c;
-        if (!REV) {
-          __builtin_nontemporal_store(c, rsk + cu.base + t * cu.dir);
-        } else {
-          const float ev = align_entry(xnm, rn[u], tpart);
-          *cellp = ev;
-          const int64_t col = t - lane;
-          if (alignp && col >= 0 && col < M) alignp[M - 1 - col] = ev;
-        }
-        slot = slot + 1 == kDRing ? 0 : slot + 1;
-      }
-
-      // Block p is complete once lane 63 has passed column 16p+15, i.e. by
-      // the end of chunk p+4; the last chunk completes every remaining block.
-      if (REV) {
-        const int plast = (int)((M - 1) / kCH);
-        const int phi = (q == qcount - 1) ? plast : q - 4;
-        for (int p = q - 4 < 0 ? 0 : q - 4; p <= phi; ++p) grad_block(p);
-      }
-
-      if (has_last && q == qlast) {
-        double v = 0.0;
-#pragma unroll
-        for (int u = 0; u < kCH; ++u) v = (u == ulast) ? bottom[u] : v;
-        if (lane == (int)(lastrow & 63)) {
-          a.loss64[b] = v;
-          a.loss[b] = (float)(v * a.g_ln2);
-        }
-      }
-      if (!last_in_seg) {
-        if (lane == 63) {
-#pragma unroll
-          for (int u = 0; u < kCH; ++u) ring[w][(t0 + u - 63) & (kRing - 1)] = bottom[u];
-        }
-      } else if (produce_global) {
-        if (lane == 63) {
-#pragma unroll
-          for (int u = 0; u < kCH; ++u) {
-            const int64_t col = t0 + u - 63;
-            if (col >= 0 && col < M) Hout[col] = bottom[u];
-          }
-          if (((q + 1) % kPub) == 0 || q == qcount - 1) {
-            int64_t done = t0 + kCH - 63;
-            done = done < 0 ? 0 : imin64(done, M);
-            __hip_atomic_store(prog_out, (unsigned)done, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < kCH; ++u) {
-          if (REV) rn[u] = rn2[u];
-          if (consume_global) tn[u] = tn2[u];
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // dx of the band's rows for this slice of D.
-  if (want_gx && active) {
-    const int c = lane & 31, h = lane >> 5;
+  if (want_gx) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      const float rsf = g.rsum[rt] + __shfl_xor(g.rsum[rt], 32, 64);
+      const float rsf = rsum[rt] + __shfl_xor(rsum[rt], 32, 64);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int rowi = 8 * (e >> 2) + 4 * h + (e & 3);
@@ -404,56 +376,90 @@ __global__ __launch_bounds__(W * 64) void k_dp_fused(DPArgs a, int64_t d0) {
           float* gxr = a.gx + ((int64_t)b * N + orr) * D;
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            const int64_t dc = d0 + 32 * t + c;
-            if (dc < dlim) gxr[dc] = g2 * (rs * xs[(32 * rt + rowi) * P + dc] - g.x[rt][t][e]);
+            const int64_t dc = dbeg + 32 * t + r32;
+            if (dc < dend) gxr[dc] = g2 * (rs * xs[(32 * rt + rowi) * P + dc] - gxa[rt][t][e]);
           }
         }
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// One band per workgroup.  Waves: 0 = band wave, then HD distance helpers,
+// then HC chain-rule helpers (reverse only), then the hand-off wave.
+// Tickets give bands in order, so a band waits only on a smaller ticket.
+// ---------------------------------------------------------------------------
+template <bool REV, int HD, int HC, int DC>
+__global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a) {
+  extern __shared__ float smem[];
+  __shared__ FusedShared sh;
+  constexpr int kIO = HD + HC + 1;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) sh.ticket = atomicAdd(&a.ctrl[0], 1u);
+  if (threadIdx.x == 0) {
+    sh.wr_in = sh.rd_in = sh.wr_out = sh.rd_out = 0u;
+    sh.d_ready = sh.dp_done = 0u;
+    for (int c = 0; c < kRevHelpC; ++c) sh.e_free[c] = 0u;
+  }
+  __syncthreads();
+  const unsigned ticket = sh.ticket;
+  const int band = (int)(ticket / (unsigned)a.B);
+  const int b = (int)(ticket % (unsigned)a.B);
+  const int64_t N = a.N, D = a.D;
+  const int P = fused_pitch(D);
+  float* xs = smem;
+  float* dr = smem + 64 * P;
+
+  // x rows of this band in sweep order, zero-padded to P columns.
+  const float* xb = a.x + (int64_t)b * N * D;
+  const int64_t r0 = (int64_t)band * 64;
+  for (int idx = threadIdx.x; idx < 64 * P; idx += blockDim.x) {
+    const int rr = idx / P, d = idx - rr * P;
+    const int64_t si = r0 + rr;
+    const bool ok = si < N && d < D;
+    const int64_t orr = si < N ? (REV ? N - 1 - si : si) : 0;
+    xs[idx] = ok ? xb[orr * D + d] : 0.f;
+  }
+  __syncthreads();
+
+  if (w == 0) {
+    fused_band<REV>(a, sh, dr, b, band, lane);
+  } else if (w <= HD) {
+    fused_dist_helper<REV, HC>(a, sh, xs, dr, b, w - 1, HD, lane);
+  } else if (w < kIO) {
+    if (REV) fused_chain_helper<DC>(a, sh, xs, dr, b, band, w - 1 - HD, lane);
+  } else {
+    const int64_t pb = (int64_t)b * a.nseg;
+    const int64_t sin = pb + (band > 0 ? band - 1 : 0), sout = pb + band;
+    segment_io_wave(band > 0, band + 1 < a.nseg, a.ctrl + 2 + sin, a.ctrl + 2 + sout,
+                    a.H + sin * a.M, a.H + sout * a.M, sh.ring_in, &sh.wr_in, &sh.rd_in,
+                    sh.ring_out, &sh.wr_out, &sh.rd_out, (unsigned)a.M, lane);
+  }
   release_ctrl(a.ctrl, (int64_t)a.B * a.nseg);
 }
 
-template <bool REV, int W, int KD, int NT>
-static hipError_t launch_fused_one(const DPArgs& a, int64_t d0, hipStream_t s) {
-  auto kern = k_dp_fused<REV, W, KD, NT>;
-  const size_t lds = fused_lds_bytes(W, a.D);
+template <bool REV, int HD, int HC, int DC>
+static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s) {
+  auto kern = k_dp_fused<REV, HD, HC, DC>;
+  const size_t lds = fused_lds_bytes(a.D);
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)a.B * (unsigned)a.nseg;
   TimedLaunch timed_(REV ? "dp_fused_rev" : "dp_fused_fwd", s);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(W * 64), lds, s, a, d0);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3((HD + HC + 2) * 64), lds, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
-  const int W = fused_bands_per_wg(a.D);
-  if (W == 0) return hipErrorNotSupported;
-  const int kd = a.D <= 64 ? 16 : (a.D <= 128 ? 32 : 64);  // ceil(D/4) <= kd
-  if (!reverse) {
-    if (W == 4) return launch_fused_one<false, 4, 16, 1>(a, 0, s);
-    if (W == 2 && kd == 32) return launch_fused_one<false, 2, 32, 1>(a, 0, s);
-    if (W == 2) return launch_fused_one<false, 2, 64, 1>(a, 0, s);
-    return launch_fused_one<false, 1, 64, 1>(a, 0, s);
-  }
-  // Reverse: one sweep per slice of D (32 * NT columns of the gradients).
-  const int nt = a.D <= 32 ? 1 : (a.D <= 64 ? 2 : (a.D <= 96 ? 3 : 4));
-  for (int64_t d0 = 0; d0 < a.D; d0 += 32 * nt) {
-    hipError_t e;
-    if (W == 4)
-      e = nt == 1 ? launch_fused_one<true, 4, 16, 1>(a, d0, s)
-                  : launch_fused_one<true, 4, 16, 2>(a, d0, s);
-    else if (W == 2 && kd == 32)
-      e = nt == 3 ? launch_fused_one<true, 2, 32, 3>(a, d0, s)
-                  : launch_fused_one<true, 2, 32, 4>(a, d0, s);
-    else if (W == 2)
-      e = launch_fused_one<true, 2, 64, 4>(a, d0, s);
-    else
-      e = launch_fused_one<true, 1, 64, 4>(a, d0, s);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
+  if (!reverse) return launch_fused_one<false, kFwdHelpD, 0, 32>(a, s);
+  // Each of the two chain-rule helpers owns DC columns of D.
+  if (a.D <= 2 * 32) return launch_fused_one<true, kRevHelpD, kRevHelpC, 32>(a, s);
+  if (a.D <= 2 * 64) return launch_fused_one<true, kRevHelpD, kRevHelpC, 64>(a, s);
+  return launch_fused_one<true, kRevHelpD, kRevHelpC, 128>(a, s);
 }
 
 }  // namespace sdtw
