@@ -26,8 +26,14 @@ struct Layout {
   size_t part = 0;                  // fp32 split partial sums of the chain rule (unfused)
   size_t cnt_rows = 0, cnt_cols = 0;  // word offsets of the chain split counters
   size_t dist = 0;                  // fp32 band-step distances, then E (unfused)
+  unsigned hcols = 0;               // inference: hand-off ring columns (0: whole rows)
   size_t total = 0;
 };
+
+// Inference mode keeps the bands' hand-off rows as rings when every band of
+// a pair (one workgroup each) fits on the GPU at once: 256 CUs hold at least
+// one of these workgroups each.
+constexpr int64_t kInferRingMaxBands = 256;
 
 bool mul_ok(size_t a, size_t b, size_t* out) {
   if (a != 0 && b > SIZE_MAX / a) return false;
@@ -48,9 +54,27 @@ bool sizes_ok(int64_t B, int64_t N, int64_t M, int64_t D) {
 }
 
 bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L) {
-  if (!sizes_ok(B, N, M, D) || (mode != SDTW_MODE_UNFUSED && mode != SDTW_MODE_FUSED))
+  if (!sizes_ok(B, N, M, D) ||
+      (mode != SDTW_MODE_UNFUSED && mode != SDTW_MODE_FUSED && mode != SDTW_MODE_INFERENCE))
     return false;
   L->nbands = (N + 63) / 64;
+  if (mode == SDTW_MODE_INFERENCE) {
+    // Loss only: control words, the final states and the hand-off rows.
+    if (sdtw::fused_bands_per_wg(D) == 0) return false;
+    L->nseg = L->nbands;
+    L->hcols = L->nbands <= kInferRingMaxBands && M > (int64_t)sdtw::kHRing ? sdtw::kHRing : 0;
+    const size_t row = L->hcols ? L->hcols : (size_t)M;
+    size_t off = 0;
+    L->ctrl = off;
+    L->ctrl_words = 2 + 2 * (size_t)B * (size_t)L->nseg;
+    off += align_up(L->ctrl_words * 4);
+    L->loss64 = off;
+    off += align_up((size_t)B * 8);
+    L->H = off;
+    off += align_up((size_t)B * (size_t)L->nseg * row * 8);
+    L->total = off;
+    return true;
+  }
   const int bpw = mode == SDTW_MODE_FUSED ? sdtw::fused_bands_per_wg(D) : sdtw::kBandsPerWG;
   if (bpw == 0) return false;  // fused mode: D beyond what the kernels hold on chip
   L->nseg = (L->nbands + bpw - 1) / bpw;
@@ -98,7 +122,7 @@ DPArgs dp_args(const Layout& L, char* ws, const float* x, const float* y,
   a.ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl) + (reverse ? 2 + B * L.nseg : 0);
   a.loss64 = reinterpret_cast<double*>(ws + L.loss64);
   a.H = reinterpret_cast<double*>(ws + L.H);
-  a.R = reinterpret_cast<double*>(ws + L.R);
+  a.R = L.R ? reinterpret_cast<double*>(ws + L.R) : nullptr;
   a.R2 = L.R2 ? reinterpret_cast<double*>(ws + L.R2) : nullptr;
   a.dsk = L.dist ? reinterpret_cast<float*>(ws + L.dist) : nullptr;
   a.N = N;
@@ -167,7 +191,18 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
   // per forward (later launches find them cleared by the kernels).
   hipError_t e = sdtw::launch_zero_u32(reinterpret_cast<unsigned*>(ws + L.ctrl),
                                        (int64_t)L.ctrl_words, s);
-  if (fused) {
+  if (mode == SDTW_MODE_INFERENCE) {
+    if (L.hcols) {
+      // Ring hand-off needs every band of a pair resident at once (one
+      // workgroup per band, at least one workgroup per CU).
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return SDTW_ERR_HIP;
+      if ((int64_t)cus < L.nseg) return SDTW_ERR_UNSUPPORTED;
+    }
+    if (e == hipSuccess) e = sdtw::launch_infer(a, L.hcols, s);
+  } else if (fused) {
     if (e == hipSuccess) e = sdtw::launch_dp_fused(a, false, s);
   } else {
     // Both sweeps at once: the loss comes from the forward one, and the
@@ -189,6 +224,7 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
   if (st != SDTW_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
+  if (mode == SDTW_MODE_INFERENCE) return SDTW_ERR_UNSUPPORTED;  // nothing kept to go back on
   DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma, mode == SDTW_MODE_FUSED);
   if (mode == SDTW_MODE_FUSED) {
     // One reverse sweep per slice of D; it writes dx, adds into dy and, if

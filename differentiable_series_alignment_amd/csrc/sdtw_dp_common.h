@@ -100,12 +100,27 @@ __device__ __forceinline__ void lds_publish(unsigned* p, unsigned v) {
 // them, so no cache write-back or invalidation is needed.  A segment waits
 // only on a smaller ticket, which is running, so the loop ends; the poll cap
 // guarantees the wave exits regardless.
+//
+// Global rows are either whole (hcols = 0: column c at H[c]) or rings of
+// hcols columns (a power of two; column c at H[c % hcols]).  With rings the
+// consumer also publishes how many columns it has fetched (fetch_out) and
+// the producer does not overwrite a slot before its consumer has fetched
+// the column in it (fetch_back); that wait points at a larger ticket, so
+// ring mode is only used where a pair's segments all fit on the GPU at once
+// and tickets run pair by pair.
+struct GlobalRow {
+  unsigned hcols;             // 0: whole rows
+  const unsigned* fetch_back; // consumer's fetched count (output side, ring mode)
+  unsigned* fetch_out;        // own fetched count (input side, ring mode)
+};
+
 __device__ __forceinline__ void segment_io_wave(
     bool do_in, bool do_out, const unsigned* prog_in, unsigned* prog_out,
     const double* Hin, double* Hout, double* ring_in, unsigned* wr_in,
     const unsigned* rd_in, const double* ring_out, const unsigned* wr_out,
-    unsigned* rd_out, unsigned M, int lane) {
-  unsigned fetched = 0, known_in = 0, pub = 0;
+    unsigned* rd_out, unsigned M, int lane, GlobalRow gr = GlobalRow{0u, nullptr, nullptr}) {
+  const unsigned hmask = gr.hcols ? gr.hcols - 1 : 0xffffffffu;
+  unsigned fetched = 0, known_in = 0, pub = 0, known_back = 0;
   for (uint32_t spin = 0; spin < kSpinCap; ++spin) {
     const bool in_left = do_in && fetched < M;
     const bool out_left = do_out && pub < M;
@@ -122,17 +137,25 @@ __device__ __forceinline__ void segment_io_wave(
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         for (unsigned c = fetched + lane; c < lim; c += 64)
           ring_in[c & (kRingC - 1)] =
-              __hip_atomic_load(Hin + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_load(Hin + (c & hmask), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (lane == 0) lds_publish(wr_in, lim);
+        if (gr.fetch_out && lane == 0)   // the loads above have returned
+          __hip_atomic_store(gr.fetch_out, lim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         fetched = lim;
         moved = true;
       }
     }
     if (out_left) {
-      const unsigned avail = lds_wait_ge(wr_out, 0);
+      unsigned avail = lds_wait_ge(wr_out, 0);
+      if (gr.hcols) {
+        if (avail > known_back + gr.hcols)
+          known_back = __hip_atomic_load(gr.fetch_back, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        if (avail > known_back + gr.hcols) avail = known_back + gr.hcols;
+      }
       if (avail > pub) {
         for (unsigned c = pub + lane; c < avail; c += 64)
-          __hip_atomic_store(Hout + c, ring_out[c & (kRingC - 1)], __ATOMIC_RELAXED,
+          __hip_atomic_store(Hout + (c & hmask), ring_out[c & (kRingC - 1)], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         if (lane == 0) lds_publish(rd_out, avail);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);

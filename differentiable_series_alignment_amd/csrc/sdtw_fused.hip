@@ -56,7 +56,7 @@ __device__ __forceinline__ unsigned umin_u(unsigned a, unsigned b) { return a < 
 // ---------------------------------------------------------------------------
 // Band wave.
 // ---------------------------------------------------------------------------
-template <bool REV>
+template <bool REV, bool STORE>
 __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, float* dr, int b,
                                            int band, int lane) {
   const int64_t N = a.N, M = a.M, S = a.S;
@@ -129,7 +129,7 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
       cur = c;
       bottom[u] = c;
       if (!REV) {
-        __builtin_nontemporal_store(c, (u < 8 ? sp : sp8) + (u & 7) * dir);
+        if (STORE) __builtin_nontemporal_store(c, (u < 8 ? sp : sp8) + (u & 7) * dir);
       } else if (!boundary) {
         const float ev = align_entry(xnm, rn[u], tp);
         dr[((t - lane) & (kFR - 1)) * kFPitch + lane] = ev;
@@ -389,9 +389,13 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
 // One band per workgroup.  Waves: 0 = band wave, then HD distance helpers,
 // then HC chain-rule helpers (reverse only), then the hand-off wave.
 // Tickets give bands in order, so a band waits only on a smaller ticket.
+// INFER: the forward sweep for the loss alone: no state is stored, tickets
+// run pair by pair, and the rows handed between bands are global rings of
+// kHRing columns (whole rows when a pair has more bands than the GPU holds
+// workgroups at once, see the API).
 // ---------------------------------------------------------------------------
-template <bool REV, int HD, int HC, int DC>
-__global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a) {
+template <bool REV, bool INFER, int HD, int HC, int DC>
+__global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsigned hcols) {
   extern __shared__ float smem[];
   __shared__ FusedShared sh;
   constexpr int kIO = HD + HC + 1;
@@ -405,8 +409,8 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a) {
   }
   __syncthreads();
   const unsigned ticket = sh.ticket;
-  const int band = (int)(ticket / (unsigned)a.B);
-  const int b = (int)(ticket % (unsigned)a.B);
+  const int band = INFER ? (int)(ticket % (unsigned)a.nseg) : (int)(ticket / (unsigned)a.B);
+  const int b = INFER ? (int)(ticket / (unsigned)a.nseg) : (int)(ticket % (unsigned)a.B);
   const int64_t N = a.N, D = a.D;
   const int P = fused_pitch(D);
   float* xs = smem;
@@ -425,7 +429,7 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a) {
   __syncthreads();
 
   if (w == 0) {
-    fused_band<REV>(a, sh, dr, b, band, lane);
+    fused_band<REV, !INFER>(a, sh, dr, b, band, lane);
   } else if (w <= HD) {
     fused_dist_helper<REV, HC>(a, sh, xs, dr, b, w - 1, HD, lane);
   } else if (w < kIO) {
@@ -433,33 +437,45 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a) {
   } else {
     const int64_t pb = (int64_t)b * a.nseg;
     const int64_t sin = pb + (band > 0 ? band - 1 : 0), sout = pb + band;
+    const int64_t row = hcols ? hcols : a.M;   // doubles per hand-off row
+    GlobalRow gr{0u, nullptr, nullptr};
+    if (INFER && hcols) {
+      // Fetched counts follow the progress counts in the control words.
+      unsigned* fetched = a.ctrl + 2 + (int64_t)a.B * a.nseg;
+      gr = GlobalRow{hcols, fetched + pb + band + 1, fetched + pb + band};
+    }
     segment_io_wave(band > 0, band + 1 < a.nseg, a.ctrl + 2 + sin, a.ctrl + 2 + sout,
-                    a.H + sin * a.M, a.H + sout * a.M, sh.ring_in, &sh.wr_in, &sh.rd_in,
-                    sh.ring_out, &sh.wr_out, &sh.rd_out, (unsigned)a.M, lane);
+                    a.H + sin * row, a.H + sout * row, sh.ring_in, &sh.wr_in, &sh.rd_in,
+                    sh.ring_out, &sh.wr_out, &sh.rd_out, (unsigned)a.M, lane, gr);
   }
-  release_ctrl(a.ctrl, (int64_t)a.B * a.nseg);
+  release_ctrl(a.ctrl, (INFER && hcols ? 2 : 1) * (int64_t)a.B * a.nseg);
 }
 
-template <bool REV, int HD, int HC, int DC>
-static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s) {
-  auto kern = k_dp_fused<REV, HD, HC, DC>;
+template <bool REV, bool INFER, int HD, int HC, int DC>
+static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcols = 0) {
+  auto kern = k_dp_fused<REV, INFER, HD, HC, DC>;
   const size_t lds = fused_lds_bytes(a.D);
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)a.B * (unsigned)a.nseg;
-  TimedLaunch timed_(REV ? "dp_fused_rev" : "dp_fused_fwd", s);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3((HD + HC + 2) * 64), lds, s, a);
+  TimedLaunch timed_(INFER ? "dp_infer" : (REV ? "dp_fused_rev" : "dp_fused_fwd"), s);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3((HD + HC + 2) * 64), lds, s, a, hcols);
   return hipGetLastError();
 }
 
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
-  if (!reverse) return launch_fused_one<false, kFwdHelpD, 0, 32>(a, s);
+  if (!reverse) return launch_fused_one<false, false, kFwdHelpD, 0, 32>(a, s);
   // Each of the two chain-rule helpers owns DC columns of D.
-  if (a.D <= 2 * 32) return launch_fused_one<true, kRevHelpD, kRevHelpC, 32>(a, s);
-  if (a.D <= 2 * 64) return launch_fused_one<true, kRevHelpD, kRevHelpC, 64>(a, s);
-  return launch_fused_one<true, kRevHelpD, kRevHelpC, 128>(a, s);
+  if (a.D <= 2 * 32) return launch_fused_one<true, false, kRevHelpD, kRevHelpC, 32>(a, s);
+  if (a.D <= 2 * 64) return launch_fused_one<true, false, kRevHelpD, kRevHelpC, 64>(a, s);
+  return launch_fused_one<true, false, kRevHelpD, kRevHelpC, 128>(a, s);
+}
+
+hipError_t launch_infer(const DPArgs& a, unsigned hcols, hipStream_t s) {
+  if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
+  return launch_fused_one<false, true, kFwdHelpD, 0, 32>(a, s, hcols);
 }
 
 }  // namespace sdtw

@@ -92,6 +92,10 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_dp_both(const DPArgs& a, hipStream_t s);
 // Fused: one sweep per launch (the reverse one with the chain rule inside).
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s);
+// Loss only: the fused forward sweep without stored state; hand-off rows are
+// global rings of `hcols` columns (0: whole rows).
+constexpr unsigned kHRing = 512;
+hipError_t launch_infer(const DPArgs& a, unsigned hcols, hipStream_t s);
 // Chain rule of the unfused backward.  The row pass forms E = 2^(Xnm-X-T')
 // from R and R2 into `esk` (the distance array, no longer needed) and, if
 // gx is given, writes dx; the column pass reads E from `esk` and writes dy.

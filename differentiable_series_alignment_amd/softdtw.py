@@ -95,10 +95,40 @@ class _SoftDTWFunction(torch.autograd.Function):
         return gx, gy, None, None
 
 
+def _loss_only(x: torch.Tensor, y: torch.Tensor, gamma: float):
+    """The loss through the library's inference mode (no state kept, O(B*N)
+    workspace), or None where that mode does not apply (D > 256, or a GPU
+    too small for its ring hand-off)."""
+    x = x.contiguous()
+    y = y.contiguous()
+    B, N, D = x.shape
+    M = y.shape[1]
+    mode = L.SDTW_MODE_INFERENCE
+    nbytes = L.sdtw_workspace_bytes(B, N, M, D, mode)
+    if nbytes == 0:
+        return None
+    with torch.cuda.device(x.device):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+        loss = torch.empty(B, dtype=torch.float32, device=x.device)
+        st = L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, gamma, mode,
+                            ws.data_ptr(), nbytes, loss.data_ptr(), _stream(x.device))
+    if st == L.SDTW_ERR_UNSUPPORTED:
+        return None
+    L.check(st, "sdtw_forward")
+    return loss
+
+
 def soft_dtw(x: torch.Tensor, y: torch.Tensor, gamma: float = 1.0,
              fused: bool = False) -> torch.Tensor:
-    """Per-pair Soft-DTW loss (B,) with autograd support."""
+    """Per-pair Soft-DTW loss (B,) with autograd support.  When no gradient
+    can be asked for (autograd off, or neither input requires one) the loss
+    comes from the inference mode, which keeps no state; its value is bitwise
+    the one of the other modes."""
     _validate(x, y, gamma)
+    if not (torch.is_grad_enabled() and (x.requires_grad or y.requires_grad)):
+        loss = _loss_only(x, y, float(gamma))
+        if loss is not None:
+            return loss
     mode = L.SDTW_MODE_FUSED if fused else L.SDTW_MODE_UNFUSED
     return _SoftDTWFunction.apply(x, y, float(gamma), mode)
 
@@ -107,7 +137,8 @@ class SoftDTW(torch.nn.Module):
     """``SoftDTW(gamma=1.0, dist="sqeuclidean", fused=False, normalize=False)``.
 
     ``normalize=True`` returns SoftDTW(x,y) - (SoftDTW(x,x) + SoftDTW(y,y))/2
-    and requires x.shape == y.shape (README "Normalization")."""
+    and requires x.shape == y.shape (README "Normalization"); the three
+    terms run as one batch of 3B pairs."""
 
     def __init__(self, gamma: float = 1.0, dist: str = "sqeuclidean",
                  fused: bool = False, normalize: bool = False):
@@ -127,10 +158,13 @@ class SoftDTW(torch.nn.Module):
             if tuple(x.shape) != tuple(y.shape):
                 raise ValueError("normalize=True requires x.shape == y.shape")
             _validate(x, y, self.gamma)
-            xy = soft_dtw(x, y, self.gamma, self.fused)
-            xx = soft_dtw(x, x, self.gamma, self.fused)
-            yy = soft_dtw(y, y, self.gamma, self.fused)
-            return xy - 0.5 * (xx + yy)
+            # The three terms as one batch of 3B pairs (x,y), (x,x), (y,y):
+            # one pass through the kernels; autograd sums the gradients that
+            # reach x and y through the concatenation.
+            B = x.shape[0]
+            loss = soft_dtw(torch.cat([x, x, y], 0), torch.cat([y, x, y], 0),
+                            self.gamma, self.fused)
+            return loss[:B] - 0.5 * (loss[B:2 * B] + loss[2 * B:])
         return soft_dtw(x, y, self.gamma, self.fused)
 
     def extra_repr(self) -> str:

@@ -28,6 +28,18 @@
  *                      programme; no B x N x M distance or E tensor exists.
  *                      Supports D <= 256 (sdtw_workspace_bytes returns 0 and
  *                      the calls return SDTW_ERR_INVALID_ARG beyond that).
+ *   SDTW_MODE_INFERENCE the loss alone (the README's "When to Use Each Mode"
+ *                      names inference as a use): distances recomputed as
+ *                      in fused mode and no
+ *                      DP state kept, so the workspace holds only control
+ *                      words and the rows handed between 64-row bands, as
+ *                      rings of 512 columns (O(B*N) bytes; whole rows, i.e.
+ *                      O(B*N*M/64), when N > 16384).  D <= 256.
+ *                      sdtw_backward returns SDTW_ERR_UNSUPPORTED for it, and
+ *                      sdtw_forward returns SDTW_ERR_UNSUPPORTED on a GPU
+ *                      with fewer CUs than the pair has 64-row bands (the
+ *                      ring hand-off needs them all resident).  The loss is
+ *                      bitwise the one the other two modes return.
  * Both modes keep the forward DP state (fp64, B x N x M) for the backward.
  * Distances are accumulated in fp64 and rounded once to fp32 in both modes,
  * so fused and unfused see identical distances, losses and alignment
@@ -69,7 +81,8 @@ typedef enum {
 
 typedef enum {
     SDTW_MODE_UNFUSED = 0,
-    SDTW_MODE_FUSED = 1
+    SDTW_MODE_FUSED = 1,
+    SDTW_MODE_INFERENCE = 2
 } sdtw_mode_t;
 
 /* Version of this ABI (SDTW_ABI_VERSION). */

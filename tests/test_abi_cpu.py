@@ -72,7 +72,7 @@ def _bwd(**kw):
 @pytest.mark.parametrize("kw", [
     dict(gamma=0.0), dict(gamma=-1.0), dict(gamma=float("nan")), dict(gamma=float("inf")),
     dict(B=0), dict(N=0), dict(M=0), dict(D=0), dict(N=-3),
-    dict(x=None), dict(y=None), dict(mode=2), dict(workspace=None),
+    dict(x=None), dict(y=None), dict(mode=3), dict(mode=-1), dict(workspace=None),
     dict(workspace=FAKE * 256 + 8),
 ])
 def test_forward_backward_reject_invalid(kw):
@@ -133,3 +133,16 @@ def test_timing_switch_without_launches():
     assert L.sdtw_timing_collect() == []
     assert L.sdtw_timing(False) == L.SDTW_OK
     assert L.lib().sdtw_timing_collect(None, None, 0) == 0
+
+
+def test_inference_mode_workspace_and_backward():
+    """Inference mode: a workspace without B x N x M arrays (rows handed
+    between bands only), D <= 256, and no backward."""
+    train = L.sdtw_workspace_bytes(32, 4096, 4096, 128, L.SDTW_MODE_UNFUSED)
+    infer = L.sdtw_workspace_bytes(32, 4096, 4096, 128, L.SDTW_MODE_INFERENCE)
+    assert 0 < infer and infer * 1000 < train
+    # ring hand-off: O(B*N) bytes, independent of M
+    assert (L.sdtw_workspace_bytes(4, 1000, 5000, 3, L.SDTW_MODE_INFERENCE)
+            == L.sdtw_workspace_bytes(4, 1000, 9000, 3, L.SDTW_MODE_INFERENCE))
+    assert L.sdtw_workspace_bytes(2, 10, 10, 257, L.SDTW_MODE_INFERENCE) == 0
+    assert _bwd(mode=L.SDTW_MODE_INFERENCE, D=3) == L.SDTW_ERR_UNSUPPORTED

@@ -348,6 +348,46 @@ def test_launch_timing_records_each_kernel(S):
     assert all(t > 0 for _, t in recs)
 
 
+@pytest.mark.parametrize("B,N,M,D", [(2, 16, 16, 1), (3, 70, 45, 3), (3, 1100, 700, 5),
+                                     (2, 300, 2000, 4), (1, 64, 5000, 2), (4, 130, 513, 8)])
+def test_inference_mode_matches_training_loss(S, B, N, M, D):
+    """The inference mode (no state kept; rows handed between bands through
+    512-column rings when M > 512) returns bitwise the training forward's
+    loss, through the C ABI; without autograd the Python layer uses it."""
+    from differentiable_series_alignment_amd import _lib as L
+    x, y = pair_batch(B, N, M, D, seed=B + N + M + D)
+    x, y = x.to(DEV), y.to(DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for mode in (L.SDTW_MODE_UNFUSED, L.SDTW_MODE_INFERENCE):
+        nb = L.sdtw_workspace_bytes(B, N, M, D, mode)
+        ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        loss = torch.empty(B, device=DEV)
+        for _ in range(2):   # the second call finds the control words it left
+            L.check(L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, 0.6, mode,
+                                   ws.data_ptr(), nb, loss.data_ptr(), s), "sdtw_forward")
+        out[mode] = loss
+    torch.testing.assert_close(out[L.SDTW_MODE_INFERENCE], out[L.SDTW_MODE_UNFUSED],
+                               rtol=0, atol=0)
+    with torch.no_grad():
+        torch.testing.assert_close(S.soft_dtw(x, y, 0.6), out[L.SDTW_MODE_UNFUSED],
+                                   rtol=0, atol=0)
+
+
+def test_normalized_is_one_batch(S):
+    """SoftDTW(normalize=True) runs its three terms as one batch of 3B pairs."""
+    from differentiable_series_alignment_amd import _lib as L
+    x, y = pair_batch(3, 40, 40, 4, seed=13)
+    xd = x.to(DEV).requires_grad_(True)
+    L.sdtw_timing(True)
+    try:
+        S.SoftDTW(gamma=1.0, normalize=True)(xd, y.to(DEV)).sum().backward()
+        names = [n for n, _ in L.sdtw_timing_collect()]
+    finally:
+        L.sdtw_timing(False)
+    assert names.count("dp_both") == 1, names
+
+
 def test_small_gamma_finite(S):
     x, y = pair_batch(4, 700, 650, 32, seed=8)
     l, gx, gy = gpu_value_and_grad(S, x, y, 0.01)
