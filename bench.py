@@ -168,6 +168,41 @@ def measure(L, torch, x, y, gamma, mode, steps, warmup):
     return e0.elapsed_time(e1) / steps, fwd, bwd, stream
 
 
+def measure_inference(L, torch, x, y, gamma, steps, warmup):
+    """Milliseconds per loss-only forward (inference mode: no state kept,
+    workspace O(B*N)) through the C ABI, and the workspace size in MiB;
+    None when the device cannot hold every band of a pair at once."""
+    B, N, D = x.shape
+    M = y.shape[1]
+    mode = L.SDTW_MODE_INFERENCE
+    nbytes = L.sdtw_workspace_bytes(B, N, M, D, mode)
+    if nbytes == 0:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    loss = torch.empty(B, dtype=torch.float32, device=x.device)
+    s = int(torch.cuda.current_stream(x.device).cuda_stream)
+
+    def fwd():
+        return L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, gamma, mode,
+                              ws.data_ptr(), nbytes, loss.data_ptr(), s)
+
+    if fwd() == L.SDTW_ERR_UNSUPPORTED:
+        return None
+    for _ in range(warmup):
+        L.check(fwd(), "sdtw_forward")
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        L.check(fwd(), "sdtw_forward")
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / steps
+    return {"ms_per_forward": t, "cells_per_s": B * N * M / (t * 1e-3),
+            "workspace_mib": nbytes / 2**20}
+
+
 def peak_mib(torch, SoftDTW, x, y, gamma, fused):
     """Peak device memory of one autograd fwd+bwd (SoftDTW(...)(x, y).mean()
     .backward()) above what was allocated before, and the part of it taken
@@ -252,6 +287,7 @@ def main():
     ms_f, _, _, _ = measure(L, torch, x, y, gamma, L.SDTW_MODE_FUSED,
                             max(5, args.steps // 5), 2)
     peak_f, peak_over_f = peak_mib(torch, SoftDTW, x, y, gamma, True)
+    infer = measure_inference(L, torch, x, y, gamma, max(5, args.steps // 5), 2)
 
     per_config = []
     if not args.headline_only:
@@ -269,6 +305,7 @@ def main():
                 pk, pko = peak_mib(torch, SoftDTW, x2, y2, g_, mode == L.SDTW_MODE_FUSED)
                 entry[name] = {"ms_per_step": t, "cells_per_s": b_ * n_ * m_ / (t * 1e-3),
                                "peak_mib": pk, "peak_mib_over_io": pko}
+            entry["inference"] = measure_inference(L, torch, x2, y2, g_, 5, 2)
             per_config.append(entry)
             del x2, y2
             torch.cuda.empty_cache()
@@ -293,6 +330,7 @@ def main():
         "peak_mib_over_io": peak_over,
         "fused": {"ms_per_step": ms_f, "cells_per_s": cells / (ms_f * 1e-3),
                   "peak_mib": peak_f, "peak_mib_over_io": peak_over_f},
+        "inference": infer,
         "roofline": {"kernel": "both sweeps of the dynamic programme (k_dp_unfused)",
                      "bound": "alu", "achieved": achieved, "peak": PEAK_ALU_TOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_ALU_TOPS,

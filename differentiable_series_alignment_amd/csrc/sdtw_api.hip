@@ -30,10 +30,25 @@ struct Layout {
   size_t total = 0;
 };
 
-// Inference mode keeps the bands' hand-off rows as rings when every band of
-// a pair (one workgroup each) fits on the GPU at once: 256 CUs hold at least
-// one of these workgroups each.
-constexpr int64_t kInferRingMaxBands = 256;
+// Inference mode hands each band's bottom row to the next band either whole
+// (B*nbands*M*8 bytes; tickets run band-major, the fastest order when the
+// workgroups of all pairs do not fit on the GPU at once) or through rings of
+// kHRing columns (B*nbands*kHRing*8 bytes; a band may then wait on the band
+// below, so tickets run pair-major and every band of a pair must be resident
+// together: at most one workgroup per CU of the 256).  Rings are taken when
+// they cost no speed, i.e. all B*nbands workgroups fit at once, or when whole
+// rows would exceed both kInferRowsFree and the size of the inputs.
+constexpr int64_t kInferCUs = 256;
+constexpr size_t kInferRowsFree = size_t(16) << 20;
+
+unsigned infer_ring_cols(int64_t B, int64_t nbands, int64_t M, int64_t N, int64_t D) {
+  if (M <= (int64_t)sdtw::kHRing || nbands > kInferCUs) return 0;
+  const size_t rows = (size_t)B * (size_t)nbands * (size_t)M * 8;
+  const size_t inputs = (size_t)B * (size_t)(N + M) * (size_t)D * 4;
+  const bool all_resident = B * nbands <= kInferCUs;
+  const bool rows_too_big = rows > kInferRowsFree && rows > inputs;
+  return (all_resident || rows_too_big) ? sdtw::kHRing : 0;
+}
 
 bool mul_ok(size_t a, size_t b, size_t* out) {
   if (a != 0 && b > SIZE_MAX / a) return false;
@@ -62,7 +77,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
     // Loss only: control words, the final states and the hand-off rows.
     if (sdtw::fused_bands_per_wg(D) == 0) return false;
     L->nseg = L->nbands;
-    L->hcols = L->nbands <= kInferRingMaxBands && M > (int64_t)sdtw::kHRing ? sdtw::kHRing : 0;
+    L->hcols = infer_ring_cols(B, L->nbands, M, N, D);
     const size_t row = L->hcols ? L->hcols : (size_t)M;
     size_t off = 0;
     L->ctrl = off;

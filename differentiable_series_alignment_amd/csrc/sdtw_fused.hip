@@ -389,10 +389,9 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
 // One band per workgroup.  Waves: 0 = band wave, then HD distance helpers,
 // then HC chain-rule helpers (reverse only), then the hand-off wave.
 // Tickets give bands in order, so a band waits only on a smaller ticket.
-// INFER: the forward sweep for the loss alone: no state is stored, tickets
-// run pair by pair, and the rows handed between bands are global rings of
-// kHRing columns (whole rows when a pair has more bands than the GPU holds
-// workgroups at once, see the API).
+// INFER: the forward sweep for the loss alone: no state is stored, and the
+// rows handed between bands are either whole (hcols = 0) or global rings of
+// hcols columns; with rings tickets run pair by pair (see above).
 // ---------------------------------------------------------------------------
 template <bool REV, bool INFER, int HD, int HC, int DC>
 __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsigned hcols) {
@@ -409,8 +408,11 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
   }
   __syncthreads();
   const unsigned ticket = sh.ticket;
-  const int band = INFER ? (int)(ticket % (unsigned)a.nseg) : (int)(ticket / (unsigned)a.B);
-  const int b = INFER ? (int)(ticket / (unsigned)a.nseg) : (int)(ticket % (unsigned)a.B);
+  // Pair-major tickets with ring hand-off (a band may wait on the one below),
+  // band-major otherwise (a band waits only on the one above).
+  const bool pair_major = INFER && hcols != 0;
+  const int band = pair_major ? (int)(ticket % (unsigned)a.nseg) : (int)(ticket / (unsigned)a.B);
+  const int b = pair_major ? (int)(ticket / (unsigned)a.nseg) : (int)(ticket % (unsigned)a.B);
   const int64_t N = a.N, D = a.D;
   const int P = fused_pitch(D);
   float* xs = smem;

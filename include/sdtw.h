@@ -30,17 +30,20 @@
  *                      the calls return SDTW_ERR_INVALID_ARG beyond that).
  *   SDTW_MODE_INFERENCE the loss alone (the README's "When to Use Each Mode"
  *                      names inference as a use): distances recomputed as
- *                      in fused mode and no
- *                      DP state kept, so the workspace holds only control
- *                      words and the rows handed between 64-row bands, as
- *                      rings of 512 columns (O(B*N) bytes; whole rows, i.e.
- *                      O(B*N*M/64), when N > 16384).  D <= 256.
- *                      sdtw_backward returns SDTW_ERR_UNSUPPORTED for it, and
- *                      sdtw_forward returns SDTW_ERR_UNSUPPORTED on a GPU
- *                      with fewer CUs than the pair has 64-row bands (the
- *                      ring hand-off needs them all resident).  The loss is
- *                      bitwise the one the other two modes return.
- * Both modes keep the forward DP state (fp64, B x N x M) for the backward.
+ *                      in fused mode and no DP state kept.  The workspace
+ *                      holds control words and the rows handed between
+ *                      64-row bands: whole rows (B*ceil(N/64)*M*8 bytes)
+ *                      while that is at most 16 MiB or the inputs' size,
+ *                      else rings of 512 columns (B*ceil(N/64)*512*8 bytes,
+ *                      O(B*N)); rings are also used whenever all the pairs'
+ *                      bands fit on 256 CUs at once.  Rings need N <= 16384.
+ *                      D <= 256.  sdtw_backward returns SDTW_ERR_UNSUPPORTED
+ *                      for it, and with rings sdtw_forward returns
+ *                      SDTW_ERR_UNSUPPORTED on a GPU with fewer CUs than
+ *                      the pair has bands (they must all be resident).  The
+ *                      loss is bitwise the one the other two modes return.
+ * The two training modes keep the forward DP state (fp64, B x N x M) for the
+ * backward.
  * Distances are accumulated in fp64 and rounded once to fp32 in both modes,
  * so fused and unfused see identical distances, losses and alignment
  * matrices (gradients agree to rounding: they are summed in other orders).

@@ -136,13 +136,21 @@ def test_timing_switch_without_launches():
 
 
 def test_inference_mode_workspace_and_backward():
-    """Inference mode: a workspace without B x N x M arrays (rows handed
-    between bands only), D <= 256, and no backward."""
+    """Inference mode: no B x N x M arrays, only the rows handed between
+    64-row bands (whole, or 512-column rings once whole rows would be large
+    or when every band fits on the GPU at once), D <= 256, and no backward."""
+    def ws(*a):
+        return L.sdtw_workspace_bytes(*a, L.SDTW_MODE_INFERENCE)
     train = L.sdtw_workspace_bytes(32, 4096, 4096, 128, L.SDTW_MODE_UNFUSED)
-    infer = L.sdtw_workspace_bytes(32, 4096, 4096, 128, L.SDTW_MODE_INFERENCE)
-    assert 0 < infer and infer * 1000 < train
-    # ring hand-off: O(B*N) bytes, independent of M
-    assert (L.sdtw_workspace_bytes(4, 1000, 5000, 3, L.SDTW_MODE_INFERENCE)
-            == L.sdtw_workspace_bytes(4, 1000, 9000, 3, L.SDTW_MODE_INFERENCE))
-    assert L.sdtw_workspace_bytes(2, 10, 10, 257, L.SDTW_MODE_INFERENCE) == 0
+    infer = ws(32, 4096, 4096, 128)
+    assert 0 < infer and infer * 100 < train
+    rows = 32 * 64 * 4096 * 8                     # whole rows: 64 MiB < the inputs
+    assert rows <= infer < rows + (1 << 20)
+    # rings (every band fits at once): O(B*N), independent of M
+    assert ws(4, 1000, 5000, 3) == ws(4, 1000, 9000, 3) < 4 * 16 * 512 * 8 + (1 << 16)
+    # rings (whole rows would be 18.9 MB, above 16 MiB and the inputs)
+    assert ws(9, 2048, 8192, 2) == ws(9, 2048, 9000, 2) < 9 * 32 * 512 * 8 + (1 << 16)
+    # whole rows (small, and more bands than CUs)
+    assert ws(40, 500, 600, 3) >= 40 * 8 * 600 * 8
+    assert ws(2, 10, 10, 257) == 0
     assert _bwd(mode=L.SDTW_MODE_INFERENCE, D=3) == L.SDTW_ERR_UNSUPPORTED

@@ -348,11 +348,15 @@ def test_launch_timing_records_each_kernel(S):
     assert all(t > 0 for _, t in recs)
 
 
-@pytest.mark.parametrize("B,N,M,D", [(2, 16, 16, 1), (3, 70, 45, 3), (3, 1100, 700, 5),
-                                     (2, 300, 2000, 4), (1, 64, 5000, 2), (4, 130, 513, 8)])
+@pytest.mark.parametrize("B,N,M,D", [
+    (2, 16, 16, 1), (3, 70, 45, 3),                       # whole rows (M <= 512)
+    (3, 1100, 700, 5), (2, 300, 2000, 4), (1, 64, 5000, 2), (4, 130, 513, 8),  # rings
+    (40, 500, 600, 3),                                    # whole rows, band-major
+    (9, 2048, 8192, 2),                                   # rings, more bands than CUs
+])
 def test_inference_mode_matches_training_loss(S, B, N, M, D):
-    """The inference mode (no state kept; rows handed between bands through
-    512-column rings when M > 512) returns bitwise the training forward's
+    """The inference mode (no state kept; rows handed between bands whole
+    or through 512-column rings) returns bitwise the training forward's
     loss, through the C ABI; without autograd the Python layer uses it."""
     from differentiable_series_alignment_amd import _lib as L
     x, y = pair_batch(B, N, M, D, seed=B + N + M + D)
