@@ -3,7 +3,8 @@
 API of the README "SoftDTW-CUDA (PyTorch + Numba)": ``SoftDTW(gamma=1.0,
 dist="sqeuclidean", fused=False, normalize=False)`` called as
 ``loss_fn(x, y)`` -> (B,) ("Usage", "Fused Mode", "Normalization") and
-``softdtw_barycenter(sequences, gamma, max_iter, lr, fused)`` -> (N, D)
+``softdtw_barycenter(sequences, gamma, max_iter, lr, fused, early_stopping,
+cosine_annealing, grad_clip)`` -> (N, D)
 ("Time Series Barycenters").  PyTorch provides device memory, streams and
 autograd; every Soft-DTW step runs in the library's HIP kernels.
 """
@@ -118,18 +119,38 @@ def _loss_only(x: torch.Tensor, y: torch.Tensor, gamma: float):
     return loss
 
 
+def choose_fused(fused, B: int, N: int, M: int, D: int, device=None) -> bool:
+    """Resolve ``fused``: True/False as given; None or "auto" selects the mode
+    (README "Time Series Barycenters", key options: fused auto-selects
+    between memory and speed).  Reading: the unfused mode is the faster one
+    here, so it is kept unless its workspace would take more than half of
+    the free device memory and fused mode supports D."""
+    if fused is None or (isinstance(fused, str) and fused == "auto"):
+        if L.sdtw_workspace_bytes(B, N, M, D, L.SDTW_MODE_FUSED) == 0:
+            return False
+        need = L.sdtw_workspace_bytes(B, N, M, D, L.SDTW_MODE_UNFUSED)
+        free, _ = torch.cuda.mem_get_info(device)
+        return need == 0 or need > free // 2
+    if isinstance(fused, str):
+        raise ValueError(f"fused must be True, False, None or 'auto', got {fused!r}")
+    return bool(fused)
+
+
 def soft_dtw(x: torch.Tensor, y: torch.Tensor, gamma: float = 1.0,
-             fused: bool = False) -> torch.Tensor:
+             fused=False) -> torch.Tensor:
     """Per-pair Soft-DTW loss (B,) with autograd support.  When no gradient
     can be asked for (autograd off, or neither input requires one) the loss
     comes from the inference mode, which keeps no state; its value is bitwise
-    the one of the other modes."""
+    the one of the other modes.  ``fused``: True, False, or None / "auto"
+    (see choose_fused)."""
     _validate(x, y, gamma)
     if not (torch.is_grad_enabled() and (x.requires_grad or y.requires_grad)):
         loss = _loss_only(x, y, float(gamma))
         if loss is not None:
             return loss
-    mode = L.SDTW_MODE_FUSED if fused else L.SDTW_MODE_UNFUSED
+    B, N, D = x.shape
+    use_fused = choose_fused(fused, B, N, y.shape[1], D, x.device)
+    mode = L.SDTW_MODE_FUSED if use_fused else L.SDTW_MODE_UNFUSED
     return _SoftDTWFunction.apply(x, y, float(gamma), mode)
 
 
@@ -141,7 +162,7 @@ class SoftDTW(torch.nn.Module):
     terms run as one batch of 3B pairs."""
 
     def __init__(self, gamma: float = 1.0, dist: str = "sqeuclidean",
-                 fused: bool = False, normalize: bool = False):
+                 fused=False, normalize: bool = False):
         super().__init__()
         if dist != "sqeuclidean":
             raise ValueError(f"only dist='sqeuclidean' is supported, got {dist!r}")
@@ -150,7 +171,9 @@ class SoftDTW(torch.nn.Module):
             raise ValueError(f"gamma must be finite and > 0, got {gamma}")
         self.gamma = g
         self.dist = dist
-        self.fused = bool(fused)
+        if isinstance(fused, str) and fused != "auto":
+            raise ValueError(f"fused must be True, False, None or 'auto', got {fused!r}")
+        self.fused = fused if (fused is None or isinstance(fused, str)) else bool(fused)
         self.normalize = bool(normalize)
 
     def forward(self, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
@@ -210,26 +233,76 @@ def alignment(x: torch.Tensor, y: torch.Tensor, gamma: float = 1.0,
     return loss, E
 
 
+class EarlyStopping:
+    """Convergence test of the barycenter loop (README "Time Series
+    Barycenters": ``early_stopping=True`` detects convergence; the README's
+    "Benchmarking" section reports it saving a large share of the
+    iterations).  The pages give no rule; reading: after each iteration,
+    an objective below best - tol*|best| becomes the new best, any other
+    counts as a stalled iteration, and the loop stops after ``patience``
+    stalled iterations in a row."""
+
+    def __init__(self, patience: int = 10, tol: float = 1e-4):
+        if int(patience) < 1 or not (float(tol) >= 0.0):
+            raise ValueError("patience must be >= 1 and tol >= 0")
+        self.patience = int(patience)
+        self.tol = float(tol)
+        self.best = math.inf
+        self.stalled = 0
+
+    def step(self, value: float) -> bool:
+        """Record one objective value; True when the loop should stop."""
+        v = float(value)
+        if self.best == math.inf or v < self.best - self.tol * abs(self.best):
+            self.best = v
+            self.stalled = 0
+        else:
+            self.stalled += 1
+        return self.stalled >= self.patience
+
+
 def softdtw_barycenter(sequences: torch.Tensor, gamma: float = 1.0,
-                       max_iter: int = 100, lr: float = 0.1, fused: bool = False,
-                       return_history: bool = False):
+                       max_iter: int = 100, lr: float = 0.1, fused=False,
+                       early_stopping: bool = False, patience: int = 10,
+                       tol: float = 1e-4, cosine_annealing: bool = False,
+                       grad_clip=None, return_history: bool = False):
     """Soft-DTW barycenter of K sequences (K, N, D) by Adam (README "Time
     Series Barycenters"; review page, "Proposed method").  The iterate starts
-    at the pointwise mean and minimises mean_k SoftDTW(z, X_k)."""
+    at the pointwise mean and minimises mean_k SoftDTW(z, X_k).
+
+    Options of the README ("Time Series Barycenters" key options and
+    "Benchmarking"): ``fused`` True/False or None/"auto" (choose_fused);
+    ``early_stopping`` (EarlyStopping(patience, tol)); ``cosine_annealing``
+    (the learning rate follows lr*(1+cos(pi*t/max_iter))/2 over the
+    iterations, torch's CosineAnnealingLR); ``grad_clip`` (the gradient's L2
+    norm is clipped to this value before each step, torch's
+    clip_grad_norm_).  The pages give no values for these; all are off by
+    default so the plain loop is Adam alone."""
     if sequences.dim() != 3:
         raise ValueError("sequences must be (K, N, D)")
+    if grad_clip is not None and not (float(grad_clip) > 0.0):
+        raise ValueError("grad_clip must be > 0 or None")
     X = sequences.detach().contiguous()
+    K, N, D = X.shape
     z = X.mean(dim=0).clone().requires_grad_(True)
     opt = torch.optim.Adam([z], lr=lr)
-    loss_fn = SoftDTW(gamma=gamma, fused=fused)
+    sched = (torch.optim.lr_scheduler.CosineAnnealingLR(opt, T_max=int(max_iter))
+             if cosine_annealing and int(max_iter) > 0 else None)
+    stop = EarlyStopping(patience, tol) if early_stopping else None
+    loss_fn = SoftDTW(gamma=gamma, fused=choose_fused(fused, K, N, N, D, X.device))
     hist = []
     for _ in range(int(max_iter)):
         opt.zero_grad(set_to_none=True)
         loss = loss_fn(z.unsqueeze(0).expand_as(X), X).mean()
         loss.backward()
+        if grad_clip is not None:
+            torch.nn.utils.clip_grad_norm_([z], float(grad_clip))
         opt.step()
-        if return_history:
-            hist.append(loss.detach())
+        if sched is not None:
+            sched.step()
+        hist.append(loss.detach())
+        if stop is not None and stop.step(loss.item()):
+            break
     z = z.detach()
     if return_history:
         return z, torch.stack(hist).cpu() if hist else torch.empty(0)

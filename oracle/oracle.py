@@ -15,13 +15,15 @@ operations:
   (README section "Normalization"; equal shapes only).
 * ``barycenter``: Adam on the mean Soft-DTW between a free sequence and the
   given ones (README "Time Series Barycenters"; review page, section
-  "Proposed method": barycenters by Adam).
+  "Proposed method": barycenters by Adam), with the README's optional
+  cosine annealing, gradient clipping and early stopping ("Benchmarking").
 
 Readings taken where the pages are silent are listed with each function.
 """
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -234,10 +236,53 @@ def barycenter_objective_and_grad(z, X, gamma: float, round_dist_f32: bool = Tru
     return float(loss.mean()), gz.sum(axis=0)
 
 
+def cosine_lr(lr: float, t: int, T: int) -> float:
+    """Learning rate of iteration t (0-based) of T under cosine annealing to
+    zero: lr * (1 + cos(pi t / T)) / 2 (Loshchilov & Hutter's SGDR schedule
+    without restarts).  The README ("Benchmarking") names cosine annealing
+    for the barycenter loop without parameters; reading: over max_iter
+    iterations, down to 0."""
+    return 0.5 * lr * (1.0 + math.cos(math.pi * t / T))
+
+
+def clip_by_norm(g, c: float):
+    """Gradient clipping by global L2 norm: g * min(1, c / (|g| + 1e-6))
+    (the README's "Benchmarking" names gradient clipping without details;
+    reading: norm clipping with the customary 1e-6 guard)."""
+    g = np.asarray(g, dtype=np.float64)
+    n = math.sqrt(float(np.sum(g * g)))
+    return g * min(1.0, c / (n + 1e-6))
+
+
+def stop_index(history, patience: int, tol: float):
+    """First iteration index after which the early-stopping rule fires, or
+    None.  Reading (the README's "Time Series Barycenters" only says early
+    stopping detects convergence): a value below best - tol*|best| is an
+    improvement and resets the count; any other value is a stall; the rule
+    fires at the patience-th stall in a row.  The first value is always an
+    improvement."""
+    best = None
+    stalls = 0
+    for i, f in enumerate(history):
+        if best is None or f < best - tol * abs(best):
+            best = f
+            stalls = 0
+        else:
+            stalls += 1
+            if stalls == patience:
+                return i
+    return None
+
+
 def barycenter(X, gamma: float = 1.0, max_iter: int = 100, lr: float = 0.1,
-               round_dist_f32: bool = True, z0=None):
+               round_dist_f32: bool = True, z0=None, cosine: bool = False,
+               clip=None, early_stopping: bool = False, patience: int = 10,
+               tol: float = 1e-4):
     """Adam on mean_k SoftDTW(z, X_k), z initialised to the pointwise mean
-    (or to ``z0`` when given).
+    (or to ``z0`` when given).  Each iteration evaluates the objective and
+    its gradient at the current iterate, clips the gradient (``clip``),
+    takes an Adam step at the iteration's learning rate (``cosine``), and
+    then applies the early-stopping rule to the objectives seen so far.
 
     Reading: the iterate is kept in fp32 between steps (the sequences are
     fp32 and the objective is evaluated on fp32 inputs); the Adam update
@@ -247,10 +292,14 @@ def barycenter(X, gamma: float = 1.0, max_iter: int = 100, lr: float = 0.1,
          else np.asarray(z0, dtype=np.float64).copy())
     st = adam_init(z.shape)
     hist = []
-    for _ in range(max_iter):
+    for t in range(max_iter):
         zf = z.astype(np.float32)
         f, g = barycenter_objective_and_grad(zf, X, gamma, round_dist_f32)
         hist.append(f)
+        if clip is not None:
+            g = clip_by_norm(g, clip)
         z = zf.astype(np.float64)
-        adam_step(z, g, st, lr)
+        adam_step(z, g, st, cosine_lr(lr, t, max_iter) if cosine else lr)
+        if early_stopping and stop_index(hist, patience, tol) is not None:
+            break
     return z.astype(np.float32), hist

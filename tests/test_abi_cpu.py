@@ -126,6 +126,20 @@ def test_python_layer_validation_on_cpu():
         soft_dtw(x[0], y[0])                            # not 3-D
 
 
+def test_fused_choice_and_early_stopping_validation():
+    from differentiable_series_alignment_amd import EarlyStopping, SoftDTW, choose_fused
+    assert choose_fused(True, 2, 4, 4, 1) is True
+    assert choose_fused(False, 2, 4, 4, 1) is False
+    with pytest.raises(ValueError, match="fused"):
+        choose_fused("yes", 2, 4, 4, 1)
+    with pytest.raises(ValueError, match="fused"):
+        SoftDTW(fused="maybe")
+    with pytest.raises(ValueError):
+        EarlyStopping(patience=0)
+    es = EarlyStopping(patience=2, tol=0.0)
+    assert [es.step(v) for v in (3.0, 2.0, 2.0, 2.5)] == [False, False, False, True]
+
+
 def test_timing_switch_without_launches():
     """Launch timing can be switched and collected with nothing recorded (no
     HIP call is made then)."""

@@ -208,6 +208,41 @@ def test_barycenter_iterates(O, S):
     assert hist[-1] < hist[0]
 
 
+def test_barycenter_options_against_oracle(O, S):
+    """Cosine annealing, gradient clipping and early stopping (README "Time
+    Series Barycenters" key options, "Benchmarking"), on the block waves.
+    The GPU loop and the oracle's fp64 loop take the same options; their
+    objective histories agree to 1e-3 relative over the common length (the
+    trajectories themselves are unpinned, as for plain Adam), and the GPU loop
+    stops exactly where the oracle's rule fires on the GPU's own history."""
+    X = block_waves(10, 100, 3, seed=0)
+    z, hist = S.softdtw_barycenter(X.to(DEV), 1.0, 100, 0.1, cosine_annealing=True,
+                                   grad_clip=1.0, early_stopping=True, patience=10,
+                                   tol=1e-4, return_history=True)
+    hist = hist.double().numpy()
+    _, hist0 = O.barycenter(X.numpy(), 1.0, 100, 0.1, cosine=True, clip=1.0,
+                            early_stopping=True, patience=10, tol=1e-4)
+    k = O.stop_index(list(hist), 10, 1e-4)
+    assert k is not None and len(hist) == k + 1 < 100
+    n = min(len(hist), len(hist0))
+    np.testing.assert_allclose(hist[:n], np.array(hist0[:n]), rtol=1e-3)
+    assert torch.isfinite(z).all() and hist[-1] < hist[0]
+
+
+def test_fused_auto_select(S):
+    """fused=None / "auto" keeps the faster unfused mode while its workspace
+    fits in half the free memory; D beyond fused mode's limit never selects
+    it; a problem whose unfused workspace exceeds the free memory does."""
+    assert S.choose_fused(None, 2, 50, 40, 3, DEV) is False
+    assert S.choose_fused("auto", 2, 10, 10, 300, DEV) is False
+    assert S.choose_fused(None, 32, 16384, 16384, 128, DEV) is True
+    x, y = pair_batch(2, 50, 40, 3, seed=4)
+    xd = x.to(DEV).requires_grad_(True)
+    la = S.SoftDTW(gamma=0.5, fused="auto")(xd, y.to(DEV))
+    lu = S.SoftDTW(gamma=0.5, fused=False)(xd, y.to(DEV))
+    torch.testing.assert_close(la, lu, rtol=0, atol=0)
+
+
 def test_barycenter_api(S):
     X = block_waves(10, 100, 3, seed=1).to(DEV)
     z, hist = S.softdtw_barycenter(X, gamma=1.0, max_iter=30, lr=0.1, return_history=True)

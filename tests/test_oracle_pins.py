@@ -306,6 +306,78 @@ def test_barycenter_decreases_objective(O):
     assert hist[-1] < hist[0]
 
 
+def test_cosine_lr_closed_values_and_torch_schedule(O):
+    T, lr = 100, 0.1
+    assert O.cosine_lr(lr, 0, T) == lr
+    assert abs(O.cosine_lr(lr, T // 2, T) - lr / 2) < 1e-16
+    assert abs(O.cosine_lr(lr, T, T)) < 1e-17
+    for t in range(T + 1):                       # symmetric about T/2
+        assert abs(O.cosine_lr(lr, t, T) + O.cosine_lr(lr, T - t, T) - lr) < 1e-15
+    p = torch.zeros(1, requires_grad=True)
+    opt = torch.optim.SGD([p], lr=lr)
+    sched = torch.optim.lr_scheduler.CosineAnnealingLR(opt, T_max=T)
+    for t in range(T):
+        assert abs(opt.param_groups[0]["lr"] - O.cosine_lr(lr, t, T)) < 1e-12, t
+        opt.step()
+        sched.step()
+
+
+def test_clip_by_norm(O):
+    rng = np.random.default_rng(5)
+    for scale in (1e-3, 0.5, 3.0, 1e4):
+        g = rng.standard_normal((100, 3)) * scale
+        c = 1.0
+        out = O.clip_by_norm(g, c)
+        n, n2 = np.linalg.norm(g), np.linalg.norm(out)
+        if n <= c:
+            np.testing.assert_array_equal(out, g)           # untouched below the limit
+        else:
+            assert abs(n2 - c * n / (n + 1e-6)) < 1e-12 * c
+            np.testing.assert_allclose(out / n2, g / n, rtol=1e-12)  # same direction
+        t = torch.tensor(g.copy(), requires_grad=True)
+        t.grad = torch.tensor(g.copy())
+        torch.nn.utils.clip_grad_norm_([t], c)
+        np.testing.assert_allclose(out, t.grad.numpy(), rtol=1e-12, atol=1e-300)
+
+
+def test_stop_index_by_hand(O):
+    # improvements of 20 % then stalls below the 1e-3 relative threshold
+    h = [5.0, 4.0, 3.9999, 3.99995, 3.0, 3.0, 3.0, 3.0]
+    assert O.stop_index(h, 2, 1e-3) == 3
+    assert O.stop_index(h, 3, 1e-3) == 7          # reset by 3.0 at index 4
+    assert O.stop_index([1.0, 1.0, 1.0], 2, 0.0) == 2
+    assert O.stop_index([1.0, 1.0, 2.0], 2, 0.0) == 2  # a rise is a stall too
+    assert O.stop_index([2.0 ** -k for k in range(50)], 1, 1e-3) is None
+
+
+def test_barycenter_options_in_oracle(O):
+    X = block_waves(4, 30, 2, seed=0).numpy()
+    z1, h1 = O.barycenter(X, 1.0, 12, 0.1)
+    z2, h2 = O.barycenter(X, 1.0, 12, 0.1, clip=1e30)       # clipping inactive
+    np.testing.assert_array_equal(z1, z2)
+    assert h1 == h2
+    _, h3 = O.barycenter(X, 1.0, 12, 0.1, cosine=True)
+    assert h3[:2] == h1[:2] and h3[2] != h1[2]               # first step at full lr
+    _, h4 = O.barycenter(X, 1.0, 200, 0.1, early_stopping=True, patience=3, tol=1e-2)
+    k = O.stop_index(h4, 3, 1e-2)
+    assert k is not None and len(h4) == k + 1
+
+
+def test_early_stopping_host_rule_matches_oracle(O):
+    """The Python layer's EarlyStopping (host logic) against the oracle's
+    rule on random histories with plateaus."""
+    from differentiable_series_alignment_amd import EarlyStopping
+    rng = np.random.default_rng(9)
+    for trial in range(200):
+        steps = rng.choice([0.0, -1e-5, -1e-2, 1e-3], size=60, p=[0.3, 0.3, 0.3, 0.1])
+        h = list(10.0 + np.cumsum(steps * 10.0))
+        patience = int(rng.integers(1, 8))
+        tol = float(rng.choice([0.0, 1e-4, 1e-3]))
+        es = EarlyStopping(patience, tol)
+        fired = next((i for i, f in enumerate(h) if es.step(f)), None)
+        assert fired == O.stop_index(h, patience, tol), trial
+
+
 def test_block_waves_recipe():
     X = block_waves(10, 100, 3, seed=0)
     assert X.shape == (10, 100, 3) and X.dtype == torch.float32
