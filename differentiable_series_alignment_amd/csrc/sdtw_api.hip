@@ -202,10 +202,11 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
   DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma, false);
   a.loss = loss;
   const bool fused = mode == SDTW_MODE_FUSED;
-  // A fresh workspace holds garbage: clear both sweeps' control words once
-  // per forward (later launches find them cleared by the kernels).
-  hipError_t e = sdtw::launch_zero_u32(reinterpret_cast<unsigned*>(ws + L.ctrl),
-                                       (int64_t)L.ctrl_words, s);
+  unsigned* ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl);
+  // A fresh workspace holds garbage: the control words are cleared once per
+  // forward (later launches find them cleared by the kernels), by the
+  // distance kernel where there is one.
+  hipError_t e = hipSuccess;
   if (mode == SDTW_MODE_INFERENCE) {
     if (L.hcols) {
       // Ring hand-off needs every band of a pair resident at once (one
@@ -216,13 +217,15 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
         return SDTW_ERR_HIP;
       if ((int64_t)cus < L.nseg) return SDTW_ERR_UNSUPPORTED;
     }
+    e = sdtw::launch_zero_u32(ctrl, (int64_t)L.ctrl_words, s);
     if (e == hipSuccess) e = sdtw::launch_infer(a, L.hcols, s);
   } else if (fused) {
+    e = sdtw::launch_zero_u32(ctrl, (int64_t)L.ctrl_words, s);
     if (e == hipSuccess) e = sdtw::launch_dp_fused(a, false, s);
   } else {
     // Both sweeps at once: the loss comes from the forward one, and the
     // reverse one leaves what the backward needs besides the forward state.
-    if (e == hipSuccess) e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, s);
+    e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, ctrl, (int64_t)L.ctrl_words, s);
     if (e == hipSuccess) e = sdtw::launch_dp_both(a, s);
   }
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;

@@ -34,8 +34,16 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
                                               const float* __restrict__ y,
                                               float* __restrict__ dist,
                                               int64_t N, int64_t M, int64_t D,
-                                              int64_t S, int nbands) {
+                                              int64_t S, int nbands,
+                                              unsigned* __restrict__ zero, int64_t nzero) {
   __shared__ float smem[kDLds];
+  // Words the next kernels of the step expect to find cleared (their
+  // control words; a fresh workspace holds garbage), spread over the grid.
+  {
+    const int64_t wg = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
+    for (int64_t k = wg * 256 + threadIdx.x; k < nzero; k += stride) zero[k] = 0u;
+  }
   float* const xs = smem;                 // [kDT][kDPK] x rows of the block
   float* const ys = smem + kDT * kDPK;    // [kDT][kDPK] y rows of the block
   float* const tile = smem;               // [kDT][kDTP] finished block (after the slabs)
@@ -168,19 +176,19 @@ hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
   {
     TimedLaunch timed_("dist", stream);
     hipLaunchKernelGGL(k_dist<false>, grid, dim3(256), 0, stream, x, y, dist, N, M, D,
-                       (int64_t)0, 0);
+                       (int64_t)0, 0, (unsigned*)nullptr, (int64_t)0);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t B,
-                            int64_t N, int64_t M, int64_t D, int64_t S,
-                            hipStream_t stream) {
+                            int64_t N, int64_t M, int64_t D, int64_t S, unsigned* zero,
+                            int64_t nzero, hipStream_t stream) {
   dim3 grid((unsigned)((M + kDT - 1) / kDT), (unsigned)((N + kDT - 1) / kDT), (unsigned)B);
   {
     TimedLaunch timed_("dist_skew", stream);
     hipLaunchKernelGGL(k_dist<true>, grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S,
-                       (int)((N + 63) / 64));
+                       (int)((N + 63) / 64), zero, nzero);
   }
   return hipGetLastError();
 }

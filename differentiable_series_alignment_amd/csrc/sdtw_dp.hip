@@ -93,9 +93,17 @@ __device__ __forceinline__ void load_chunk(const float* dbase, int64_t off, floa
 }
 
 // One band of one pair, swept column chunk by column chunk.  The band's top
-// row comes from LDS ring `w` (unless it is the first band of the pair); its
-// bottom row goes to LDS ring `w + 1` when a band or the segment's I/O wave
-// reads it.
+// row comes from LDS ring `w`: the previous band's bottom row, the row the
+// segment's I/O wave copies in, or (first band of a pair) a ring the
+// workgroup filled with kBig and marked complete.  Its bottom row goes to
+// LDS ring `w + 1` when a band or the segment's I/O wave reads it.
+//
+// The next chunk's top entries are read at the end of each chunk, after the
+// ring's written count; if that count already covers them (the usual case:
+// a band runs a little slower than the band above it), the chunk starts
+// without touching LDS, otherwise it polls and reads them again.  LDS
+// operations of one wave complete in issue order, so entries read after a
+// count that covers them are the published ones.
 template <bool REV>
 __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int w, int nb_seg,
                                            double (*ring)[kRingC + kCH], unsigned* wr,
@@ -106,7 +114,6 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
   const int64_t r0 = (int64_t)band * 64;
   const int64_t i = r0 + lane;                         // sweep-space row
   const int qcount = (int)(sweep_steps(M) / kCH);
-  const bool top_ring = band > 0;
   const bool out_used = (w + 1 < nb_seg) || (seg + 1 < a.nseg);
   const unsigned Mu = (unsigned)M;
 
@@ -123,12 +130,18 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
 
   double cur = kBig;
   double up = (band == 0 && lane == 0) ? 0.0 : kBig;
-  unsigned seen_wr = 0, seen_rd = 0;
+  unsigned seen_rd = 0;
 
   // Chunk inputs alternate between two register sets: chunk q computes from
   // one while the requests for chunk q+1 fill the other.
   float dnA[kCH], dnB[kCH];
   load_chunk<REV>(dbase, 0, dnA);
+  // Top entries of the first chunk and the count they were read under.
+  double top[kCH];
+  unsigned seen_wr = __hip_atomic_load(&wr[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+  for (int u = 0; u < kCH; ++u) top[u] = ring[w][u];
   __builtin_amdgcn_s_waitcnt(0);
 
   auto chunk = [&](int q, const float (&dn)[kCH], float (&dn2)[kCH]) {
@@ -138,15 +151,11 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
     // operations in flight completes the loads and leaves the stores going.
     __builtin_amdgcn_s_waitcnt(kWaitVm16);
     // Top row, columns t0 .. t0+15 (entries past M are never used).
-    double top[kCH];
-    if (top_ring) {
-      const unsigned need = (unsigned)t0 + kCH < Mu ? (unsigned)t0 + kCH : Mu;
-      if (seen_wr < need) seen_wr = lds_wait_ge(&wr[w], need);
+    const unsigned need = (unsigned)t0 + kCH < Mu ? (unsigned)t0 + kCH : Mu;
+    if (seen_wr < need) {
+      seen_wr = lds_wait_ge(&wr[w], need);
 #pragma unroll
       for (int u = 0; u < kCH; ++u) top[u] = ring[w][(t0 + u) & (kRingC - 1)];
-    } else {
-#pragma unroll
-      for (int u = 0; u < kCH; ++u) top[u] = kBig;
     }
     // Unconditional (the last chunk re-reads its own cells), so the
     // compiler's wait bookkeeping stays exact across the loop.
@@ -167,15 +176,14 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
         a.loss[b] = (float)(v * a.g_ln2);
       }
     }
-    // The top entries of this chunk have long been read: release them.
-    if (top_ring && lane == 0)
-      lds_publish(&rd[w], (unsigned)t0 + kCH < Mu ? (unsigned)t0 + kCH : Mu);
+    // The top entries of this chunk have been read: release them.
+    if (lane == 0) lds_publish(&rd[w], need);
     // Lane 63's cells (row r0+63, columns t0+u-63) go to the row below.
     if (out_used) {
       const int cmax = t0 + kCH - 1 - 63;          // newest column of this chunk
       if (cmax >= kRingC) {
-        const unsigned need = (unsigned)(cmax - kRingC + 1);
-        if (seen_rd < need) seen_rd = lds_wait_ge(&rd[w + 1], need);
+        const unsigned need_rd = (unsigned)(cmax - kRingC + 1);
+        if (seen_rd < need_rd) seen_rd = lds_wait_ge(&rd[w + 1], need_rd);
       }
       if (lane == 63) {
         // Columns t0-63 .. t0-48 occupy slots s .. s+15 with s = 1 (mod 16),
@@ -192,6 +200,12 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
         lds_publish(&wr[w + 1], done <= 0 ? 0u : ((unsigned)done < Mu ? (unsigned)done : Mu));
       }
     }
+    // Next chunk's top entries, read after the count (see above).  Their
+    // slots are not released yet, so the band above cannot overwrite them.
+    seen_wr = __hip_atomic_load(&wr[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int u = 0; u < kCH; ++u) top[u] = ring[w][(t0 + kCH + u) & (kRingC - 1)];
   };
 
   for (int q = 0; q < qcount; q += 2) {
@@ -215,16 +229,21 @@ __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a)
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   if (threadIdx.x == 0) s_ticket = atomicAdd(&a.ctrl[0], 1u);
-  if (threadIdx.x < W + 1) {
-    wr[threadIdx.x] = 0u;
-    rd[threadIdx.x] = 0u;
-  }
   __syncthreads();
   const unsigned ticket = s_ticket;
   const int rev = (int)(ticket & 1u);
   const unsigned rest = ticket >> 1;
   const int seg = (int)(rest / (unsigned)a.B);
   const int b = (int)(rest % (unsigned)a.B);
+  // The first band of a pair reads its top row (the +inf boundary) from
+  // ring 0, filled with kBig and marked complete.
+  if (threadIdx.x < W + 1) {
+    wr[threadIdx.x] = (seg == 0 && threadIdx.x == 0) ? (unsigned)a.M : 0u;
+    rd[threadIdx.x] = 0u;
+  }
+  if (seg == 0)
+    for (int k = threadIdx.x; k < kRingC + kCH; k += blockDim.x) ring[0][k] = kBig;
+  __syncthreads();
   const int nb_seg = min(W, a.nbands - seg * W);
   const int64_t per_sweep = (int64_t)a.B * a.nseg;
 

@@ -21,6 +21,8 @@
 //  - one wave hands the band's bottom row to the next band's workgroup and
 //    receives the row above from the previous one (segment_io_wave).
 // All coordination inside a workgroup goes through LDS counters.
+#include <type_traits>
+
 #include "sdtw_dp_common.h"
 
 namespace sdtw {
@@ -30,12 +32,20 @@ constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
 constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
 constexpr int kRevHelpD = 2; // distance helpers, reverse sweep
 constexpr int kRevHelpC = 2; // chain-rule helpers, reverse sweep
+constexpr int kYB = 16;      // feature steps (of 4) per batch of y loads
 
 __host__ __device__ inline int fused_pitch(int64_t D) { return (int)(((D + 3) / 4) * 4 + 4); }
 
-// Dynamic LDS of one workgroup: the band's x rows and the distance/E ring.
-size_t fused_lds_bytes(int64_t D) {
-  return (size_t)64 * fused_pitch(D) * 4 + (size_t)kFR * kFPitch * 4;
+// y rows staged for a chain-rule helper: two blocks of 16 rows, DC columns of
+// D each, rows padded by 2 floats (LDS banks).
+__host__ __device__ constexpr int chain_y_floats(int DC) { return 2 * 16 * (DC + 2); }
+
+// Dynamic LDS of one workgroup: the band's x rows and the distance/E ring,
+// plus (reverse sweep, DC columns of D per chain-rule helper) the helpers'
+// staged y rows.
+size_t fused_lds_bytes(int64_t D, int DC = 0) {
+  return (size_t)64 * fused_pitch(D) * 4 + (size_t)kFR * kFPitch * 4 +
+         (DC ? (size_t)kRevHelpC * chain_y_floats(DC) * 4 : 0);
 }
 
 // One band per workgroup; 0 when D is beyond what the kernels hold on chip.
@@ -222,17 +232,35 @@ __device__ __forceinline__ void fused_dist_helper(const DPArgs& a, FusedShared& 
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) acc[ti] = (v4d){0.0, 0.0, 0.0, 0.0};
     double ny = 0.0;
-    for (int s = 0; s < steps4; ++s) {
-      const int d = 4 * s + kk;
-      const float yv = yr[d < D ? d : D - 1];
-      const double bv = (d < D && cok) ? (double)yv : 0.0;
-      ny = fma(bv, bv, ny);
+    // y values in batches of kYB feature steps, all requested before the
+    // batch's matrix instructions, so a batch costs one memory round trip
+    // instead of one per step.  Full batches run unguarded; the last, partial
+    // one skips the steps past D.
+    auto batch = [&](int s0, auto guard) {
+      float yv[kYB];
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        const double av = (double)xs[(16 * ti + r16) * P + 4 * s + kk];
-        acc[ti] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[ti], 0, 0, 0);
+      for (int j = 0; j < kYB; ++j) {
+        const int d = 4 * (s0 + j) + kk;
+        yv[j] = yr[d < D ? d : D - 1];
       }
-    }
+#pragma unroll
+      for (int j = 0; j < kYB; ++j) {
+        const int s = s0 + j;
+        if (!decltype(guard)::value || s < steps4) {
+          const int d = 4 * s + kk;
+          const double bv = (d < D && cok) ? (double)yv[j] : 0.0;
+          ny = fma(bv, bv, ny);
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) {
+            const double av = (double)xs[(16 * ti + r16) * P + 4 * s + kk];
+            acc[ti] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[ti], 0, 0, 0);
+          }
+        }
+      }
+    };
+    int s0 = 0;
+    for (; s0 + kYB <= steps4; s0 += kYB) batch(s0, std::false_type{});
+    if (s0 < steps4) batch(s0, std::true_type{});
     ny += __shfl_xor(ny, 16, 64);
     ny += __shfl_xor(ny, 32, 64);
     float* col = dr + (int)(sc & (kFR - 1)) * kFPitch;
@@ -253,13 +281,18 @@ __device__ __forceinline__ void fused_dist_helper(const DPArgs& a, FusedShared& 
 }
 
 // ---------------------------------------------------------------------------
-// Chain-rule helper c (reverse sweep): columns [c*DC, (c+1)*DC) of D.
+// Chain-rule helper c (reverse sweep): columns [c*DC, (c+1)*DC) of D.  The y
+// rows of block p+1 are requested while block p is processed and staged in
+// the helper's LDS area `ys` (two blocks), so a block never waits on memory.
 // ---------------------------------------------------------------------------
 template <int DC>
 __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared& sh,
-                                                   const float* xs, const float* dr, int b,
-                                                   int band, int c, int lane) {
+                                                   const float* xs, const float* dr,
+                                                   float* ys, int b, int band, int c,
+                                                   int lane) {
   constexpr int NT = DC / 32;
+  constexpr int YP = DC + 2;            // staged row pitch
+  constexpr int YL = 16 * DC / 64;      // staged values per lane per block
   const int64_t N = a.N, M = a.M, D = a.D;
   const int P = fused_pitch(D);
   const int qcount = (int)(sweep_steps(M) / kCH);
@@ -284,22 +317,49 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
 #pragma unroll
       for (int e = 0; e < 16; ++e) gxa[rt][t][e] = 0.f;
 
+  // Block p's y rows (sweep columns 16p .. 16p+15, columns dbeg .. dbeg+DC-1
+  // of D; rows past M and columns past D are clamped copies, multiplied by
+  // zero alignment entries or never written out).
+  float yreg[YL];
+  auto load_y = [&](int p) {
+#pragma unroll
+    for (int k = 0; k < YL; ++k) {
+      const int idx = lane + 64 * k;
+      const int64_t sc = (int64_t)p * kCH + idx / DC;
+      const int64_t oc = sc < M ? M - 1 - sc : 0;
+      const int64_t dc = dbeg + idx % DC;
+      yreg[k] = yb[oc * D + (dc < D ? dc : D - 1)];
+    }
+  };
+  auto stage_y = [&](int p) {
+    float* yd = ys + (p & 1) * 16 * YP;
+#pragma unroll
+    for (int k = 0; k < YL; ++k) {
+      const int idx = lane + 64 * k;
+      yd[(idx / DC) * YP + idx % DC] = yreg[k];
+    }
+  };
+
   const int nreal = (int)((M + kCH - 1) / kCH);
+  load_y(0);
+  stage_y(0);
   unsigned seen_dp = 0;
   for (int p = 0; p < nreal; ++p) {
+    const bool more = p + 1 < nreal;
+    if (more) load_y(p + 1);
     // Block p is complete once the band wave has finished chunk p+4 (the
     // last chunk completes every remaining block).
     const unsigned need = umin_u((unsigned)p + 5, (unsigned)qcount);
     if (seen_dp < need) seen_dp = lds_wait_ge(&sh.dp_done, need);
     const int64_t c0 = (int64_t)p * kCH;
+    const float* yc = ys + (p & 1) * 16 * YP;
     if (want_gx) {
       // dx += E[64 x 16] . Y[16 x DC] on v_mfma_f32_32x32x2_f32.
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const int64_t sc = c0 + 2 * s + h;
-        const bool cok = sc < M;
-        const int64_t oc = cok ? M - 1 - sc : 0;
-        const float* ecol = dr + (int)(sc & (kFR - 1)) * kFPitch;
+        const int cl = 2 * s + h;                 // column of the block
+        const bool cok = c0 + cl < M;
+        const float* ecol = dr + (int)((c0 + cl) & (kFR - 1)) * kFPitch;
         float av[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -309,24 +369,22 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const int64_t dc = dbeg + 32 * t + r32;
-          const float bv = yb[oc * D + (dc < D ? dc : D - 1)];
+          const float bv = yc[cl * YP + 32 * t + r32];
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt)
             gxa[rt][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[rt], bv, gxa[rt][t], 0, 0, 0);
         }
       }
     }
+    v4f acc[2 * NT];
+    float cs = 0.f;
     if (want_gy) {
       // dy[16 columns] += 2g (colsum(E) y - E^T . X[64 x DC]) on
       // v_mfma_f32_16x16x4_f32, added atomically (other bands add too).
-      v4f acc[2 * NT];
 #pragma unroll
       for (int t = 0; t < 2 * NT; ++t) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
-      const int64_t sc = c0 + r16;
-      const bool cok = sc < M;
-      const float* ecol = dr + (int)(sc & (kFR - 1)) * kFPitch;
-      float cs = 0.f;
+      const bool cok = c0 + r16 < M;
+      const float* ecol = dr + (int)((c0 + r16) & (kFR - 1)) * kFPitch;
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const int row = 4 * s + kk;
@@ -341,6 +399,11 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
       }
       cs += __shfl_xor(cs, 16, 64);
       cs += __shfl_xor(cs, 32, 64);
+    }
+    // Block p+1's y rows go into the other staging slot (last read in block
+    // p-1) before this block's atomics are issued.
+    if (more) stage_y(p + 1);
+    if (want_gy) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ci = 4 * kk + e;  // fp32 16x16x4 accumulator row
@@ -349,11 +412,11 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
         if (scol < M) {
           const int64_t oc = M - 1 - scol;
           float* gyr = a.gy + ((int64_t)b * M + oc) * D;
-          const float* yr = yb + oc * D;
 #pragma unroll
           for (int t = 0; t < 2 * NT; ++t) {
             const int64_t dc = dbeg + 16 * t + r16;
-            if (dc < dend) atomicAdd(gyr + dc, g2 * (csum * yr[dc] - acc[t][e]));
+            if (dc < dend)
+              atomicAdd(gyr + dc, g2 * (csum * yc[ci * YP + 16 * t + r16] - acc[t][e]));
           }
         }
       }
@@ -435,7 +498,11 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
   } else if (w <= HD) {
     fused_dist_helper<REV, HC>(a, sh, xs, dr, b, w - 1, HD, lane);
   } else if (w < kIO) {
-    if (REV) fused_chain_helper<DC>(a, sh, xs, dr, b, band, w - 1 - HD, lane);
+    if (REV) {
+      const int c = w - 1 - HD;
+      float* ys = dr + kFR * kFPitch + c * chain_y_floats(DC);
+      fused_chain_helper<DC>(a, sh, xs, dr, ys, b, band, c, lane);
+    }
   } else {
     const int64_t pb = (int64_t)b * a.nseg;
     const int64_t sin = pb + (band > 0 ? band - 1 : 0), sout = pb + band;
@@ -456,7 +523,7 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
 template <bool REV, bool INFER, int HD, int HC, int DC>
 static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcols = 0) {
   auto kern = k_dp_fused<REV, INFER, HD, HC, DC>;
-  const size_t lds = fused_lds_bytes(a.D);
+  const size_t lds = fused_lds_bytes(a.D, REV ? DC : 0);
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -82,9 +82,11 @@ class TimedLaunch {
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
                        int64_t N, int64_t M, int64_t D, hipStream_t stream);
+// Band-step distances; also clears `nzero` words at `zero` (the step's
+// control words) for the kernels that follow on the stream.
 hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t B,
-                            int64_t N, int64_t M, int64_t D, int64_t S,
-                            hipStream_t stream);
+                            int64_t N, int64_t M, int64_t D, int64_t S, unsigned* zero,
+                            int64_t nzero, hipStream_t stream);
 hipError_t launch_unskew(const float* esk, float* out, int64_t B, int64_t N,
                          int64_t M, int64_t S, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
