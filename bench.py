@@ -203,7 +203,7 @@ def measure_inference(L, torch, x, y, gamma, steps, warmup):
             "workspace_mib": nbytes / 2**20}
 
 
-def peak_mib(torch, SoftDTW, x, y, gamma, fused):
+def peak_mib(torch, SoftDTW, x, y, gamma, fused, checkpoint=False):
     """Peak device memory of one autograd fwd+bwd (SoftDTW(...)(x, y).mean()
     .backward()) above what was allocated before, and the part of it taken
     by x, y and their gradients."""
@@ -214,7 +214,7 @@ def peak_mib(torch, SoftDTW, x, y, gamma, fused):
     torch.cuda.reset_peak_memory_stats(dev)
     xg = x.clone().requires_grad_(True)
     yg = y.clone().requires_grad_(True)
-    SoftDTW(gamma=gamma, fused=fused)(xg, yg).mean().backward()
+    SoftDTW(gamma=gamma, fused=fused, checkpoint=checkpoint)(xg, yg).mean().backward()
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated(dev) - base
     io = 2 * (xg.numel() + yg.numel()) * 4
@@ -300,9 +300,11 @@ def main():
             xc2, yc2 = pair_batch(b_, n_, m_, d_, seed=0)
             x2, y2 = xc2.to(dev), yc2.to(dev)
             entry = {"workload": f"B={b_} N={n_} M={m_} D={d_} gamma={g_}"}
-            for mode, name in ((L.SDTW_MODE_UNFUSED, "unfused"), (L.SDTW_MODE_FUSED, "fused")):
+            for mode, name in ((L.SDTW_MODE_UNFUSED, "unfused"), (L.SDTW_MODE_FUSED, "fused"),
+                               (L.SDTW_MODE_CHECKPOINT, "checkpoint")):
                 t, _, _, _ = measure(L, torch, x2, y2, g_, mode, 5, 2)
-                pk, pko = peak_mib(torch, SoftDTW, x2, y2, g_, mode == L.SDTW_MODE_FUSED)
+                pk, pko = peak_mib(torch, SoftDTW, x2, y2, g_, mode == L.SDTW_MODE_FUSED,
+                                   mode == L.SDTW_MODE_CHECKPOINT)
                 entry[name] = {"ms_per_step": t, "cells_per_s": b_ * n_ * m_ / (t * 1e-3),
                                "peak_mib": pk, "peak_mib_over_io": pko}
             entry["inference"] = measure_inference(L, torch, x2, y2, g_, 5, 2)

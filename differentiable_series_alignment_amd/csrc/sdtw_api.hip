@@ -27,8 +27,23 @@ struct Layout {
   size_t cnt_rows = 0, cnt_cols = 0;  // word offsets of the chain split counters
   size_t dist = 0;                  // fp32 band-step distances, then E (unfused)
   unsigned hcols = 0;               // inference: hand-off ring columns (0: whole rows)
+  // Checkpointed training: groups of G bands, ng groups, ng-1 checkpoint
+  // rows; control words of the group launches (2 + B*G, then the word
+  // holding M and a sink word), checkpoint rows [B][ng-1][M + 2*kCkPad],
+  // two reverse hand-off rows [2][B][M], and the X of one group (band-step).
+  int64_t G = 0, ng = 0;
+  size_t gctrl = 0, ckpt = 0, rh = 0;
   size_t total = 0;
 };
+
+// Bands per checkpoint group: about the square root of the band count, so
+// the checkpoint rows (one per group) and the recomputed group of bands
+// both stay near sqrt(N/64) rows of M states per pair.
+int64_t ckpt_group(int64_t nbands) {
+  int64_t g = 1;
+  while (g * g < nbands) ++g;
+  return g;
+}
 
 // Inference mode hands each band's bottom row to the next band either whole
 // (B*nbands*M*8 bytes; tickets run band-major, the fastest order when the
@@ -70,9 +85,40 @@ bool sizes_ok(int64_t B, int64_t N, int64_t M, int64_t D) {
 
 bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L) {
   if (!sizes_ok(B, N, M, D) ||
-      (mode != SDTW_MODE_UNFUSED && mode != SDTW_MODE_FUSED && mode != SDTW_MODE_INFERENCE))
+      (mode != SDTW_MODE_UNFUSED && mode != SDTW_MODE_FUSED && mode != SDTW_MODE_INFERENCE &&
+       mode != SDTW_MODE_CHECKPOINT))
     return false;
   L->nbands = (N + 63) / 64;
+  if (mode == SDTW_MODE_CHECKPOINT) {
+    // The loss-only forward (plus checkpoint rows), then per group a forward
+    // over the group's rows that keeps X and a reverse over them.
+    if (sdtw::fused_bands_per_wg(D) == 0) return false;
+    L->nseg = L->nbands;
+    L->hcols = infer_ring_cols(B, L->nbands, M, N, D);
+    L->S = sdtw::skew_steps(M);
+    L->G = ckpt_group(L->nbands);
+    L->ng = (L->nbands + L->G - 1) / L->G;
+    const size_t row = L->hcols ? L->hcols : (size_t)M;
+    const size_t hrow = (size_t)L->nbands * row > (size_t)L->G * (size_t)M
+                            ? (size_t)L->nbands * row : (size_t)L->G * (size_t)M;
+    size_t off = 0;
+    L->ctrl = off;
+    L->gctrl = 2 + 2 * (size_t)B * (size_t)L->nseg;
+    L->ctrl_words = L->gctrl + 2 + (size_t)B * (size_t)L->G + 2;
+    off += align_up(L->ctrl_words * 4);
+    L->loss64 = off;
+    off += align_up((size_t)B * 8);
+    L->H = off;
+    off += align_up((size_t)B * hrow * 8);
+    L->ckpt = off;
+    off += align_up((size_t)B * (size_t)(L->ng - 1) * ((size_t)M + 2 * sdtw::kCkPad) * 8);
+    L->rh = off;
+    off += align_up(2 * (size_t)B * (size_t)M * 8);
+    L->R = off;
+    off += align_up((size_t)B * (size_t)L->G * (size_t)L->S * 64 * 8);
+    L->total = off;
+    return true;
+  }
   if (mode == SDTW_MODE_INFERENCE) {
     // Loss only: control words, the final states and the hand-off rows.
     if (sdtw::fused_bands_per_wg(D) == 0) return false;
@@ -153,6 +199,58 @@ DPArgs dp_args(const Layout& L, char* ws, const float* x, const float* y,
   return a;
 }
 
+// Checkpointed backward: the reverse sweep runs group by group from the
+// bottom of the grid (reverse bands hG .. hG+G-1), each group after a
+// forward sweep that recomputes X of the group's rows from the checkpoint
+// row above them (the grid's top boundary for the last group).  The reverse
+// sweep's row between groups passes through the two hand-off rows in turn.
+int backward_checkpointed(const Layout& L, char* ws, const float* x, const float* y,
+                          int64_t B, int64_t N, int64_t M, int64_t D, float gamma,
+                          const float* grad_loss, float* grad_x, float* grad_y, float* align,
+                          hipStream_t s) {
+  unsigned* ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl);
+  unsigned* gctrl = ctrl + L.gctrl;
+  unsigned* full = gctrl + 2 + (size_t)B * (size_t)L.G;
+  double* ckpt = reinterpret_cast<double*>(ws + L.ckpt);
+  double* rh = reinterpret_cast<double*>(ws + L.rh);
+  const int64_t G = L.G, ng = L.ng, nb = L.nbands;
+  hipError_t e = hipSuccess;
+  if (grad_y) e = sdtw::launch_zero_f32(grad_y, B * M * D, s);
+  // Group control words start cleared (each launch leaves them so); the
+  // full word tells a range launch that its top row is complete.
+  if (e == hipSuccess) e = sdtw::launch_zero_u32(gctrl, 2 + B * G, s);
+  if (e == hipSuccess) e = sdtw::launch_fill_u32(full, 1, (unsigned)M, s);
+  DPArgs base = dp_args(L, ws, x, y, B, N, M, D, gamma, false);
+  base.ctrl = gctrl;
+  base.nbands = (int)G;                      // bands of the X buffer
+  base.full_word = full;
+  base.sink_word = full + 1;
+  for (int64_t h = 0; h < ng && e == hipSuccess; ++h) {
+    const int64_t r1 = N - 64 * h * G;       // original rows [r0, r1)
+    const int64_t r0 = N - 64 * (h + 1) * G > 0 ? N - 64 * (h + 1) * G : 0;
+    DPArgs f = base;
+    f.row0 = f.xrow0 = r0;
+    f.nseg = (int)((r1 - r0 + 63) / 64);
+    f.top_row = h + 1 < ng ? ckpt + h * (M + 2 * sdtw::kCkPad) + sdtw::kCkPad : nullptr;
+    f.top_ld = (ng - 1) * (M + 2 * sdtw::kCkPad);
+    e = sdtw::launch_fused_range(f, false, s);
+    if (e != hipSuccess) break;
+    DPArgs r = base;
+    r.row0 = 64 * h * G;
+    r.xrow0 = r0;
+    r.nseg = (int)(nb - h * G < G ? nb - h * G : G);
+    r.top_row = h > 0 ? rh + ((h - 1) & 1) * B * M : nullptr;
+    r.top_ld = M;
+    r.bot_row = h + 1 < ng ? rh + (h & 1) * B * M : nullptr;
+    r.gl = grad_loss;
+    r.gx = grad_x;
+    r.gy = grad_y;
+    r.align = align;
+    e = sdtw::launch_fused_range(r, true, s);
+  }
+  return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
+}
+
 int check_ws(const Layout& L, void* ws, size_t bytes) {
   if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return SDTW_ERR_INVALID_ARG;
   if (bytes < L.total) return SDTW_ERR_WORKSPACE;
@@ -207,7 +305,7 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
   // forward (later launches find them cleared by the kernels), by the
   // distance kernel where there is one.
   hipError_t e = hipSuccess;
-  if (mode == SDTW_MODE_INFERENCE) {
+  if (mode == SDTW_MODE_INFERENCE || mode == SDTW_MODE_CHECKPOINT) {
     if (L.hcols) {
       // Ring hand-off needs every band of a pair resident at once (one
       // workgroup per band, at least one workgroup per CU).
@@ -218,6 +316,12 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
       if ((int64_t)cus < L.nseg) return SDTW_ERR_UNSUPPORTED;
     }
     e = sdtw::launch_zero_u32(ctrl, (int64_t)L.ctrl_words, s);
+    if (mode == SDTW_MODE_CHECKPOINT) {
+      a.R = nullptr;
+      a.ckpt = reinterpret_cast<double*>(ws + L.ckpt);
+      a.ck_span = 64 * L.G;
+      a.nck = (int)(L.ng - 1);
+    }
     if (e == hipSuccess) e = sdtw::launch_infer(a, L.hcols, s);
   } else if (fused) {
     e = sdtw::launch_zero_u32(ctrl, (int64_t)L.ctrl_words, s);
@@ -243,6 +347,11 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
   if (mode == SDTW_MODE_INFERENCE) return SDTW_ERR_UNSUPPORTED;  // nothing kept to go back on
+  if (mode == SDTW_MODE_CHECKPOINT) {
+    if (!grad_x && !grad_y && !align) return SDTW_OK;
+    return backward_checkpointed(L, ws, x, y, B, N, M, D, gamma, grad_loss, grad_x, grad_y,
+                                 align, (hipStream_t)stream);
+  }
   DPArgs a = dp_args(L, ws, x, y, B, N, M, D, gamma, mode == SDTW_MODE_FUSED);
   if (mode == SDTW_MODE_FUSED) {
     // One reverse sweep per slice of D; it writes dx, adds into dy and, if

@@ -269,6 +269,18 @@ hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ void k_fill_u32(unsigned* p, int64_t n, unsigned v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_u32(unsigned* p, int64_t n, unsigned v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  TimedLaunch timed_("fill_u32", s);
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
 __global__ void k_zero_f32(float* p, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.f;

@@ -200,4 +200,28 @@ __device__ __forceinline__ LaneCursor lane_cursor(bool rev, int64_t b, int64_t i
   return c;
 }
 
+// The fused kernels' view: R holds original rows xrow0 .. of each pair in
+// nbands bands, and the sweep rows of a launch may start anywhere.  The
+// forward sweep's rows past the grid stay in the launch's last band; the
+// reverse sweep's rows past the grid only load (their values are never
+// used) and read row xrow0 + lane instead.
+__device__ __forceinline__ LaneCursor lane_cursor_rows(bool rev, int64_t b, int64_t i,
+                                                       int lane, int64_t N, int64_t M,
+                                                       int nbands, int64_t S, int64_t xrow0) {
+  LaneCursor c;
+  if (!rev) {
+    const int64_t r = i - xrow0;
+    const int64_t l = r & 63;
+    // cell (r, t - lane) is at step t - lane + l + off
+    c.base = ((b * nbands + (r >> 6)) * S + (kSkewOff + l - lane)) * 64 + l;
+    c.dir = 64;
+  } else {
+    const int64_t r = i < N ? N - 1 - i - xrow0 : lane;
+    const int64_t l = r & 63;
+    c.base = ((b * nbands + (r >> 6)) * S + (M - 1 + lane + l + kSkewOff)) * 64 + l;
+    c.dir = -64;
+  }
+  return c;
+}
+
 }  // namespace sdtw

@@ -66,30 +66,42 @@ __device__ __forceinline__ unsigned umin_u(unsigned a, unsigned b) { return a < 
 // ---------------------------------------------------------------------------
 // Band wave.
 // ---------------------------------------------------------------------------
-template <bool REV, bool STORE>
+template <bool REV, bool STORE, bool CKPT>
 __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, float* dr, int b,
                                            int band, int lane) {
   const int64_t N = a.N, M = a.M, S = a.S;
-  const int64_t r0 = (int64_t)band * 64;
+  const int64_t r0 = a.row0 + (int64_t)band * 64;
   const int64_t i = r0 + lane;
   const int qcount = (int)(sweep_steps(M) / kCH);
-  const bool top_ring = band > 0;
-  const bool out_used = band + 1 < a.nbands;
+  const bool top_ring = band > 0 || a.top_row != nullptr;
+  const bool out_used = band + 1 < a.nseg || a.bot_row != nullptr;
   const unsigned Mu = (unsigned)M;
-  const LaneCursor cu = lane_cursor(REV, b, i, lane, N, M, a.nbands, S);
-  double* const rbase = a.R + cu.base;
+  const LaneCursor cu = lane_cursor_rows(REV, b, i, lane, N, M, a.nbands, S, a.xrow0);
+  double* const rbase = (REV || STORE) ? a.R + cu.base : nullptr;
   const double k2 = a.k2;
   const double xnm = REV ? a.loss64[b] : 0.0;
   const int64_t lastrow = N - 1;
-  const bool has_last = !REV && (lastrow >> 6) == band;
-  const int64_t tlast = M - 1 + (lastrow & 63);
+  const bool has_last = !REV && a.loss != nullptr && lastrow >= r0 && lastrow < r0 + 64;
+  const int64_t tlast = M - 1 + (lastrow - r0);
   const int qlast = (int)(tlast / kCH), ulast = (int)(tlast % kCH);
+  // Checkpoint row of this lane (forward, CKPT): stored for every step, its
+  // columns outside 0..M-1 going to the row's padding.
+  double* ckp = nullptr;
+  bool band_ck = false;
+  if (CKPT) {
+    const int64_t back = N - 1 - i;
+    const bool ck = i < N && back > 0 && back % a.ck_span == 0 && back / a.ck_span <= a.nck;
+    if (ck)
+      ckp = a.ckpt + ((int64_t)b * a.nck + (back / a.ck_span - 1)) * (M + 2 * kCkPad) + kCkPad -
+            lane;
+    band_ck = __ballot(ck) != 0;
+  }
   float* alignp = (REV && a.align && i < N) ? a.align + ((int64_t)b * N + (N - 1 - i)) * M
                                             : nullptr;
   constexpr int dir = REV ? -64 : 64;
 
   double cur = kBig;
-  double up = (band == 0 && lane == 0) ? 0.0 : kBig;
+  double up = (r0 == 0 && lane == 0) ? 0.0 : kBig;
   unsigned seen_wr = 0, seen_rd = 0, seen_d = 0;
 
   // Reverse sweep: the forward state of the chunk's cells, requested one
@@ -140,6 +152,7 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
       bottom[u] = c;
       if (!REV) {
         if (STORE) __builtin_nontemporal_store(c, (u < 8 ? sp : sp8) + (u & 7) * dir);
+        if (CKPT && band_ck && ckp) ckp[t] = c;
       } else if (!boundary) {
         const float ev = align_entry(xnm, rn[u], tp);
         dr[((t - lane) & (kFR - 1)) * kFPitch + lane] = ev;
@@ -296,7 +309,7 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
   const int64_t N = a.N, M = a.M, D = a.D;
   const int P = fused_pitch(D);
   const int qcount = (int)(sweep_steps(M) / kCH);
-  const int64_t r0 = (int64_t)band * 64;
+  const int64_t r0 = a.row0 + (int64_t)band * 64;
   const int64_t dbeg = (int64_t)c * DC;
   const bool want_gx = a.gx != nullptr, want_gy = a.gy != nullptr;
   if ((!want_gx && !want_gy) || dbeg >= D) {
@@ -456,7 +469,7 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
 // rows handed between bands are either whole (hcols = 0) or global rings of
 // hcols columns; with rings tickets run pair by pair (see above).
 // ---------------------------------------------------------------------------
-template <bool REV, bool INFER, int HD, int HC, int DC>
+template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC>
 __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsigned hcols) {
   extern __shared__ float smem[];
   __shared__ FusedShared sh;
@@ -483,7 +496,7 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
 
   // x rows of this band in sweep order, zero-padded to P columns.
   const float* xb = a.x + (int64_t)b * N * D;
-  const int64_t r0 = (int64_t)band * 64;
+  const int64_t r0 = a.row0 + (int64_t)band * 64;
   for (int idx = threadIdx.x; idx < 64 * P; idx += blockDim.x) {
     const int rr = idx / P, d = idx - rr * P;
     const int64_t si = r0 + rr;
@@ -494,7 +507,7 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
   __syncthreads();
 
   if (w == 0) {
-    fused_band<REV, !INFER>(a, sh, dr, b, band, lane);
+    fused_band<REV, !INFER, CKPT>(a, sh, dr, b, band, lane);
   } else if (w <= HD) {
     fused_dist_helper<REV, HC>(a, sh, xs, dr, b, w - 1, HD, lane);
   } else if (w < kIO) {
@@ -513,16 +526,24 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
       unsigned* fetched = a.ctrl + 2 + (int64_t)a.B * a.nseg;
       gr = GlobalRow{hcols, fetched + pb + band + 1, fetched + pb + band};
     }
-    segment_io_wave(band > 0, band + 1 < a.nseg, a.ctrl + 2 + sin, a.ctrl + 2 + sout,
-                    a.H + sin * row, a.H + sout * row, sh.ring_in, &sh.wr_in, &sh.rd_in,
-                    sh.ring_out, &sh.wr_out, &sh.rd_out, (unsigned)a.M, lane, gr);
+    // A range launch takes its first band's top row complete from top_row
+    // and hands its last band's bottom row out through bot_row.
+    const bool ext_in = band == 0 && a.top_row != nullptr;
+    const bool ext_out = band + 1 == a.nseg && a.bot_row != nullptr;
+    segment_io_wave(band > 0 || ext_in, band + 1 < a.nseg || ext_out,
+                    ext_in ? a.full_word : a.ctrl + 2 + sin,
+                    ext_out ? a.sink_word : a.ctrl + 2 + sout,
+                    ext_in ? a.top_row + (int64_t)b * a.top_ld : a.H + sin * row,
+                    ext_out ? a.bot_row + (int64_t)b * a.M : a.H + sout * row, sh.ring_in,
+                    &sh.wr_in, &sh.rd_in, sh.ring_out, &sh.wr_out, &sh.rd_out,
+                    (unsigned)a.M, lane, gr);
   }
   release_ctrl(a.ctrl, (INFER && hcols ? 2 : 1) * (int64_t)a.B * a.nseg);
 }
 
-template <bool REV, bool INFER, int HD, int HC, int DC>
+template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC>
 static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcols = 0) {
-  auto kern = k_dp_fused<REV, INFER, HD, HC, DC>;
+  auto kern = k_dp_fused<REV, INFER, CKPT, HD, HC, DC>;
   const size_t lds = fused_lds_bytes(a.D, REV ? DC : 0);
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -535,16 +556,25 @@ static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcol
 
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
-  if (!reverse) return launch_fused_one<false, false, kFwdHelpD, 0, 32>(a, s);
+  if (!reverse) return launch_fused_one<false, false, false, kFwdHelpD, 0, 32>(a, s);
   // Each of the two chain-rule helpers owns DC columns of D.
-  if (a.D <= 2 * 32) return launch_fused_one<true, false, kRevHelpD, kRevHelpC, 32>(a, s);
-  if (a.D <= 2 * 64) return launch_fused_one<true, false, kRevHelpD, kRevHelpC, 64>(a, s);
-  return launch_fused_one<true, false, kRevHelpD, kRevHelpC, 128>(a, s);
+  if (a.D <= 2 * 32) return launch_fused_one<true, false, false, kRevHelpD, kRevHelpC, 32>(a, s);
+  if (a.D <= 2 * 64) return launch_fused_one<true, false, false, kRevHelpD, kRevHelpC, 64>(a, s);
+  return launch_fused_one<true, false, false, kRevHelpD, kRevHelpC, 128>(a, s);
+}
+
+hipError_t launch_fused_range(const DPArgs& a, bool reverse, hipStream_t s) {
+  // Forward ranges start their state rows at their first sweep row, so a
+  // lane's storage row keeps the lane's position in its band.
+  if (!reverse && a.row0 != a.xrow0) return hipErrorInvalidValue;
+  if (reverse && (a.row0 & 63) != 0) return hipErrorInvalidValue;
+  return launch_dp_fused(a, reverse, s);
 }
 
 hipError_t launch_infer(const DPArgs& a, unsigned hcols, hipStream_t s) {
   if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
-  return launch_fused_one<false, true, kFwdHelpD, 0, 32>(a, s, hcols);
+  if (a.ckpt) return launch_fused_one<false, true, true, kFwdHelpD, 0, 32>(a, s, hcols);
+  return launch_fused_one<false, true, false, kFwdHelpD, 0, 32>(a, s, hcols);
 }
 
 }  // namespace sdtw

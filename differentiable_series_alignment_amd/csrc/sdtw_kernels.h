@@ -54,7 +54,26 @@ struct DPArgs {
   int B, nbands, nseg;
   double k2;            // log2(e) / gamma
   double g_ln2;         // gamma * ln(2) = 1 / k2
+  // Fused kernels on a range of rows (checkpointed training).  The launch's
+  // band k covers sweep rows row0 + 64k .. row0 + 64k + 63 (nseg bands);
+  // R holds original rows xrow0 .. xrow0 + 64*nbands - 1.  When set, top_row
+  // (row stride top_ld) is the complete row above the first band and bot_row
+  // receives the last band's bottom row; full_word holds M and sink_word
+  // takes the unused progress count.  All zero for whole-grid launches.
+  int64_t row0, xrow0, top_ld;
+  const double* top_row;
+  double* bot_row;
+  const unsigned* full_word;
+  unsigned* sink_word;
+  // Checkpoint rows written by the forward: original row r with
+  // (N-1-r) = ck_span*(h+1), h < nck, goes to ckpt[(b*nck + h)*(M+2*kCkPad) + kCkPad + c].
+  double* ckpt;
+  int64_t ck_span;
+  int nck;
 };
+// Padding on each side of a stored checkpoint row (columns the band wave
+// touches outside 0..M-1 land there).
+constexpr int64_t kCkPad = 80;
 
 // Bands (64 rows each) per workgroup of the DP kernels.
 constexpr int kBandsPerWG = 4;
@@ -95,9 +114,14 @@ hipError_t launch_dp_both(const DPArgs& a, hipStream_t s);
 // Fused: one sweep per launch (the reverse one with the chain rule inside).
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s);
 // Loss only: the fused forward sweep without stored state; hand-off rows are
-// global rings of `hcols` columns (0: whole rows).
+// global rings of `hcols` columns (0: whole rows).  With a.ckpt set it also
+// writes the checkpoint rows.
 constexpr unsigned kHRing = 512;
 hipError_t launch_infer(const DPArgs& a, unsigned hcols, hipStream_t s);
+// Fused sweep over a range of rows (a.row0, a.nseg bands, see DPArgs): the
+// forward one stores X of the range into R, the reverse one reads it.
+hipError_t launch_fused_range(const DPArgs& a, bool reverse, hipStream_t s);
+hipError_t launch_fill_u32(unsigned* p, int64_t n, unsigned v, hipStream_t s);
 // Chain rule of the unfused backward.  The row pass forms E = 2^(Xnm-X-T')
 // from R and R2 into `esk` (the distance array, no longer needed) and, if
 // gx is given, writes dx; the column pass reads E from `esk` and writes dy.

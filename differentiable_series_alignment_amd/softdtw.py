@@ -137,20 +137,27 @@ def choose_fused(fused, B: int, N: int, M: int, D: int, device=None) -> bool:
 
 
 def soft_dtw(x: torch.Tensor, y: torch.Tensor, gamma: float = 1.0,
-             fused=False) -> torch.Tensor:
+             fused=False, checkpoint: bool = False) -> torch.Tensor:
     """Per-pair Soft-DTW loss (B,) with autograd support.  When no gradient
     can be asked for (autograd off, or neither input requires one) the loss
     comes from the inference mode, which keeps no state; its value is bitwise
     the one of the other modes.  ``fused``: True, False, or None / "auto"
-    (see choose_fused)."""
+    (see choose_fused).  ``checkpoint=True`` trains with distances recomputed
+    as in fused mode and without the B x N x M forward state: the backward
+    recomputes it group by group of rows from checkpoint rows (about
+    sqrt(N/64) groups), for a workspace of about sqrt(N/64) x 64 rows of M
+    states per pair instead of N."""
     _validate(x, y, gamma)
     if not (torch.is_grad_enabled() and (x.requires_grad or y.requires_grad)):
         loss = _loss_only(x, y, float(gamma))
         if loss is not None:
             return loss
     B, N, D = x.shape
-    use_fused = choose_fused(fused, B, N, y.shape[1], D, x.device)
-    mode = L.SDTW_MODE_FUSED if use_fused else L.SDTW_MODE_UNFUSED
+    if checkpoint:
+        mode = L.SDTW_MODE_CHECKPOINT
+    else:
+        use_fused = choose_fused(fused, B, N, y.shape[1], D, x.device)
+        mode = L.SDTW_MODE_FUSED if use_fused else L.SDTW_MODE_UNFUSED
     return _SoftDTWFunction.apply(x, y, float(gamma), mode)
 
 
@@ -162,7 +169,7 @@ class SoftDTW(torch.nn.Module):
     terms run as one batch of 3B pairs."""
 
     def __init__(self, gamma: float = 1.0, dist: str = "sqeuclidean",
-                 fused=False, normalize: bool = False):
+                 fused=False, normalize: bool = False, checkpoint: bool = False):
         super().__init__()
         if dist != "sqeuclidean":
             raise ValueError(f"only dist='sqeuclidean' is supported, got {dist!r}")
@@ -175,6 +182,7 @@ class SoftDTW(torch.nn.Module):
             raise ValueError(f"fused must be True, False, None or 'auto', got {fused!r}")
         self.fused = fused if (fused is None or isinstance(fused, str)) else bool(fused)
         self.normalize = bool(normalize)
+        self.checkpoint = bool(checkpoint)
 
     def forward(self, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
         if self.normalize:
@@ -186,13 +194,13 @@ class SoftDTW(torch.nn.Module):
             # reach x and y through the concatenation.
             B = x.shape[0]
             loss = soft_dtw(torch.cat([x, x, y], 0), torch.cat([y, x, y], 0),
-                            self.gamma, self.fused)
+                            self.gamma, self.fused, self.checkpoint)
             return loss[:B] - 0.5 * (loss[B:2 * B] + loss[2 * B:])
-        return soft_dtw(x, y, self.gamma, self.fused)
+        return soft_dtw(x, y, self.gamma, self.fused, self.checkpoint)
 
     def extra_repr(self) -> str:
         return (f"gamma={self.gamma}, dist={self.dist!r}, fused={self.fused}, "
-                f"normalize={self.normalize}")
+                f"normalize={self.normalize}, checkpoint={self.checkpoint}")
 
 
 def sqeuclidean(x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
@@ -211,14 +219,15 @@ def sqeuclidean(x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
 
 
 def alignment(x: torch.Tensor, y: torch.Tensor, gamma: float = 1.0,
-              fused: bool = False):
+              fused: bool = False, checkpoint: bool = False):
     """(loss[B], E[B,N,M]): the loss and the alignment matrix dloss/dDist."""
     _validate(x, y, gamma)
     x = x.contiguous()
     y = y.contiguous()
     B, N, D = x.shape
     M = y.shape[1]
-    mode = L.SDTW_MODE_FUSED if fused else L.SDTW_MODE_UNFUSED
+    mode = (L.SDTW_MODE_CHECKPOINT if checkpoint else
+            L.SDTW_MODE_FUSED if fused else L.SDTW_MODE_UNFUSED)
     s = _stream(x.device)
     with torch.cuda.device(x.device):
         ws = _workspace(B, N, M, D, mode, x.device)

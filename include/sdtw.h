@@ -41,9 +41,22 @@
  *                      for it, and with rings sdtw_forward returns
  *                      SDTW_ERR_UNSUPPORTED on a GPU with fewer CUs than
  *                      the pair has bands (they must all be resident).  The
- *                      loss is bitwise the one the other two modes return.
- * The two training modes keep the forward DP state (fp64, B x N x M) for the
- * backward.
+ *                      loss is bitwise the one the other modes return.
+ *   SDTW_MODE_CHECKPOINT training without the B x N x M forward state
+ *                      (distances recomputed as in fused mode, D <= 256):
+ *                      the forward is the inference one and also keeps one
+ *                      checkpoint row (fp64, M states) every G = ceil(sqrt(
+ *                      ceil(N/64))) bands; the backward runs the reverse
+ *                      sweep group by group of G bands from the bottom,
+ *                      each after a forward sweep that recomputes the
+ *                      group's states from the checkpoint row above it.
+ *                      Workspace about B*(G*64*(M+222)*8 + N/(64G)*M*8)
+ *                      bytes, plus the inference mode's hand-off rows (the
+ *                      same CU condition applies to its forward).  Loss, alignment matrix and grad_x are
+ *                      bitwise those of SDTW_MODE_FUSED (same arithmetic on
+ *                      the same values); the backward is repeatable.
+ * The unfused and fused modes keep the forward DP state (fp64, B x N x M)
+ * for the backward.
  * Distances are accumulated in fp64 and rounded once to fp32 in both modes,
  * so fused and unfused see identical distances, losses and alignment
  * matrices (gradients agree to rounding: they are summed in other orders).
@@ -85,7 +98,8 @@ typedef enum {
 typedef enum {
     SDTW_MODE_UNFUSED = 0,
     SDTW_MODE_FUSED = 1,
-    SDTW_MODE_INFERENCE = 2
+    SDTW_MODE_INFERENCE = 2,
+    SDTW_MODE_CHECKPOINT = 3
 } sdtw_mode_t;
 
 /* Version of this ABI (SDTW_ABI_VERSION). */

@@ -72,7 +72,7 @@ def _bwd(**kw):
 @pytest.mark.parametrize("kw", [
     dict(gamma=0.0), dict(gamma=-1.0), dict(gamma=float("nan")), dict(gamma=float("inf")),
     dict(B=0), dict(N=0), dict(M=0), dict(D=0), dict(N=-3),
-    dict(x=None), dict(y=None), dict(mode=3), dict(mode=-1), dict(workspace=None),
+    dict(x=None), dict(y=None), dict(mode=4), dict(mode=-1), dict(workspace=None),
     dict(workspace=FAKE * 256 + 8),
 ])
 def test_forward_backward_reject_invalid(kw):
@@ -138,6 +138,19 @@ def test_fused_choice_and_early_stopping_validation():
         EarlyStopping(patience=0)
     es = EarlyStopping(patience=2, tol=0.0)
     assert [es.step(v) for v in (3.0, 2.0, 2.0, 2.5)] == [False, False, False, True]
+
+
+def test_checkpoint_mode_workspace():
+    """Checkpointed training keeps checkpoint rows and one group of bands'
+    forward state (about sqrt(N/64) bands) instead of all N rows."""
+    def ws(*a):
+        return L.sdtw_workspace_bytes(*a, L.SDTW_MODE_CHECKPOINT)
+    fused = L.sdtw_workspace_bytes(32, 4096, 4096, 128, L.SDTW_MODE_FUSED)
+    assert 0 < ws(32, 4096, 4096, 128) * 5 < fused
+    # the group of bands kept grows like sqrt(N): 4x the rows, about 2x the state
+    r = ws(8, 16384, 1000, 4) / ws(8, 4096, 1000, 4)
+    assert 1.7 < r < 2.5, r
+    assert ws(2, 10, 10, 257) == 0 and ws(2, 10, 10, 256) > 0
 
 
 def test_timing_switch_without_launches():

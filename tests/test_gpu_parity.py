@@ -30,10 +30,10 @@ def S():
     return pkg
 
 
-def gpu_value_and_grad(S, x, y, gamma, fused=False):
+def gpu_value_and_grad(S, x, y, gamma, fused=False, checkpoint=False):
     xd = x.to(DEV).requires_grad_(True)
     yd = y.to(DEV).requires_grad_(True)
-    loss = S.soft_dtw(xd, yd, gamma, fused=fused)
+    loss = S.soft_dtw(xd, yd, gamma, fused=fused, checkpoint=checkpoint)
     loss.mean().backward()
     torch.cuda.synchronize()
     return (loss.detach().cpu().double().numpy(), xd.grad.cpu().double().numpy(),
@@ -267,6 +267,56 @@ def test_fused_matches_unfused(S, N, M, D):
     _, gxf, gyf = gpu_value_and_grad(S, x, y, 0.7, fused=True)
     np.testing.assert_allclose(gxf, gxu, rtol=1e-4, atol=1e-6)
     np.testing.assert_allclose(gyf, gyu, rtol=1e-4, atol=1e-6)
+
+
+# --- checkpointed training against fused mode and the oracle -----------------------------
+
+@pytest.mark.parametrize("B,N,M,D", [
+    (2, 16, 16, 1),        # one band, one group
+    (3, 300, 200, 5),      # 5 bands in groups of 3: two groups, ragged top
+    (2, 256, 300, 64),     # 4 bands, groups of 2, N a multiple of 64
+    (1, 513, 40, 3),       # 9 bands, groups of 3, one row in the top band
+    (2, 1100, 70, 8),      # 18 bands, groups of 5
+    (2, 130, 1100, 16),    # long M
+])
+def test_checkpoint_matches_fused(S, B, N, M, D):
+    """Checkpointed training recomputes the forward state group by group of
+    rows from checkpoint rows: the same arithmetic on the same values as
+    fused mode, so the loss, the alignment matrix and dx agree bitwise (dy
+    is summed with atomics in both modes); a second backward on the same
+    forward gives the same result."""
+    x, y = pair_batch(B, N, M, D, seed=N + M + D + 7)
+    xd, yd = x.to(DEV), y.to(DEV)
+    lf, Ef = S.alignment(xd, yd, 0.8, fused=True)
+    lc, Ec = S.alignment(xd, yd, 0.8, checkpoint=True)
+    torch.testing.assert_close(lc, lf, rtol=0, atol=0)
+    torch.testing.assert_close(Ec, Ef, rtol=0, atol=0)
+    _, gxf, gyf = gpu_value_and_grad(S, x, y, 0.8, fused=True)
+    xg = xd.clone().requires_grad_(True)
+    yg = yd.clone().requires_grad_(True)
+    loss = S.soft_dtw(xg, yg, 0.8, checkpoint=True).mean()
+    gx1, gy1 = torch.autograd.grad(loss, (xg, yg), retain_graph=True)
+    gx2, gy2 = torch.autograd.grad(loss, (xg, yg))
+    np.testing.assert_array_equal(gx1.cpu().double().numpy(), gxf)
+    torch.testing.assert_close(gx2, gx1, rtol=0, atol=0)
+    np.testing.assert_allclose(gy1.cpu().double().numpy(), gyf, rtol=1e-4, atol=1e-6)
+
+
+@pytest.mark.parametrize("B,N,M,D,gamma", [(3, 300, 200, 5, 1.0), (2, 700, 90, 4, 0.1)])
+def test_checkpoint_against_oracle(O, S, B, N, M, D, gamma):
+    x, y = pair_batch(B, N, M, D, seed=3 * N + M)
+    l, gx, gy = gpu_value_and_grad(S, x, y, gamma, checkpoint=True)
+    l0, gx0, gy0 = O.value_and_grad(x.numpy(), y.numpy(), gamma, np.full(B, 1.0 / B))
+    assert_loss(l, l0, "checkpoint")
+    assert_grad(gx, gx0, "checkpoint dx")
+    assert_grad(gy, gy0, "checkpoint dy")
+
+
+def test_checkpoint_workspace_is_smaller():
+    from differentiable_series_alignment_amd import _lib as L
+    fused = L.sdtw_workspace_bytes(32, 4096, 4096, 128, L.SDTW_MODE_FUSED)
+    ck = L.sdtw_workspace_bytes(32, 4096, 4096, 128, L.SDTW_MODE_CHECKPOINT)
+    assert 0 < ck * 5 < fused
 
 
 def test_fused_rejects_large_D(S):
