@@ -92,6 +92,27 @@ struct StageXT {
   }
 };
 
+// Work item of a workgroup in a 1-D grid of 8 * ceil(W / 8) workgroups over
+// W = n0 * n1 * n2 items (n0 fastest).  The GPU deals consecutive workgroups
+// to its 8 XCDs in turn, so workgroup g takes item (g % 8) * ceil(W / 8) +
+// g / 8: each XCD gets a contiguous run of items, and the items of one pair
+// (consecutive in n0) share that XCD's L2.  Returns false past the last item.
+struct WorkItem {
+  int64_t i0, i1, i2;
+};
+__device__ __forceinline__ bool xcd_item(int64_t n0, int64_t n1, int64_t n2, WorkItem* it) {
+  const int64_t per = (n0 * n1 * n2 + 7) / 8;
+  const int64_t w = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= n0 * n1 * n2) return false;
+  it->i0 = w % n0;
+  it->i1 = (w / n0) % n1;
+  it->i2 = w / (n0 * n1);
+  return true;
+}
+__host__ inline unsigned xcd_grid(int64_t n0, int64_t n1, int64_t n2) {
+  return (unsigned)(8 * ((n0 * n1 * n2 + 7) / 8));
+}
+
 // Split sums.  When the columns (dx) or the bands (dy) of one workgroup's sum
 // are spread over `nsplit` workgroups, each writes its partial (the NTW
 // accumulator tiles and the row or column sum, per thread) to `part`
@@ -153,7 +174,7 @@ __device__ __forceinline__ bool split_reduce(v16f (&acc)[NTW], float& sum, float
 // registers while the current block computes.  FORM: the window comes from
 // the sweeps' states and E is formed (and stored) on the way; otherwise it
 // is read from the stored E.  GX = false forms E only.  The band's column
-// blocks are split over gridDim.z workgroups (split sums, above).
+// blocks are split over nsplit workgroups (split sums, above).
 template <int NTW, bool GX, bool FORM>
 __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
                                                     const double* __restrict__ R,
@@ -166,10 +187,13 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
                                                     int64_t M, int64_t D, int64_t S,
                                                     int nbands, int64_t d0,
                                                     float* __restrict__ part,
-                                                    unsigned* __restrict__ cnt) {
+                                                    unsigned* __restrict__ cnt,
+                                                    int64_t nb_pairs, int nsplit) {
   __shared__ float ring[kRingSteps * kRingPitch];
-  const int64_t b = blockIdx.y, band = blockIdx.x;
-  const int p = blockIdx.z, nsplit = gridDim.z;
+  WorkItem it;
+  if (!xcd_item(nbands, nb_pairs, nsplit, &it)) return;
+  const int64_t b = it.i1, band = it.i0;
+  const int p = (int)it.i2;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int r = l & 31, h = l >> 5;
   const int rt = w & 1, dsel = w >> 1;
@@ -288,7 +312,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
 // dy for 64 columns of one pair, columns of D in [d0, d0 + 128), summing over
 // every band.  Wave w: column tile w & 1, d tiles (w >> 1) + 2t.  The band's
 // window of steps [j0, j0 + 128) is fetched into registers one band ahead.
-// The bands are split over gridDim.z workgroups (split sums, above).
+// The bands are split over nsplit workgroups (split sums, above).
 template <int NTW>
 __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ esk,
                                                     const float* __restrict__ x,
@@ -298,10 +322,14 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
                                                     int64_t M, int64_t D, int64_t S,
                                                     int nbands, int64_t d0,
                                                     float* __restrict__ part,
-                                                    unsigned* __restrict__ cnt) {
+                                                    unsigned* __restrict__ cnt,
+                                                    int64_t nb_pairs, int nsplit) {
   __shared__ float ring[kRingSteps * kRingPitch];
-  const int64_t b = blockIdx.y, j0 = (int64_t)blockIdx.x * 64;
-  const int p = blockIdx.z, nsplit = gridDim.z;
+  const int64_t ncb = (M + 63) / 64;
+  WorkItem it;
+  if (!xcd_item(ncb, nb_pairs, nsplit, &it)) return;
+  const int64_t b = it.i1, cb = it.i0, j0 = cb * 64;
+  const int p = (int)it.i2;
   const int64_t bb0 = (int64_t)p * nbands / nsplit, bb1 = (int64_t)(p + 1) * nbands / nsplit;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int r = l & 31, h = l >> 5;
@@ -368,8 +396,8 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
   }
 
   if (nsplit > 1 &&
-      !split_reduce<NTW>(acc, csum, part + (b * gridDim.x + blockIdx.x) * (int64_t)nsplit * (16 * NTW + 1) * 256,
-                         cnt + b * gridDim.x + blockIdx.x, p, nsplit))
+      !split_reduce<NTW>(acc, csum, part + (b * ncb + cb) * (int64_t)nsplit * (16 * NTW + 1) * 256,
+                         cnt + b * ncb + cb, p, nsplit))
     return;
 
   csum += __shfl_xor(csum, 32, 64);
@@ -417,18 +445,19 @@ size_t chain_part_floats(int64_t B, int64_t N, int64_t M) {
 }
 
 template <int NTW, bool FORM>
-static void launch_rows(dim3 grid, hipStream_t s, float* esk, const double* R,
-                        const double* R2, const double* loss64, const float* x,
-                        const float* y, const float* gl, float* gx, int64_t N, int64_t M,
-                        int64_t D, int64_t S, int nb, int64_t d0, float* part,
+static void launch_rows(int64_t B, unsigned nsplit, hipStream_t s, float* esk,
+                        const double* R, const double* R2, const double* loss64,
+                        const float* x, const float* y, const float* gl, float* gx, int64_t N,
+                        int64_t M, int64_t D, int64_t S, int nb, int64_t d0, float* part,
                         unsigned* cnt) {
+  const dim3 grid(xcd_grid(nb, B, nsplit));
   TimedLaunch timed_("chain_rows", s);
   if (gx)
     hipLaunchKernelGGL((k_chain_rows<NTW, true, FORM>), grid, dim3(256), 0, s, esk, R, R2,
-                       loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt);
+                       loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt, B, (int)nsplit);
   else
     hipLaunchKernelGGL((k_chain_rows<1, false, FORM>), grid, dim3(256), 0, s, esk, R, R2,
-                       loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt);
+                       loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt, B, (int)nsplit);
 }
 
 hipError_t launch_chain(float* esk, const double* R, const double* R2,
@@ -444,17 +473,16 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
     if (d0 > 0 && !gx) break;
     const int64_t dw = D - d0 < 128 ? D - d0 : 128;
     const bool two = dw > 64;  // more than two 32-wide d tiles
-    const dim3 grid((unsigned)nb, (unsigned)B, pr);
     if (d0 == 0) {
       if (two)
-        launch_rows<2, true>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
+        launch_rows<2, true>(B, pr, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
       else
-        launch_rows<1, true>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
+        launch_rows<1, true>(B, pr, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
     } else {
       if (two)
-        launch_rows<2, false>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
+        launch_rows<2, false>(B, pr, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
       else
-        launch_rows<1, false>(grid, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
+        launch_rows<1, false>(B, pr, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -462,12 +490,12 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
   if (!gy) return hipSuccess;
   for (int64_t d0 = 0; d0 < D; d0 += 128) {
     const int64_t dw = D - d0 < 128 ? D - d0 : 128;
-    const dim3 grid((unsigned)((M + 63) / 64), (unsigned)B, pc);
+    const dim3 grid(xcd_grid((M + 63) / 64, B, pc));
     TimedLaunch timed_("chain_cols", s);
     if (dw > 64)
-      hipLaunchKernelGGL(k_chain_cols<2>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0, part, cnt_cols);
+      hipLaunchKernelGGL(k_chain_cols<2>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0, part, cnt_cols, B, (int)pc);
     else
-      hipLaunchKernelGGL(k_chain_cols<1>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0, part, cnt_cols);
+      hipLaunchKernelGGL(k_chain_cols<1>, grid, dim3(256), 0, s, esk, x, y, gl, gy, N, M, D, S, nb, d0, part, cnt_cols, B, (int)pc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
