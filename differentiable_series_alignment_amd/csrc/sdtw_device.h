@@ -53,20 +53,30 @@ __device__ __forceinline__ double max_nonan(double a, double b) {
 // Soft-minimum part of one cell of the recurrence in base-2 units
 // X = R * log2(e) / g:
 //   X = d + T,  T = m - log2(2^(m-a) + 2^(m-b) + 2^(m-c)),  m = min(a, b, c),
-// which is R = D + softmin_g(...) scaled by log2(e)/g; this returns T.  The
+// which is R = D + softmin_g(...) scaled by log2(e)/g.  The
 // term of the minimum is exactly 1, so only the other two are
 // exponentiated: with m1 = min(a,c), p = max(a,c), m = min(m1,b),
 // q = max(m1,b), the multiset {a,b,c} is {m,p,q}.  State and differences
 // are fp64; the exponentials and the logarithm are the fp32 hardware
 // instructions applied to the (small, non-positive) fp64 differences.
-__device__ __forceinline__ double softmin2_part(double a, double b, double c) {
+//
+// softmin2_cell returns the whole state X = (m + d) - log2(...) of a cell with
+// scaled distance d, and sets t = T = m - log2(...): m + d is formed while
+// the exponentials and the logarithm are in flight, so the distance costs no
+// step on the dependency chain from one cell to the next.
+__device__ __forceinline__ double softmin2_cell(double a, double b, double c, double d,
+                                                double& t) {
   const double m1 = min_nonan(a, c);
   const double p = max_nonan(a, c);
   const double m = min_nonan(m1, b);
   const double q = max_nonan(m1, b);
+  const double md = m + d;
   const float ep = hw_exp2((float)(m - p));
   const float eq = hw_exp2((float)(m - q));
-  return m - (double)hw_log2((1.0f + ep) + eq);
+  const double lg = (double)hw_log2((1.0f + ep) + eq);
+  const double x = md - lg;
+  t = m - lg;
+  return x;
 }
 
 // Alignment-matrix entry from the two sweeps: with X the forward state of

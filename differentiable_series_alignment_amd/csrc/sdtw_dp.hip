@@ -68,8 +68,8 @@ __device__ __forceinline__ void band_chunk(double& cur, double& up, const double
     double d = (double)dn[u] * k2;
     if (MASK) d = (t0 + u < lane) ? kBig : d;
     const double upn = wave_shr1(cur, top[u]);
-    const double t = softmin2_part(up, upn, cur);
-    const double c = t + d;
+    double t;
+    const double c = softmin2_cell(up, upn, cur, d, t);
     up = upn;
     cur = c;
     bottom[u] = c;

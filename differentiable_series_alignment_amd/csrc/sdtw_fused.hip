@@ -145,8 +145,8 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
       double d = (double)dn[u] * k2;
       d = boundary ? kBig : d;
       const double upn = wave_shr1(cur, top[u]);
-      const double tp = softmin2_part(up, upn, cur);
-      const double c = tp + d;
+      double tp;
+      const double c = softmin2_cell(up, upn, cur, d, tp);
       up = upn;
       cur = c;
       bottom[u] = c;
