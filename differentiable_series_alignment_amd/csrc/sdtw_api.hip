@@ -374,7 +374,7 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
   hipError_t e = sdtw::launch_chain(a.dsk, a.R, a.R2, a.loss64, x, y, grad_loss, grad_x,
                                     grad_y, B, N, M, D, L.S,
                                     reinterpret_cast<float*>(ws + L.part),
-                                    ctrl + L.cnt_rows, ctrl + L.cnt_cols, s);
+                                    ctrl + L.cnt_rows, ctrl + L.cnt_cols, align != nullptr, s);
   if (e == hipSuccess && align) e = sdtw::launch_unskew(a.dsk, align, B, N, M, L.S, s);
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
 }

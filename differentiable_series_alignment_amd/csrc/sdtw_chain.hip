@@ -76,6 +76,7 @@ struct StageXT {
       }
     }
   }
+  template <bool EOUT = true>
   __device__ __forceinline__ void store(float* ring, float* ebp, int64_t s0, double xnm) const {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -87,7 +88,7 @@ struct StageXT {
         q[j] = align_entry(xnm, xv[4 * k + j], tv[4 * k + j]);
         ring[slot * kRingPitch + (e & 63) + j] = q[j];
       }
-      __builtin_nontemporal_store(q, reinterpret_cast<v4f*>(ebp + off[k]));
+      if (EOUT) __builtin_nontemporal_store(q, reinterpret_cast<v4f*>(ebp + off[k]));
     }
   }
 };
@@ -175,7 +176,14 @@ __device__ __forceinline__ bool split_reduce(v16f (&acc)[NTW], float& sum, float
 // the sweeps' states and E is formed (and stored) on the way; otherwise it
 // is read from the stored E.  GX = false forms E only.  The band's column
 // blocks are split over nsplit workgroups (split sums, above).
-template <int NTW, bool GX, bool FORM>
+//
+// GYP (D <= 64, FORM): E is not stored; instead each block also yields the
+// band's shares of dy for its 32 columns: P[b][band][j][d] = -sum over the
+// band's rows i of E[i,j] x_i[d] (d < D) and P[b][band][j][D] = sum of
+// E[i,j], into `esk` viewed as [B][nbands][M][D+1] (k_chain_gy adds the
+// bands up).  Wave w: d tile w >> 1, rows 32 (w & 1) .. +31; the two row
+// halves meet in LDS.
+template <int NTW, bool GX, bool FORM, bool GYP>
 __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
                                                     const double* __restrict__ R,
                                                     const double* __restrict__ R2,
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
   for (int64_t s0 = kb0 * 32; s0 < kb0 * 32 + 96; s0 += 32) {
     if (FORM) {
       sx.load(xbp, tbp, s0, smax);
-      sx.store(ring, bandp, s0, xnm);
+      sx.template store<!GYP>(ring, bandp, s0, xnm);
     } else {
       st.load(bandp, s0, smax);
       st.store(ring, s0);
@@ -244,6 +252,21 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
     }
   };
   if (GX) load_y(kb0 * 32, yv);
+  // GYP: this wave's x rows (B operand of E^T . X, fixed for the band) and
+  // the LDS area where the second row half hands over its sums.
+  const int gdt = w >> 1, grh = w & 1;
+  const int64_t gd = 32 * gdt + r;                 // column of D
+  float xg[16];
+  __shared__ float gsum[GYP ? 2 * 17 * 64 : 1];
+  if (GYP) {
+    const float* xb = x + b * N * D;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      int64_t rr = band * 64 + 32 * grh + 2 * s + h;
+      rr = rr < N ? rr : N - 1;
+      xg[s] = gd < D ? xb[rr * D + gd] : 0.f;
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -269,10 +292,49 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, yv[s][t], acc[t], 0, 0, 0);
       }
     }
+    v16f gacc;
+    float gcs = 0.f;
+    if (GYP) {
+      // E^T . X over this wave's 32 rows: A[j][k] = E[row 32*grh + 2s + k,
+      // column j0 + j] in lane j + 32k.
+#pragma unroll
+      for (int e = 0; e < 16; ++e) gacc[e] = 0.f;
+      const int64_t j = j0 + r;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int lrow = 32 * grh + 2 * s + h;
+        const float a = (band * 64 + lrow < N && j < M)
+                            ? ring[(int)((j + lrow) & (kRingSteps - 1)) * kRingPitch + lrow]
+                            : 0.f;
+        gcs += a;
+        gacc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xg[s], gacc, 0, 0, 0);
+      }
+      gcs += __shfl_xor(gcs, 32, 64);          // column sums over this half
+      if (grh == 1) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) gsum[(gdt * 17 + e) * 64 + l] = gacc[e];
+        gsum[(gdt * 17 + 16) * 64 + l] = gcs;
+      }
+    }
     __syncthreads();
+    if (GYP && grh == 0) {
+      // P[j][d] = colsum_j y_j[d] - (E^T X)[j][d] for the band's 64 rows.
+#pragma unroll
+      for (int e = 0; e < 16; ++e) gacc[e] += gsum[(gdt * 17 + e) * 64 + l];
+      gcs += gsum[(gdt * 17 + 16) * 64 + l];
+      const int64_t D1 = D + 1;
+      float* pb = esk + (b * nbands + band) * M * D1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int jr = 8 * (e >> 2) + 4 * h + (e & 3);   // accumulator row
+        const int64_t jj = j0 + jr;
+        if (jj < M && gd < D) pb[jj * D1 + gd] = -gacc[e];
+      }
+      if (gdt == 0 && h == 0 && j0 + r < M) pb[(j0 + r) * D1 + D] = gcs;
+    }
     if (more) {
       if (FORM)
-        sx.store(ring, bandp, j0 + 96, xnm);
+        sx.template store<!GYP>(ring, bandp, j0 + 96, xnm);
       else
         st.store(ring, j0 + 96);
       if (GX) {
@@ -419,6 +481,32 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
   }
 }
 
+// dy[b,j,d] = 2 g_b (y[b,j,d] sum_k P[b][k][j][D] + sum_k P[b][k][j][d]),
+// the bands k added in order (the shares the row pass wrote with GYP).
+__global__ __launch_bounds__(256) void k_chain_gy(const float* __restrict__ P,
+                                                  const float* __restrict__ y,
+                                                  const float* __restrict__ gl,
+                                                  float* __restrict__ gy, int64_t B, int64_t M,
+                                                  int64_t D, int nbands) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * M * D) return;
+  const int64_t b = i / (M * D), jd = i - b * M * D;
+  const int64_t j = jd / D, d = jd - j * D;
+  const int64_t D1 = D + 1;
+  const float* pp = P + (b * nbands * M + j) * D1;
+  float cs = 0.f, ex = 0.f;
+  for (int k = 0; k < nbands; ++k) {
+    cs += pp[(int64_t)k * M * D1 + D];
+    ex += pp[(int64_t)k * M * D1 + d];
+  }
+  gy[i] = 2.f * gl[b] * (cs * y[i] + ex);
+}
+
+// Whether the per-band shares of dy fit where the distances were.
+bool chain_gy_fits(int64_t M, int64_t D, int64_t S) {
+  return D <= 64 && M * (D + 1) <= S * 64;
+}
+
 // Workgroups per band (dx) or per 64-column block (dy): a launch with fewer
 // groups than the GPU has CUs splits each group's reduction range so that it
 // fills them, keeping at least two column blocks (or bands) per workgroup.
@@ -444,7 +532,7 @@ size_t chain_part_floats(int64_t B, int64_t N, int64_t M) {
   return (size_t)(rows > cols ? rows : cols) * 33 * 256;
 }
 
-template <int NTW, bool FORM>
+template <int NTW, bool FORM, bool GYP = false>
 static void launch_rows(int64_t B, unsigned nsplit, hipStream_t s, float* esk,
                         const double* R, const double* R2, const double* loss64,
                         const float* x, const float* y, const float* gl, float* gx, int64_t N,
@@ -453,10 +541,10 @@ static void launch_rows(int64_t B, unsigned nsplit, hipStream_t s, float* esk,
   const dim3 grid(xcd_grid(nb, B, nsplit));
   TimedLaunch timed_("chain_rows", s);
   if (gx)
-    hipLaunchKernelGGL((k_chain_rows<NTW, true, FORM>), grid, dim3(256), 0, s, esk, R, R2,
+    hipLaunchKernelGGL((k_chain_rows<NTW, true, FORM, GYP>), grid, dim3(256), 0, s, esk, R, R2,
                        loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt, B, (int)nsplit);
   else
-    hipLaunchKernelGGL((k_chain_rows<1, false, FORM>), grid, dim3(256), 0, s, esk, R, R2,
+    hipLaunchKernelGGL((k_chain_rows<1, false, FORM, GYP>), grid, dim3(256), 0, s, esk, R, R2,
                        loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt, B, (int)nsplit);
 }
 
@@ -464,10 +552,22 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
                         const double* loss64, const float* x, const float* y,
                         const float* gl, float* gx, float* gy, int64_t B, int64_t N,
                         int64_t M, int64_t D, int64_t S, float* part, unsigned* cnt_rows,
-                        unsigned* cnt_cols, hipStream_t s) {
+                        unsigned* cnt_cols, bool keep_e, hipStream_t s) {
   const int nb = (int)((N + 63) / 64);
   const unsigned pr = (unsigned)chain_splits_rows(B, N, M);
   const unsigned pc = (unsigned)chain_splits_cols(B, N, M);
+  if (gy && !keep_e && chain_gy_fits(M, D, S)) {
+    // One row pass makes dx and the bands' shares of dy (in place of E);
+    // a short pass adds the shares up.
+    launch_rows<1, true, true>(B, pr, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, 0,
+                               part, cnt_rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    TimedLaunch timed_("chain_gy", s);
+    hipLaunchKernelGGL(k_chain_gy, dim3((unsigned)((B * M * D + 255) / 256)), dim3(256), 0, s,
+                       esk, y, gl, gy, B, M, D, nb);
+    return hipGetLastError();
+  }
   // Row pass(es): the first forms E; later D slices read it back.
   for (int64_t d0 = 0; d0 < D; d0 += 128) {
     if (d0 > 0 && !gx) break;

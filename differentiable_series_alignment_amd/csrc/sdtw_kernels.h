@@ -125,6 +125,9 @@ hipError_t launch_fill_u32(unsigned* p, int64_t n, unsigned v, hipStream_t s);
 // Chain rule of the unfused backward.  The row pass forms E = 2^(Xnm-X-T')
 // from R and R2 into `esk` (the distance array, no longer needed) and, if
 // gx is given, writes dx; the column pass reads E from `esk` and writes dy.
+// With D <= 64 and E not wanted afterwards (keep_e false) the row pass
+// writes the bands' shares of dy into `esk` instead and a short pass adds
+// them up.
 // Small problems split each sum over several workgroups: `part` holds
 // chain_part_floats() floats of partial sums and the counters (B*nbands for
 // the rows, B*ceil(M/64) for the columns) start at zero and are left at zero.
@@ -135,6 +138,6 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
                         const double* loss64, const float* x, const float* y,
                         const float* gl, float* gx, float* gy, int64_t B, int64_t N,
                         int64_t M, int64_t D, int64_t S, float* part, unsigned* cnt_rows,
-                        unsigned* cnt_cols, hipStream_t s);
+                        unsigned* cnt_cols, bool keep_e, hipStream_t s);
 
 }  // namespace sdtw

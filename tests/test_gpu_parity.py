@@ -415,11 +415,45 @@ def test_abi_backward_repeatable(S):
     assert torch.isfinite(outs[0][2]).all()
 
 
-def test_launch_timing_records_each_kernel(S):
-    """sdtw_timing brackets every launch of a forward+backward with events on
-    the call's stream and reports them by name, in launch order."""
+def test_unfused_gradient_paths_agree(S):
+    """Up to D = 64 dy comes from per-band shares made by the row pass; with
+    the alignment matrix requested it comes from the column pass over E.
+    Asking for dy alone gives bitwise the dy of a call that asks for both."""
     from differentiable_series_alignment_amd import _lib as L
-    x, y = pair_batch(2, 100, 90, 8, seed=12)
+    B, N, M, D = 3, 300, 170, 16
+    x, y = pair_batch(B, N, M, D, seed=21)
+    xd, yd = x.to(DEV), y.to(DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    nb = L.sdtw_workspace_bytes(B, N, M, D, L.SDTW_MODE_UNFUSED)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    loss = torch.empty(B, device=DEV)
+    gl = torch.full((B,), 0.5, device=DEV)
+    L.check(L.sdtw_forward(xd.data_ptr(), yd.data_ptr(), B, N, M, D, 0.9, 0, ws.data_ptr(),
+                           nb, loss.data_ptr(), s), "sdtw_forward")
+    outs = []
+    for want_x, want_e in ((True, False), (False, False), (True, True)):
+        gx = torch.zeros_like(xd)
+        gy = torch.zeros_like(yd)
+        E = torch.empty(B, N, M, device=DEV) if want_e else None
+        L.check(L.sdtw_backward(xd.data_ptr(), yd.data_ptr(), B, N, M, D, 0.9, 0,
+                                ws.data_ptr(), nb, gl.data_ptr(),
+                                gx.data_ptr() if want_x else None, gy.data_ptr(),
+                                E.data_ptr() if want_e else None, s), "sdtw_backward")
+        outs.append((gx, gy))
+    torch.testing.assert_close(outs[1][1], outs[0][1], rtol=0, atol=0)
+    torch.testing.assert_close(outs[2][0], outs[0][0], rtol=0, atol=0)
+    torch.testing.assert_close(outs[2][1], outs[0][1], rtol=1e-4, atol=1e-6)
+
+
+@pytest.mark.parametrize("D,chain", [(8, ["chain_rows", "chain_gy"]),
+                                     (100, ["chain_rows", "chain_cols"])])
+def test_launch_timing_records_each_kernel(S, D, chain):
+    """sdtw_timing brackets every launch of a forward+backward with events on
+    the call's stream and reports them by name, in launch order.  Up to
+    D = 64 the row pass also makes the bands' shares of dy, which a short
+    pass adds up; beyond, a column pass reads E."""
+    from differentiable_series_alignment_amd import _lib as L
+    x, y = pair_batch(2, 100, 90, D, seed=12)
     xd = x.to(DEV).requires_grad_(True)
     yd = y.to(DEV).requires_grad_(True)
     L.sdtw_timing(True)
@@ -429,7 +463,7 @@ def test_launch_timing_records_each_kernel(S):
     finally:
         L.sdtw_timing(False)
     names = [n for n, _ in recs]
-    assert names == ["dist_skew", "dp_both", "chain_rows", "chain_cols"], names
+    assert names == ["dist_skew", "dp_both"] + chain, names
     assert all(t > 0 for _, t in recs)
 
 
