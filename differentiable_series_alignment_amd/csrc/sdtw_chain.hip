@@ -507,6 +507,20 @@ bool chain_gy_fits(int64_t M, int64_t D, int64_t S) {
   return D <= 64 && M * (D + 1) <= S * 64;
 }
 
+// Row-pass splits when it makes the dy shares: up to kChainFillGy
+// workgroups (at least two column blocks each), as far as their partial
+// sums fit in the distance region after the shares.
+constexpr int64_t kChainFillGy = 1024;
+int chain_splits_rows_gy(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S) {
+  const int64_t nb = (N + 63) / 64, groups = B * nb, nblk = (M + 31) / 32;
+  int64_t p = (kChainFillGy + groups - 1) / groups;
+  p = p < nblk / 2 ? p : nblk / 2;
+  p = p < 1 ? 1 : (p > 8 ? 8 : p);
+  const int64_t room = groups * (S * 64 - M * (D + 1));
+  while (p > 1 && groups * p * 17 * 256 > room) --p;
+  return (int)p;
+}
+
 // Workgroups per band (dx) or per 64-column block (dy): a launch with fewer
 // groups than the GPU has CUs splits each group's reduction range so that it
 // fills them, keeping at least two column blocks (or bands) per workgroup.
@@ -558,9 +572,12 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
   const unsigned pc = (unsigned)chain_splits_cols(B, N, M);
   if (gy && !keep_e && chain_gy_fits(M, D, S)) {
     // One row pass makes dx and the bands' shares of dy (in place of E);
-    // a short pass adds the shares up.
-    launch_rows<1, true, true>(B, pr, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, 0,
-                               part, cnt_rows);
+    // a short pass adds the shares up.  Its split partial sums go after the
+    // shares.
+    const unsigned pg = (unsigned)chain_splits_rows_gy(B, N, M, D, S);
+    float* gpart = esk + B * nb * M * (D + 1);
+    launch_rows<1, true, true>(B, pg, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, 0,
+                               gpart, cnt_rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TimedLaunch timed_("chain_gy", s);
