@@ -54,8 +54,8 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_dp_common.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h"],
-    "sha256": "fac6c14e11c9dbc79fe6043c4edca8e44f479798173aca1a2e122cfb2e6b213f",
-    "fetch_kib": 37418, "fetch_scale": 2.0,
+    "sha256": "558eae182eeb95a6196e58fd08919697a5097d2fddeb0e2a9d6db5583be75cf1",
+    "fetch_kib": 37431, "fetch_scale": 2.0,
     "write_kib": 147856, "write_scale": 1.0,
 }
 
