@@ -14,7 +14,7 @@
 // lanes: A[r][k] sits in lane r + 16k, B[k][c] in lane c + 16k; the
 // accumulator's element (4*e + l/16, l%16) sits in lane l, register e
 // (checked on the hardware).  The contraction index k of step s is
-// d = 4s + k.  The x and y rows pass through LDS in slabs of 16 features
+// d = 4s + k.  The x and y rows pass through LDS in slabs of 16 features,
 // (the next slab is fetched into registers while the current one feeds the
 // MFMAs); the finished block is staged in LDS (over the slabs) and leaves
 // either row-major or in the band-step layout of the dynamic programme.
@@ -27,7 +27,8 @@ constexpr int kDT = 128;                 // output block edge per workgroup
 constexpr int kDKC = 16;                 // features per slab
 constexpr int kDPK = kDKC + 4;           // slab row pitch (floats)
 constexpr int kDTP = kDT + 16;           // output block row pitch (floats)
-constexpr int kDLds = (2 * kDT * kDPK > kDT * kDTP ? 2 * kDT * kDPK : kDT * kDTP);
+constexpr int kDSlab = 2 * kDT * kDPK;   // x and y rows of one slab (floats)
+constexpr int kDLds = (2 * kDSlab > kDT * kDTP ? 2 * kDSlab : kDT * kDTP);
 
 template <bool SKEW>
 __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
@@ -44,9 +45,9 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
     const int64_t stride = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
     for (int64_t k = wg * 256 + threadIdx.x; k < nzero; k += stride) zero[k] = 0u;
   }
-  float* const xs = smem;                 // [kDT][kDPK] x rows of the block
-  float* const ys = smem + kDT * kDPK;    // [kDT][kDPK] y rows of the block
-  float* const tile = smem;               // [kDT][kDTP] finished block (after the slabs)
+  // Two slab buffers, each [kDT][kDPK] x rows then [kDT][kDPK] y rows; the
+  // finished block [kDT][kDTP] overlays them at the end.
+  float* const tile = smem;
   const int l = lane_id();
   const int w = threadIdx.x >> 6;
   const int wr = w >> 1, wc = w & 1;      // this wave's 64x64 quarter
@@ -74,7 +75,9 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
       sy[q] = (dok && gj < M) ? vy : 0.f;
     }
   };
-  auto stash = [&]() {
+  auto stash = [&](int buf) {
+    float* xs = smem + buf * kDSlab;
+    float* ys = xs + kDT * kDPK;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       const int e = (int)threadIdx.x + 256 * q;
@@ -89,16 +92,19 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (v4d){0.0, 0.0, 0.0, 0.0};
   double nx[4] = {0, 0, 0, 0}, ny[4] = {0, 0, 0, 0};
-  const float* xa = xs + (wr * 64 + r) * kDPK + kk;
-  const float* yb_l = ys + (wc * 64 + r) * kDPK + kk;
   const int64_t steps = (D + 3) / 4;
+  // Double-buffered slabs: slab k is read from buffer k & 1 while slab k+1
+  // is written into the other one, and slab k+2 is fetched into registers;
+  // one barrier per slab.
+  const int nslab = (int)((D + kDKC - 1) / kDKC);
   fetch(0);
-  for (int64_t k0 = 0; k0 < D; k0 += kDKC) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (k0 + kDKC < D) fetch(k0 + kDKC);
-    const int64_t s0 = k0 / 4;
+  stash(0);
+  if (nslab > 1) fetch(kDKC);
+  __syncthreads();
+  for (int k = 0; k < nslab; ++k) {
+    const float* xa = smem + (k & 1) * kDSlab + (wr * 64 + r) * kDPK + kk;
+    const float* yb_l = smem + (k & 1) * kDSlab + kDT * kDPK + (wc * 64 + r) * kDPK + kk;
+    const int64_t s0 = (int64_t)k * (kDKC / 4);
     const int ns = (int)(steps - s0 < kDKC / 4 ? steps - s0 : kDKC / 4);
     for (int sl = 0; sl < ns; ++sl) {  // step s = s0 + sl, feature d = 4s + kk
       double a[4], bv[4];
@@ -115,6 +121,9 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bv[j], acc[i][j], 0, 0, 0);
     }
+    if (k + 1 < nslab) stash((k + 1) & 1);
+    if (k + 2 < nslab) fetch((int64_t)(k + 2) * kDKC);
+    __syncthreads();
   }
   // Complete the norms over the four k lane groups (lanes r, r+16, r+32, r+48).
 #pragma unroll
@@ -125,8 +134,7 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
     ny[i] += __shfl_xor(ny[i], 32, 64);
   }
   // Dist = max(0, |x|^2 + |y|^2 - 2 x.y), rounded once to fp32, into the
-  // LDS block (which now overlays the slabs).
-  __syncthreads();
+  // LDS block (which now overlays the slabs; the loop ended on a barrier).
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
