@@ -278,6 +278,7 @@ def test_fused_matches_unfused(S, N, M, D):
     (1, 513, 40, 3),       # 9 bands, groups of 3, one row in the top band
     (2, 1100, 70, 8),      # 18 bands, groups of 5
     (2, 130, 1100, 16),    # long M
+    (2, 2100, 300, 32),    # 33 bands, groups of 6 (last group of 3)
 ])
 def test_checkpoint_matches_fused(S, B, N, M, D):
     """Checkpointed training recomputes the forward state group by group of
