@@ -22,8 +22,10 @@
  *   SDTW_MODE_UNFUSED  materialises Dist (fp32, B x N x M) in the workspace;
  *                      the forward runs the forward and the reverse sweep of
  *                      the dynamic programme at once and keeps both states
- *                      (fp64); the backward forms E from them in place of
- *                      Dist and applies the chain rule.
+ *                      (fp64); the backward forms E from them and applies
+ *                      the chain rule, using the distance region for E (or,
+ *                      for D <= 64 without an alignment output, for each
+ *                      64-row band's share of grad_y).
  *   SDTW_MODE_FUSED    recomputes distances from x and y inside the dynamic
  *                      programme; no B x N x M distance or E tensor exists.
  *                      Supports D <= 256 (sdtw_workspace_bytes returns 0 and
@@ -132,12 +134,14 @@ int sdtw_forward(const float *x, const float *y, int64_t B, int64_t N,
  * workspace must be as sdtw_forward left it for the same arguments.
  * grad_x ([B,N,D]) and grad_y ([B,M,D]) are written (not accumulated); either
  * may be NULL to skip it.  align ([B,N,M] fp32), if not NULL, receives E
- * (both modes; in fused mode it is the only B x N x M array written).  The
- * backward never reads the distances again (unfused mode replaces them with
- * E, formed from the two sweeps' states), so it may be repeated on one
- * forward in both modes; with every output NULL it does nothing.  In fused
- * mode grad_y is accumulated with atomic adds across row bands, so its last
- * bits may differ from run to run. */
+ * (every training mode; in the fused and checkpointed modes it is the only
+ * B x N x M array written).  The backward never reads the distances again
+ * (unfused mode overwrites them, with E formed from the two sweeps' states
+ * or with the bands' shares of grad_y), so it may be repeated on one forward
+ * in every training mode; with every output NULL it does nothing.  In the
+ * fused and checkpointed modes grad_y is accumulated with atomic adds across
+ * row bands, so its last bits may differ from run to run.  Inference mode:
+ * SDTW_ERR_UNSUPPORTED. */
 int sdtw_backward(const float *x, const float *y, int64_t B, int64_t N,
                   int64_t M, int64_t D, float gamma, int mode, void *workspace,
                   size_t workspace_bytes, const float *grad_loss,
