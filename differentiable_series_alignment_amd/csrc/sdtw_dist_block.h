@@ -138,21 +138,43 @@ __device__ __forceinline__ void dist_block(const float* __restrict__ x,
   if (SKEW) {
     // Band bb of the block (64 rows, columns bj0 .. bj0+127) covers steps
     // bj0 + p, p = 0..190, of that band; lane l of step p holds column
-    // bj0 + p - l.  Each store writes one step's contiguous lane run.
+    // bj0 + p - l.  Per pass, thread t moves lanes l0..l0+3 (l0 = 4(t%16))
+    // of step p = 16*pass + t/16: one 16-byte store when all four cells lie
+    // in the block, single words at its diagonal edges.  A wave writes four
+    // whole steps (1 KiB) per pass; the LDS reads of a pass do not wait on
+    // the stores of the previous one.
+    const int t = (int)threadIdx.x;
+    const int l0 = 4 * (t & 15);
+    const int cmax = (int)(M - bj0 < kDT ? M - bj0 : kDT);   // block columns in the grid
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       const int64_t band = (bi0 >> 6) + bb;
       if (band >= nbands) break;
-      float* bandp = dist + ((b * nbands + band) * S + bj0 + kSkewOff) * 64;
-      const float* trow = tile + (64 * bb + l) * kDTP;
-      for (int p = w; p < kDT + 63; p += 4) {
-        const int cl = p - l;
-        if (cl >= 0 && cl < kDT && bj0 + cl < M) {
-          if (COH)
-            __hip_atomic_store(&bandp[(int64_t)p * 64 + l], trow[cl], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          else
-            bandp[(int64_t)p * 64 + l] = trow[cl];
+      float* bandp = dist + ((b * nbands + band) * S + bj0 + kSkewOff) * 64 + l0;
+      const float* tb = tile + (64 * bb + l0) * kDTP;
+#pragma unroll 4
+      for (int pass = 0; pass < (kDT + 63 + 15) / 16; ++pass) {
+        const int p = 16 * pass + (t >> 4);
+        float v[4];
+        bool ok[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int cl = p - l0 - j;
+          ok[j] = cl >= 0 && cl < cmax;
+          v[j] = tb[j * kDTP + (ok[j] ? cl : 0)];
+        }
+        float* dst = bandp + (int64_t)p * 64;
+        if (COH) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (ok[j])
+              __hip_atomic_store(dst + j, v[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (ok[0] && ok[3]) {   // the valid lanes of a step are contiguous
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (ok[j]) dst[j] = v[j];
         }
       }
     }
