@@ -20,6 +20,11 @@ namespace sdtw {
 
 constexpr int kRingSteps = 128;
 constexpr int kRingPitch = 65;
+// Rows past the ring's end that mirror its first rows, so a run of up to
+// kRingPad + 1 consecutive steps starting anywhere in the ring can be read
+// at one base address plus constant offsets (no wrap-around per read).
+constexpr int kRingPad = 32;
+constexpr int kRingFloats = (kRingSteps + kRingPad) * kRingPitch;
 
 // Copy band steps [s0, s0 + 32) (relative to the band's first column step)
 // between global memory, registers and the LDS ring; 256 threads x 8 floats.
@@ -38,6 +43,7 @@ struct Stage32 {
       v[4 * k + 3] = q[3];
     }
   }
+  template <bool MIRROR = true>
   __device__ __forceinline__ void store(float* ring, int64_t s0) const {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -45,6 +51,11 @@ struct Stage32 {
       const int slot = (int)((s0 + e / 64) & (kRingSteps - 1));
 #pragma unroll
       for (int q = 0; q < 4; ++q) ring[slot * kRingPitch + (e & 63) + q] = v[4 * k + q];
+      if (MIRROR && slot < kRingPad) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ring[(slot + kRingSteps) * kRingPitch + (e & 63) + q] = v[4 * k + q];
+      }
     }
   }
 };
@@ -87,6 +98,10 @@ struct StageXT {
       for (int j = 0; j < 4; ++j) {
         q[j] = align_entry(xnm, xv[4 * k + j], tv[4 * k + j]);
         ring[slot * kRingPitch + (e & 63) + j] = q[j];
+      }
+      if (slot < kRingPad) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ring[(slot + kRingSteps) * kRingPitch + (e & 63) + j] = q[j];
       }
       if (EOUT) __builtin_nontemporal_store(q, reinterpret_cast<v4f*>(ebp + off[k]));
     }
@@ -197,7 +212,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
                                                     float* __restrict__ part,
                                                     unsigned* __restrict__ cnt,
                                                     int64_t nb_pairs, int nsplit) {
-  __shared__ float ring[kRingSteps * kRingPitch];
+  __shared__ float ring[kRingFloats];
   WorkItem it;
   if (!xcd_item(nbands, nb_pairs, nsplit, &it)) return;
   const int64_t b = it.i1, band = it.i0;
@@ -281,11 +296,16 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
       if (GX) load_y(j0 + 32, yn);
     }
     if (GX) {
+      // E[row, j0 + 2s + h] for s = 0..15: ring rows base + 2s (the pad
+      // mirrors the wrap), all read before the first product.
+      const float* ea = ring + (int)((j0 + h + lr) & (kRingSteps - 1)) * kRingPitch + lr;
+      float ev[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) ev[s] = ea[s * 2 * kRingPitch];
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const int64_t j = j0 + 2 * s + h;
-        const float a =
-            (row_ok && j < M) ? ring[(int)((j + lr) & (kRingSteps - 1)) * kRingPitch + lr] : 0.f;
+        const float a = (row_ok && j < M) ? ev[s] : 0.f;
         rsum += a;
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
@@ -300,12 +320,15 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
 #pragma unroll
       for (int e = 0; e < 16; ++e) gacc[e] = 0.f;
       const int64_t j = j0 + r;
+      const int lrow0 = 32 * grh + h;
+      const float* eg = ring + (int)((j + lrow0) & (kRingSteps - 1)) * kRingPitch + lrow0;
+      float ev[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) ev[s] = eg[s * (2 * kRingPitch + 2)];
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const int lrow = 32 * grh + 2 * s + h;
-        const float a = (band * 64 + lrow < N && j < M)
-                            ? ring[(int)((j + lrow) & (kRingSteps - 1)) * kRingPitch + lrow]
-                            : 0.f;
+        const int lrow = lrow0 + 2 * s;
+        const float a = (band * 64 + lrow < N && j < M) ? ev[s] : 0.f;
         gcs += a;
         gacc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xg[s], gacc, 0, 0, 0);
       }
@@ -432,15 +455,20 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
 
   for (int64_t band = bb0; band < bb1; ++band) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) win[k].store(ring, 32 * k);
+    for (int k = 0; k < 4; ++k) win[k].template store<false>(ring, 32 * k);
     __syncthreads();
     const bool more = band + 1 < bb1;
     if (more) load_band(band + 1, nxt, xn);
+    // Steps jl + lr of rows lr = 2s + h (no wrap: jl + lr < 128), all read
+    // before the first product.
+    float ev[32];
+#pragma unroll
+    for (int s = 0; s < 32; ++s) ev[s] = ring[(jl + 2 * s + h) * kRingPitch + 2 * s + h];
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
       const int lr = 2 * s + h;
       const bool ok = col_ok && band * 64 + lr < N;
-      const float a = ok ? ring[(jl + lr) * kRingPitch + lr] : 0.f;
+      const float a = ok ? ev[s] : 0.f;
       csum += a;
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
