@@ -55,7 +55,7 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h"],
     "sha256": "558eae182eeb95a6196e58fd08919697a5097d2fddeb0e2a9d6db5583be75cf1",
-    "fetch_kib": 37431, "fetch_scale": 2.0,
+    "fetch_kib": 37390, "fetch_scale": 2.0,
     "write_kib": 147856, "write_scale": 1.0,
 }
 
