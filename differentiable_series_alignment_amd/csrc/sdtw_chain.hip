@@ -63,7 +63,9 @@ struct Stage32 {
 // The same 32-step window, formed from the two sweeps' states instead:
 // E = 2^(Xnm - X - T') for each cell, written both to the LDS ring and to
 // the band-step E array (the distance array, no longer needed) for the
-// column pass and the optional alignment output.
+// column pass and the optional alignment output.  Cells outside the grid
+// (rows from rows_left on, columns outside 0..M-1) are stored as 0, so the
+// products and sums over the ring need no masks.
 typedef double v2d __attribute__((ext_vector_type(2)));
 struct StageXT {
   double xv[8], tv[8];
@@ -88,15 +90,19 @@ struct StageXT {
     }
   }
   template <bool EOUT = true>
-  __device__ __forceinline__ void store(float* ring, float* ebp, int64_t s0, double xnm) const {
+  __device__ __forceinline__ void store(float* ring, float* ebp, int64_t s0, double xnm,
+                                        int rows_left, int64_t M) const {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int e = (int)threadIdx.x * 4 + 1024 * k;
       const int slot = (int)((s0 + e / 64) & (kRingSteps - 1));
+      const int64_t col0 = s0 + e / 64 - (e & 63);   // column of lane (e & 63)
       v4f q;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        q[j] = align_entry(xnm, xv[4 * k + j], tv[4 * k + j]);
+        const int64_t c = col0 - j;
+        const bool ok = (e & 63) + j < rows_left && c >= 0 && c < M;
+        q[j] = ok ? align_entry(xnm, xv[4 * k + j], tv[4 * k + j]) : 0.f;
         ring[slot * kRingPitch + (e & 63) + j] = q[j];
       }
       if (slot < kRingPad) {
@@ -214,15 +220,18 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
                                                     int64_t nb_pairs, int nsplit) {
   __shared__ float ring[kRingFloats];
   WorkItem it;
-  if (!xcd_item(nbands, nb_pairs, nsplit, &it)) return;
-  const int64_t b = it.i1, band = it.i0;
-  const int p = (int)it.i2;
+  // The split parts of a band are consecutive items (same XCD, dispatched
+  // together), so the window steps they both read come from one L2.
+  if (!xcd_item(nsplit, nbands, nb_pairs, &it)) return;
+  const int64_t b = it.i2, band = it.i1;
+  const int p = (int)it.i0;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int r = l & 31, h = l >> 5;
   const int rt = w & 1, dsel = w >> 1;
   const int lr = 32 * rt + r;
   const int64_t row = band * 64 + lr;
   const bool row_ok = row < N;
+  const int rows_left = (int)(N - band * 64 < 64 ? N - band * 64 : 64);
   const int64_t boff = ((b * nbands + band) * S + kSkewOff) * 64;
   float* bandp = esk + boff;
   const double* xbp = R + boff;
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
   for (int64_t s0 = kb0 * 32; s0 < kb0 * 32 + 96; s0 += 32) {
     if (FORM) {
       sx.load(xbp, tbp, s0, smax);
-      sx.template store<!GYP>(ring, bandp, s0, xnm);
+      sx.template store<!GYP>(ring, bandp, s0, xnm, rows_left, M);
     } else {
       st.load(bandp, s0, smax);
       st.store(ring, s0);
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const int64_t j = j0 + 2 * s + h;
-        const float a = (row_ok && j < M) ? ev[s] : 0.f;
+        const float a = (FORM || (row_ok && j < M)) ? ev[s] : 0.f;   // FORM: masked
         rsum += a;
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
@@ -327,8 +336,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
       for (int s = 0; s < 16; ++s) ev[s] = eg[s * (2 * kRingPitch + 2)];
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const int lrow = lrow0 + 2 * s;
-        const float a = (band * 64 + lrow < N && j < M) ? ev[s] : 0.f;
+        const float a = ev[s];   // cells outside the grid were stored as 0
         gcs += a;
         gacc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xg[s], gacc, 0, 0, 0);
       }
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
     }
     if (more) {
       if (FORM)
-        sx.template store<!GYP>(ring, bandp, j0 + 96, xnm);
+        sx.template store<!GYP>(ring, bandp, j0 + 96, xnm, rows_left, M);
       else
         st.store(ring, j0 + 96);
       if (GX) {
@@ -412,9 +420,9 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
   __shared__ float ring[kRingSteps * kRingPitch];
   const int64_t ncb = (M + 63) / 64;
   WorkItem it;
-  if (!xcd_item(ncb, nb_pairs, nsplit, &it)) return;
-  const int64_t b = it.i1, cb = it.i0, j0 = cb * 64;
-  const int p = (int)it.i2;
+  if (!xcd_item(nsplit, ncb, nb_pairs, &it)) return;
+  const int64_t b = it.i2, cb = it.i1, j0 = cb * 64;
+  const int p = (int)it.i0;
   const int64_t bb0 = (int64_t)p * nbands / nsplit, bb1 = (int64_t)(p + 1) * nbands / nsplit;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int r = l & 31, h = l >> 5;
