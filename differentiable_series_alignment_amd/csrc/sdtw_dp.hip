@@ -176,6 +176,14 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
         a.loss[b] = (float)(v * a.g_ln2);
       }
     }
+    // Next chunk's top entries, read after the count (see above), and ahead
+    // of this chunk's LDS writes so that they return first.  Their slots are
+    // not released yet, so the band above cannot overwrite them.
+    seen_wr = __hip_atomic_load(&wr[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int u = 0; u < kCH; ++u) top[u] = ring[w][(t0 + kCH + u) & (kRingC - 1)];
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     // The top entries of this chunk have been read: release them.
     if (lane == 0) lds_publish(&rd[w], need);
     // Lane 63's cells (row r0+63, columns t0+u-63) go to the row below.
@@ -200,12 +208,6 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
         lds_publish(&wr[w + 1], done <= 0 ? 0u : ((unsigned)done < Mu ? (unsigned)done : Mu));
       }
     }
-    // Next chunk's top entries, read after the count (see above).  Their
-    // slots are not released yet, so the band above cannot overwrite them.
-    seen_wr = __hip_atomic_load(&wr[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-#pragma unroll
-    for (int u = 0; u < kCH; ++u) top[u] = ring[w][(t0 + kCH + u) & (kRingC - 1)];
   };
 
   for (int q = 0; q < qcount; q += 2) {
