@@ -9,8 +9,10 @@
 // inputs within ~1e-13 relative of a rounding midpoint.
 //
 // Work split: a 256-thread workgroup owns a 128x128 block of (i,j) for one
-// pair; each wave owns a 64x64 quarter as 4x4 tiles of
-// v_mfma_f64_16x16x4_f64, i.e. 16 independent accumulation chains.  Operand
+// pair, each wave a 64x64 quarter as 4x4 tiles of v_mfma_f64_16x16x4_f64
+// (16 independent accumulation chains); or a 64x128 block, each wave a
+// 64x32 part as 4x2 tiles (the band-step kernel's choice depends on the
+// grid size, see dist_rows).  Operand
 // lanes: A[r][k] sits in lane r + 16k, B[k][c] in lane c + 16k; the
 // accumulator's element (4*e + l/16, l%16) sits in lane l, register e
 // (checked on the hardware).  The contraction index k of step s is
@@ -22,14 +24,14 @@
 
 namespace sdtw {
 
-template <bool SKEW>
+template <int TR, bool SKEW>
 __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
                                               const float* __restrict__ y,
                                               float* __restrict__ dist,
                                               int64_t N, int64_t M, int64_t D,
                                               int64_t S, int nbands,
                                               unsigned* __restrict__ zero, int64_t nzero) {
-  __shared__ float smem[kDLds];
+  __shared__ float smem[DistTile<TR>::kLds];
   // Words the next kernels of the step expect to find cleared (their
   // control words; a fresh workspace holds garbage), spread over the grid.
   {
@@ -37,8 +39,25 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
     const int64_t stride = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
     for (int64_t k = wg * 256 + threadIdx.x; k < nzero; k += stride) zero[k] = 0u;
   }
-  dist_block<SKEW, false>(x, y, dist, blockIdx.z, (int64_t)blockIdx.y * kDT,
-                          (int64_t)blockIdx.x * kDT, N, M, D, S, nbands, smem);
+  dist_block<TR, SKEW>(x, y, dist, blockIdx.z, (int64_t)blockIdx.y * TR,
+                       (int64_t)blockIdx.x * kDT, N, M, D, S, nbands, smem);
+}
+
+// Block height of the band-step distance kernel.  128-row blocks (two
+// workgroups per CU) are used when they fill the GPU in exactly one round,
+// as at B=32, N=M=512; otherwise 64-row blocks: twice the workgroups, three
+// per CU, so one block's stores drain while others compute, and small
+// batches still spread over every CU.
+static int dist_rows(int64_t B, int64_t N, int64_t M) {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 256;
+    return n;
+  }();
+  const int64_t blocks128 = B * ((N + 127) / 128) * ((M + kDT - 1) / kDT);
+  return (blocks128 > cus && blocks128 <= 2 * (int64_t)cus) ? 128 : 64;
 }
 
 hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
@@ -46,7 +65,7 @@ hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
   dim3 grid((unsigned)((M + kDT - 1) / kDT), (unsigned)((N + kDT - 1) / kDT), (unsigned)B);
   {
     TimedLaunch timed_("dist", stream);
-    hipLaunchKernelGGL(k_dist<false>, grid, dim3(256), 0, stream, x, y, dist, N, M, D,
+    hipLaunchKernelGGL((k_dist<128, false>), grid, dim3(256), 0, stream, x, y, dist, N, M, D,
                        (int64_t)0, 0, (unsigned*)nullptr, (int64_t)0);
   }
   return hipGetLastError();
@@ -55,11 +74,16 @@ hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
 hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t B,
                             int64_t N, int64_t M, int64_t D, int64_t S, unsigned* zero,
                             int64_t nzero, hipStream_t stream) {
-  dim3 grid((unsigned)((M + kDT - 1) / kDT), (unsigned)((N + kDT - 1) / kDT), (unsigned)B);
+  const int tr = dist_rows(B, N, M);
+  dim3 grid((unsigned)((M + kDT - 1) / kDT), (unsigned)((N + tr - 1) / tr), (unsigned)B);
   {
     TimedLaunch timed_("dist_skew", stream);
-    hipLaunchKernelGGL(k_dist<true>, grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S,
-                       (int)((N + 63) / 64), zero, nzero);
+    if (tr == 64)
+      hipLaunchKernelGGL((k_dist<64, true>), grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S,
+                         (int)((N + 63) / 64), zero, nzero);
+    else
+      hipLaunchKernelGGL((k_dist<128, true>), grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S,
+                         (int)((N + 63) / 64), zero, nzero);
   }
   return hipGetLastError();
 }

@@ -1,121 +1,137 @@
-// Squared Euclidean distance block on fp64 MFMA (gfx950), shared by the
-// distance kernel and the distance workers of the small-grid sweep kernel.
-// See sdtw_dist.hip for the method; here only the block routine.
+// Squared Euclidean distance block on fp64 MFMA (gfx950): the routine the
+// distance kernels run per block.  See sdtw_dist.hip for the method.
 #pragma once
 #include "sdtw_device.h"
 #include "sdtw_kernels.h"
 
 namespace sdtw {
 
-constexpr int kDT = 128;                 // output block edge per workgroup
+constexpr int kDT = 128;                 // output block width (columns)
 constexpr int kDKC = 16;                 // features per slab
 constexpr int kDPK = kDKC + 4;           // slab row pitch (floats)
 constexpr int kDTP = kDT + 16;           // output block row pitch (floats)
-constexpr int kDSlab = 2 * kDT * kDPK;   // x and y rows of one slab (floats)
-constexpr int kDLds = (2 * kDSlab > kDT * kDTP ? 2 * kDSlab : kDT * kDTP);
 
-// One 128 x 128 block (rows bi0.., columns bj0..) of pair b.  Threads 0..255
-// of the workgroup compute; any further threads only take part in the
-// barriers.  SKEW: band-step output (else row-major [B,N,M]); COH: the
-// stores are device-coherent (they bypass the per-XCD caches, for readers
-// in the same launch).  smem: kDLds floats.
-template <bool SKEW, bool COH>
+// LDS floats of a block of TR rows (64 or 128) x kDT columns: two slab
+// buffers of TR x rows and kDT y rows each, which the finished block
+// [TR][kDTP] overlays at the end.
+template <int TR>
+struct DistTile {
+  static constexpr int kSlab = (TR + kDT) * kDPK;
+  static constexpr int kLds = (2 * kSlab > TR * kDTP ? 2 * kSlab : TR * kDTP);
+};
+
+// One TR x 128 block (rows bi0.., columns bj0..) of pair b, computed by a
+// 256-thread workgroup.  The four waves split the block into TR/64 x 4/(TR/64)
+// parts of 64 rows each (64 x 64 for TR = 128, 64 x 32 for TR = 64).
+// SKEW: band-step output (else row-major [B,N,M]).  smem: DistTile<TR>::kLds
+// floats.
+template <int TR, bool SKEW>
 __device__ __forceinline__ void dist_block(const float* __restrict__ x,
                                            const float* __restrict__ y,
                                            float* __restrict__ dist, int64_t b, int64_t bi0,
                                            int64_t bj0, int64_t N, int64_t M, int64_t D,
                                            int64_t S, int nbands, float* smem) {
-  const bool act = threadIdx.x < 256;
-  // Two slab buffers, each [kDT][kDPK] x rows then [kDT][kDPK] y rows; the
-  // finished block [kDT][kDTP] overlays them at the end.
+  static_assert(TR == 64 || TR == 128, "block height");
+  constexpr int WR = TR / 64;            // wave rows
+  constexpr int WC = 4 / WR;             // wave columns
+  constexpr int CW = kDT / WC;           // columns per wave
+  constexpr int NJ = CW / 16;            // 16-column tiles per wave
+  constexpr int kSlab = DistTile<TR>::kSlab;
   float* const tile = smem;
   const int l = lane_id();
   const int w = threadIdx.x >> 6;
-  const int wr = w >> 1, wc = w & 1;      // this wave's 64x64 quarter
+  const int wr = w / WC, wc = w % WC;    // this wave's part
   const int r = l & 15, kk = l >> 4;
   const float* xb = x + b * N * D;
   const float* yb = y + b * M * D;
 
-  // Staging: thread t moves elements t + 256q (q < 8) of each 128 x 16
-  // slab; rows outside the grid and features >= D are stored as zeros.
-  constexpr int kQ = kDT * kDKC / 256;
-  float sx[kQ], sy[kQ];
+  // Staging: thread t moves elements t + 256q of the TR x 16 x slab and of
+  // the 128 x 16 y slab; rows outside the grid and features >= D are stored
+  // as zeros.
+  constexpr int kQX = TR * kDKC / 256, kQY = kDT * kDKC / 256;
+  float sx[kQX], sy[kQY];
   auto fetch = [&](int64_t k0) {
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
+    for (int q = 0; q < kQY; ++q) {
       const int e = (int)threadIdx.x + 256 * q;
       const int row = e / kDKC, col = e % kDKC;
       const int64_t d = k0 + col;
-      const int64_t gi = bi0 + row, gj = bj0 + row;
       const bool dok = d < D;
-      const float vx = xb[(gi < N ? gi : 0) * D + (dok ? d : 0)];
+      if (q < kQX) {
+        const int64_t gi = bi0 + row;
+        const float vx = xb[(gi < N ? gi : 0) * D + (dok ? d : 0)];
+        sx[q < kQX ? q : 0] = (dok && gi < N) ? vx : 0.f;
+      }
+      const int64_t gj = bj0 + row;
       const float vy = yb[(gj < M ? gj : 0) * D + (dok ? d : 0)];
-      sx[q] = (dok && gi < N) ? vx : 0.f;
       sy[q] = (dok && gj < M) ? vy : 0.f;
     }
   };
   auto stash = [&](int buf) {
-    float* xs = smem + buf * kDSlab;
-    float* ys = xs + kDT * kDPK;
+    float* xs = smem + buf * kSlab;
+    float* ys = xs + TR * kDPK;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
+    for (int q = 0; q < kQY; ++q) {
       const int e = (int)threadIdx.x + 256 * q;
-      xs[(e / kDKC) * kDPK + e % kDKC] = sx[q];
+      if (q < kQX) xs[(e / kDKC) * kDPK + e % kDKC] = sx[q < kQX ? q : 0];
       ys[(e / kDKC) * kDPK + e % kDKC] = sy[q];
     }
   };
 
-  v4d acc[4][4];
+  v4d acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (v4d){0.0, 0.0, 0.0, 0.0};
-  double nx[4] = {0, 0, 0, 0}, ny[4] = {0, 0, 0, 0};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = (v4d){0.0, 0.0, 0.0, 0.0};
+  double nx[4] = {0, 0, 0, 0}, ny[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) ny[j] = 0.0;
   const int64_t steps = (D + 3) / 4;
   // Double-buffered slabs: slab k is read from buffer k & 1 while slab k+1
   // is written into the other one, and slab k+2 is fetched into registers;
   // one barrier per slab.
   const int nslab = (int)((D + kDKC - 1) / kDKC);
-  if (act) {
-    fetch(0);
-    stash(0);
-    if (nslab > 1) fetch(kDKC);
-  }
+  fetch(0);
+  stash(0);
+  if (nslab > 1) fetch(kDKC);
   __syncthreads();
   for (int k = 0; k < nslab; ++k) {
-    if (act) {
-    const float* xa = smem + (k & 1) * kDSlab + (wr * 64 + r) * kDPK + kk;
-    const float* yb_l = smem + (k & 1) * kDSlab + kDT * kDPK + (wc * 64 + r) * kDPK + kk;
+    const float* xa = smem + (k & 1) * kSlab + (wr * 64 + r) * kDPK + kk;
+    const float* yb_l = smem + (k & 1) * kSlab + TR * kDPK + (wc * CW + r) * kDPK + kk;
     const int64_t s0 = (int64_t)k * (kDKC / 4);
     const int ns = (int)(steps - s0 < kDKC / 4 ? steps - s0 : kDKC / 4);
     for (int sl = 0; sl < ns; ++sl) {  // step s = s0 + sl, feature d = 4s + kk
-      double a[4], bv[4];
+      double a[4], bv[NJ];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         a[i] = (double)xa[16 * i * kDPK + 4 * sl];
-        bv[i] = (double)yb_l[16 * i * kDPK + 4 * sl];
         nx[i] = fma(a[i], a[i], nx[i]);
-        ny[i] = fma(bv[i], bv[i], ny[i]);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        bv[j] = (double)yb_l[16 * j * kDPK + 4 * sl];
+        ny[j] = fma(bv[j], bv[j], ny[j]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bv[j], acc[i][j], 0, 0, 0);
     }
     if (k + 1 < nslab) stash((k + 1) & 1);
     if (k + 2 < nslab) fetch((int64_t)(k + 2) * kDKC);
-    }
     __syncthreads();
   }
-  if (act) {
   // Complete the norms over the four k lane groups (lanes r, r+16, r+32, r+48).
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     nx[i] += __shfl_xor(nx[i], 16, 64);
     nx[i] += __shfl_xor(nx[i], 32, 64);
-    ny[i] += __shfl_xor(ny[i], 16, 64);
-    ny[i] += __shfl_xor(ny[i], 32, 64);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    ny[j] += __shfl_xor(ny[j], 16, 64);
+    ny[j] += __shfl_xor(ny[j], 32, 64);
   }
   // Dist = max(0, |x|^2 + |y|^2 - 2 x.y), rounded once to fp32, into the
   // LDS block (which now overlays the slabs; the loop ended on a barrier).
@@ -126,15 +142,13 @@ __device__ __forceinline__ void dist_block(const float* __restrict__ x,
       const int rl = 4 * e + kk;
       const double nxr = __shfl(nx[i], rl, 64);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         double v = nxr + ny[j] - 2.0 * acc[i][j][e];
         v = v > 0.0 ? v : 0.0;
-        tile[(wr * 64 + 16 * i + rl) * kDTP + wc * 64 + 16 * j + r] = (float)v;
+        tile[(wr * 64 + 16 * i + rl) * kDTP + wc * CW + 16 * j + r] = (float)v;
       }
     }
-  }
   __syncthreads();
-  if (!act) return;
   if (SKEW) {
     // Band bb of the block (64 rows, columns bj0 .. bj0+127) covers steps
     // bj0 + p, p = 0..190, of that band; lane l of step p holds column
@@ -147,7 +161,7 @@ __device__ __forceinline__ void dist_block(const float* __restrict__ x,
     const int l0 = 4 * (t & 15);
     const int cmax = (int)(M - bj0 < kDT ? M - bj0 : kDT);   // block columns in the grid
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
+    for (int bb = 0; bb < WR; ++bb) {
       const int64_t band = (bi0 >> 6) + bb;
       if (band >= nbands) break;
       float* bandp = dist + ((b * nbands + band) * S + bj0 + kSkewOff) * 64 + l0;
@@ -164,12 +178,7 @@ __device__ __forceinline__ void dist_block(const float* __restrict__ x,
           v[j] = tb[j * kDTP + (ok[j] ? cl : 0)];
         }
         float* dst = bandp + (int64_t)p * 64;
-        if (COH) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (ok[j])
-              __hip_atomic_store(dst + j, v[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else if (ok[0] && ok[3]) {   // the valid lanes of a step are contiguous
+        if (ok[0] && ok[3]) {   // the valid lanes of a step are contiguous
           *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
         } else {
 #pragma unroll
@@ -180,7 +189,7 @@ __device__ __forceinline__ void dist_block(const float* __restrict__ x,
     }
   } else {
     float* ob = dist + b * N * M;
-    for (int rr = w; rr < kDT; rr += 4) {
+    for (int rr = w; rr < TR; rr += 4) {
       const int64_t gi = bi0 + rr;
       if (gi >= N) break;
 #pragma unroll
