@@ -54,9 +54,9 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_dp_common.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h"],
-    "sha256": "558eae182eeb95a6196e58fd08919697a5097d2fddeb0e2a9d6db5583be75cf1",
-    "fetch_kib": 37390, "fetch_scale": 2.0,
-    "write_kib": 147856, "write_scale": 1.0,
+    "sha256": "cd99669cf32e1c025c23862751517d0b416be5ae13024c568589f2334a869251",
+    "fetch_kib": 37380, "fetch_scale": 2.0,
+    "write_kib": 147855, "write_scale": 1.0,
 }
 
 
