@@ -367,7 +367,21 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
     const int64_t c0 = (int64_t)p * kCH;
     const float* yc = ys + (p & 1) * 16 * YP;
     if (want_gx) {
-      // dx += E[64 x 16] . Y[16 x DC] on v_mfma_f32_32x32x2_f32.
+      // dx += E[64 x 16] . Y[16 x DC] on v_mfma_f32_32x32x2_f32.  Up to
+      // DC = 64 the block's E entries are read as one batch (unconditional
+      // reads, masked after), so the LDS latency is paid once per block, not
+      // once per product; the widest slice keeps per-product reads (its
+      // accumulators leave no registers for the batch).
+      constexpr bool kBatch = NT <= 2;
+      float ev[8][2];
+      if (kBatch) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const float* ecol = dr + (int)((c0 + 2 * s + h) & (kFR - 1)) * kFPitch;
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) ev[s][rt] = ecol[32 * rt + r32];
+        }
+      }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int cl = 2 * s + h;                 // column of the block
@@ -377,7 +391,8 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
           const int row = 32 * rt + r32;
-          av[rt] = (cok && r0 + row < N) ? ecol[row] : 0.f;
+          const bool ok = cok && r0 + row < N;
+          av[rt] = kBatch ? (ok ? ev[s][rt] : 0.f) : (ok ? ecol[row] : 0.f);
           rsum[rt] += av[rt];
         }
 #pragma unroll
@@ -398,15 +413,31 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
       for (int t = 0; t < 2 * NT; ++t) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
       const bool cok = c0 + r16 < M;
       const float* ecol = dr + (int)((c0 + r16) & (kFR - 1)) * kFPitch;
+      // Up to DC = 64, E and the x operands are read as one batch; columns
+      // of D past dend then read a clamped in-range entry whose products are
+      // never written out.
+      constexpr bool kBatchY = NT <= 2;
+      float ev[16];
+      int xo[2 * NT];
+#pragma unroll
+      for (int t = 0; t < 2 * NT; ++t) {
+        const int64_t dc = dbeg + 16 * t + r16;
+        xo[t] = (int)(dc < D ? dc : D - 1);
+      }
+      if (kBatchY) {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) ev[s] = ecol[4 * s + kk];
+      }
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const int row = 4 * s + kk;
-        const float av = (cok && r0 + row < N) ? ecol[row] : 0.f;
+        const bool ok = cok && r0 + row < N;
+        const float av = kBatchY ? (ok ? ev[s] : 0.f) : (ok ? ecol[row] : 0.f);
         cs += av;
 #pragma unroll
         for (int t = 0; t < 2 * NT; ++t) {
           const int64_t dc = dbeg + 16 * t + r16;
-          const float bv = dc < dend ? xs[row * P + dc] : 0.f;
+          const float bv = kBatchY ? xs[row * P + xo[t]] : (dc < dend ? xs[row * P + dc] : 0.f);
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[t], 0, 0, 0);
         }
       }
