@@ -31,7 +31,8 @@ constexpr int kFR = 128;     // distance/E ring columns per band (8 blocks of 16
 constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
 constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
 constexpr int kRevHelpD = 2; // distance helpers, reverse sweep
-constexpr int kRevHelpC = 2; // chain-rule helpers, reverse sweep
+constexpr int kRevHelpC = 2; // chain-rule helpers, reverse sweep (4 beyond D = 128)
+constexpr int kRevHelpCMax = 4;
 constexpr int kYB = 16;      // feature steps (of 4) per batch of y loads
 
 __host__ __device__ inline int fused_pitch(int64_t D) { return (int)(((D + 3) / 4) * 4 + 4); }
@@ -41,11 +42,11 @@ __host__ __device__ inline int fused_pitch(int64_t D) { return (int)(((D + 3) / 
 __host__ __device__ constexpr int chain_y_floats(int DC) { return 2 * 16 * (DC + 2); }
 
 // Dynamic LDS of one workgroup: the band's x rows and the distance/E ring,
-// plus (reverse sweep, DC columns of D per chain-rule helper) the helpers'
-// staged y rows.
-size_t fused_lds_bytes(int64_t D, int DC = 0) {
+// plus (reverse sweep, HC chain-rule helpers of DC columns of D each) the
+// helpers' staged y rows.
+size_t fused_lds_bytes(int64_t D, int DC = 0, int HC = 0) {
   return (size_t)64 * fused_pitch(D) * 4 + (size_t)kFR * kFPitch * 4 +
-         (DC ? (size_t)kRevHelpC * chain_y_floats(DC) * 4 : 0);
+         (DC ? (size_t)HC * chain_y_floats(DC) * 4 : 0);
 }
 
 // One band per workgroup; 0 when D is beyond what the kernels hold on chip.
@@ -57,7 +58,7 @@ struct FusedShared {
   unsigned wr_in, rd_in, wr_out, rd_out;
   unsigned d_ready;               // distance blocks published, in order
   unsigned dp_done;               // chunks completed by the band wave
-  unsigned e_free[kRevHelpC];     // blocks released by each chain-rule helper
+  unsigned e_free[kRevHelpCMax];  // blocks released by each chain-rule helper
   unsigned ticket;
 };
 
@@ -511,7 +512,7 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
   if (threadIdx.x == 0) {
     sh.wr_in = sh.rd_in = sh.wr_out = sh.rd_out = 0u;
     sh.d_ready = sh.dp_done = 0u;
-    for (int c = 0; c < kRevHelpC; ++c) sh.e_free[c] = 0u;
+    for (int c = 0; c < kRevHelpCMax; ++c) sh.e_free[c] = 0u;
   }
   __syncthreads();
   const unsigned ticket = sh.ticket;
@@ -575,7 +576,8 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
 template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC>
 static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcols = 0) {
   auto kern = k_dp_fused<REV, INFER, CKPT, HD, HC, DC>;
-  const size_t lds = fused_lds_bytes(a.D, REV ? DC : 0);
+  static_assert(HC <= kRevHelpCMax, "chain-rule helpers");
+  const size_t lds = fused_lds_bytes(a.D, REV ? DC : 0, HC);
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -588,10 +590,12 @@ static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcol
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
   if (!reverse) return launch_fused_one<false, false, false, kFwdHelpD, 0, 32>(a, s);
-  // Each of the two chain-rule helpers owns DC columns of D.
+  // Each chain-rule helper owns DC columns of D: two helpers up to D = 128,
+  // then four of 64 columns (one helper of 128 columns would not keep its
+  // accumulators in registers).
   if (a.D <= 2 * 32) return launch_fused_one<true, false, false, kRevHelpD, kRevHelpC, 32>(a, s);
   if (a.D <= 2 * 64) return launch_fused_one<true, false, false, kRevHelpD, kRevHelpC, 64>(a, s);
-  return launch_fused_one<true, false, false, kRevHelpD, kRevHelpC, 128>(a, s);
+  return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 64>(a, s);
 }
 
 hipError_t launch_fused_range(const DPArgs& a, bool reverse, hipStream_t s) {
