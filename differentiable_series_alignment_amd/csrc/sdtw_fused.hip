@@ -590,11 +590,12 @@ static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcol
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
   if (!reverse) return launch_fused_one<false, false, false, kFwdHelpD, 0, 32>(a, s);
-  // Each chain-rule helper owns DC columns of D: two helpers up to D = 128,
-  // then four of 64 columns (one helper of 128 columns would not keep its
-  // accumulators in registers).
+  // Each chain-rule helper owns DC columns of D: two of 32 columns up to
+  // D = 64, four of 32 up to 128, then four of 64 (wider helpers would not
+  // keep their accumulators in registers, and more helpers share the work
+  // of a block).
   if (a.D <= 2 * 32) return launch_fused_one<true, false, false, kRevHelpD, kRevHelpC, 32>(a, s);
-  if (a.D <= 2 * 64) return launch_fused_one<true, false, false, kRevHelpD, kRevHelpC, 64>(a, s);
+  if (a.D <= 4 * 32) return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 32>(a, s);
   return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 64>(a, s);
 }
 
