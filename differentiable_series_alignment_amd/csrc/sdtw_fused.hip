@@ -31,7 +31,7 @@ constexpr int kFR = 128;     // distance/E ring columns per band (8 blocks of 16
 constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
 constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
 constexpr int kRevHelpD = 2; // distance helpers, reverse sweep
-constexpr int kRevHelpC = 2; // chain-rule helpers, reverse sweep (4 beyond D = 128)
+constexpr int kRevHelpC = 2; // chain-rule helpers, reverse sweep (4 beyond D = 64)
 constexpr int kRevHelpCMax = 4;
 constexpr int kYB = 16;      // feature steps (of 4) per batch of y loads
 
