@@ -54,7 +54,7 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_dp_common.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h"],
-    "sha256": "cd99669cf32e1c025c23862751517d0b416be5ae13024c568589f2334a869251",
+    "sha256": "74af352d0fad50fb3222c734cf5f813885f6c1661cff8258ad9c764a0b7ea1d6",
     "fetch_kib": 37380, "fetch_scale": 2.0,
     "write_kib": 147855, "write_scale": 1.0,
 }

@@ -7,13 +7,8 @@
 namespace sdtw {
 
 constexpr int kCH = 16;                      // steps per chunk
-constexpr int kLag = 2 + 62 / kCH;           // chunks between adjacent bands
-constexpr int kRing = 128;                   // LDS ring columns per boundary
-constexpr int kPub = 4;                      // chunks between global publishes
-constexpr int kSlack = 96;                   // extra columns awaited at start
 constexpr uint32_t kSpinCap = 1u << 25;      // polls before a wait gives up
 constexpr uint32_t kLdsSpinCap = 1u << 22;   // the same for waits on LDS counters
-static_assert(kRing >= (kLag + 3) * kCH, "LDS ring too small");
 static_assert(kCH == 16, "band_chunk unrolls 16 steps");
 
 // Control words of one sweep: [0] ticket, [1] finished workgroups,
