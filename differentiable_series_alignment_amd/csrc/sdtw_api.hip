@@ -159,7 +159,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
     L->R2 = off;
     off += align_up(cells * 8);
     L->part = off;
-    off += align_up(sdtw::chain_part_floats(B, N, M) * 4);
+    off += align_up(sdtw::chain_part_floats(B, N, M, D, L->S) * 4);
     L->dist = off;
     off += align_up(cells * 4);
   }

@@ -543,14 +543,20 @@ bool chain_gy_fits(int64_t M, int64_t D, int64_t S) {
   return D <= 64 && M * (D + 1) <= S * 64;
 }
 
-// Row-pass splits when it makes the dy shares: up to kChainFillGy
-// workgroups (at least two column blocks each), as far as their partial
-// sums fit in the distance region after the shares.
-constexpr int64_t kChainFillGy = 1024;
+// Row-pass splits when it makes the dy shares.  Every part first loads a
+// 96-step window, so short parts mostly load: the parts fill the GPU with
+// one workgroup per CU keeping at least two column blocks each, or with two
+// per CU keeping at least four, whichever splits more; and only as far as
+// their partial sums fit in the distance region after the shares.
+// Measured: 32x256x256 31 us with two parts per band against 34 with four;
+// 10x100x100 18 us with two against 22 unsplit; 32x1024x1024 194 us
+// unsplit against 213 with two; 32x512x512 the same with two to four.
 int chain_splits_rows_gy(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S) {
   const int64_t nb = (N + 63) / 64, groups = B * nb, nblk = (M + 31) / 32;
-  int64_t p = (kChainFillGy + groups - 1) / groups;
-  p = p < nblk / 2 ? p : nblk / 2;
+  int64_t p1 = (256 + groups - 1) / groups, p2 = (512 + groups - 1) / groups;
+  p1 = p1 < nblk / 2 ? p1 : nblk / 2;
+  p2 = p2 < nblk / 4 ? p2 : nblk / 4;
+  int64_t p = p1 > p2 ? p1 : p2;
   p = p < 1 ? 1 : (p > 8 ? 8 : p);
   const int64_t room = groups * (S * 64 - M * (D + 1));
   while (p > 1 && groups * p * 17 * 256 > room) --p;
@@ -560,10 +566,13 @@ int chain_splits_rows_gy(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S) 
 // Workgroups per band (dx) or per 64-column block (dy): a launch with fewer
 // groups than the GPU has CUs splits each group's reduction range so that it
 // fills them, keeping at least two column blocks (or bands) per workgroup.
-// Larger launches do not split (at C2 a split gains nothing and its partial
-// sums would cost memory).
+// Larger launches do not split (a split gains nothing there and its partial
+// sums would cost memory).  Where the dy shares can be made, the row pass
+// splits as the share path does whether or not E is requested, so dx is
+// summed in the same order either way.
 constexpr int64_t kChainFill = 256;
-int chain_splits_rows(int64_t B, int64_t N, int64_t M) {
+int chain_splits_rows(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S) {
+  if (chain_gy_fits(M, D, S)) return chain_splits_rows_gy(B, N, M, D, S);
   const int64_t groups = B * ((N + 63) / 64), nblk = (M + 31) / 32;
   int64_t p = (kChainFill + groups - 1) / groups;
   p = p < nblk / 2 ? p : nblk / 2;
@@ -575,8 +584,8 @@ int chain_splits_cols(int64_t B, int64_t N, int64_t M) {
   p = p < nb / 2 ? p : nb / 2;
   return (int)(p < 1 ? 1 : (p > 8 ? 8 : p));
 }
-size_t chain_part_floats(int64_t B, int64_t N, int64_t M) {
-  const int64_t pr = chain_splits_rows(B, N, M), pc = chain_splits_cols(B, N, M);
+size_t chain_part_floats(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S) {
+  const int64_t pr = chain_splits_rows(B, N, M, D, S), pc = chain_splits_cols(B, N, M);
   const int64_t rows = pr > 1 ? B * ((N + 63) / 64) * pr : 0;
   const int64_t cols = pc > 1 ? B * ((M + 63) / 64) * pc : 0;
   return (size_t)(rows > cols ? rows : cols) * 33 * 256;
@@ -604,7 +613,7 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
                         int64_t M, int64_t D, int64_t S, float* part, unsigned* cnt_rows,
                         unsigned* cnt_cols, bool keep_e, hipStream_t s) {
   const int nb = (int)((N + 63) / 64);
-  const unsigned pr = (unsigned)chain_splits_rows(B, N, M);
+  const unsigned pr = (unsigned)chain_splits_rows(B, N, M, D, S);
   const unsigned pc = (unsigned)chain_splits_cols(B, N, M);
   if (gy && !keep_e && chain_gy_fits(M, D, S)) {
     // One row pass makes dx and the bands' shares of dy (in place of E);

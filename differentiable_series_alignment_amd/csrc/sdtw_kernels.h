@@ -131,9 +131,9 @@ hipError_t launch_fill_u32(unsigned* p, int64_t n, unsigned v, hipStream_t s);
 // Small problems split each sum over several workgroups: `part` holds
 // chain_part_floats() floats of partial sums and the counters (B*nbands for
 // the rows, B*ceil(M/64) for the columns) start at zero and are left at zero.
-int chain_splits_rows(int64_t B, int64_t N, int64_t M);
+int chain_splits_rows(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S);
 int chain_splits_cols(int64_t B, int64_t N, int64_t M);
-size_t chain_part_floats(int64_t B, int64_t N, int64_t M);
+size_t chain_part_floats(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S);
 hipError_t launch_chain(float* esk, const double* R, const double* R2,
                         const double* loss64, const float* x, const float* y,
                         const float* gl, float* gx, float* gy, int64_t B, int64_t N,
