@@ -193,7 +193,9 @@ __device__ __forceinline__ bool split_reduce(v16f (&acc)[NTW], float& sum, float
 // dx for one band (64 rows) of one pair, columns of D in [d0, d0 + 128).
 // Wave w: row tile w & 1, d tiles (w >> 1) + 2t.  Column blocks of 32 need
 // band steps [j0, j0 + 96); the next block's 32 new steps are fetched into
-// registers while the current block computes.  FORM: the window comes from
+// registers while the current block computes, and its y rows once this
+// block's products are issued (one register set for y instead of two:
+// 4096x1000, D=128 627 us against 704; 32x512x512 61 against 64).  FORM: the window comes from
 // the sweeps' states and E is formed (and stored) on the way; otherwise it
 // is read from the stored E.  GX = false forms E only.  The band's column
 // blocks are split over nsplit workgroups (split sums, above).
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
       st.store(ring, s0);
     }
   }
-  float yv[16][NTW], yn[16][NTW];
+  float yv[16][NTW];
   auto load_y = [&](int64_t j0, float (&Y)[16][NTW]) {
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
@@ -302,7 +304,6 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
         sx.load(xbp, tbp, j0 + 96, smax);
       else
         st.load(bandp, j0 + 96, smax);
-      if (GX) load_y(j0 + 32, yn);
     }
     if (GX) {
       // E[row, j0 + 2s + h] for s = 0..15: ring rows base + 2s (the pad
@@ -320,6 +321,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
         for (int t = 0; t < NTW; ++t)
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, yv[s][t], acc[t], 0, 0, 0);
       }
+      if (more) load_y(j0 + 32, yv);
     }
     v16f gacc;
     float gcs = 0.f;
@@ -368,12 +370,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
         sx.template store<!GYP>(ring, bandp, j0 + 96, xnm, rows_left, M);
       else
         st.store(ring, j0 + 96);
-      if (GX) {
-#pragma unroll
-        for (int s = 0; s < 16; ++s)
-#pragma unroll
-          for (int t = 0; t < NTW; ++t) yv[s][t] = yn[s][t];
-      }
+
     }
     __syncthreads();
   }
@@ -404,7 +401,10 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
 
 // dy for 64 columns of one pair, columns of D in [d0, d0 + 128), summing over
 // every band.  Wave w: column tile w & 1, d tiles (w >> 1) + 2t.  The band's
-// window of steps [j0, j0 + 128) is fetched into registers one band ahead.
+// window of steps [j0, j0 + 128) is fetched into registers one band ahead;
+// the next band's x rows are fetched once this band's products are issued
+// (a second register set for them would leave one wave per SIMD: 280
+// VGPRs against 228, and 4096x1000, D=128 takes 584 us against 442).
 // The bands are split over nsplit workgroups (split sums, above).
 template <int NTW>
 __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ esk,
@@ -445,11 +445,13 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
   float csum = 0.f;
 
   Stage32 win[4], nxt[4];
-  float xv[32][NTW], xn[32][NTW];
-  auto load_band = [&](int64_t band, Stage32 (&Wn)[4], float (&X)[32][NTW]) {
+  float xv[32][NTW];
+  auto load_win = [&](int64_t band, Stage32 (&Wn)[4]) {
     const float* bandp = esk + ((b * nbands + band) * S + kSkewOff) * 64;
 #pragma unroll
     for (int k = 0; k < 4; ++k) Wn[k].load(bandp, j0 + 32 * k, smax);
+  };
+  auto load_x = [&](int64_t band, float (&X)[32][NTW]) {
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
       int64_t rr = band * 64 + 2 * s + h;
@@ -458,7 +460,8 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
       for (int t = 0; t < NTW; ++t) X[s][t] = xb[rr * D + dcol[t]];
     }
   };
-  load_band(bb0, win, xv);
+  load_win(bb0, win);
+  load_x(bb0, xv);
   __builtin_amdgcn_s_waitcnt(0);
 
   for (int64_t band = bb0; band < bb1; ++band) {
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
     for (int k = 0; k < 4; ++k) win[k].template store<false>(ring, 32 * k);
     __syncthreads();
     const bool more = band + 1 < bb1;
-    if (more) load_band(band + 1, nxt, xn);
+    if (more) load_win(band + 1, nxt);
     // Steps jl + lr of rows lr = 2s + h (no wrap: jl + lr < 128), all read
     // before the first product.
     float ev[32];
@@ -482,14 +485,11 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
       for (int t = 0; t < NTW; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xv[s][t], acc[t], 0, 0, 0);
     }
+    if (more) load_x(band + 1, xv);
     __syncthreads();
     if (more) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) win[k] = nxt[k];
-#pragma unroll
-      for (int s = 0; s < 32; ++s)
-#pragma unroll
-        for (int t = 0; t < NTW; ++t) xv[s][t] = xn[s][t];
     }
   }
 
