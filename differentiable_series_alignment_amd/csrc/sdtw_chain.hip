@@ -26,6 +26,10 @@ constexpr int kRingPitch = 65;
 constexpr int kRingPad = 32;
 constexpr int kRingFloats = (kRingSteps + kRingPad) * kRingPitch;
 
+// Row pitch (floats) of the bands' dy shares: D values and the column sum,
+// rounded up to whole 16-byte words.
+__host__ __device__ inline int64_t gy_pitch(int64_t D) { return (D + 4) & ~int64_t(3); }
+
 // Copy band steps [s0, s0 + 32) (relative to the band's first column step)
 // between global memory, registers and the LDS ring; 256 threads x 8 floats.
 struct Stage32 {
@@ -203,8 +207,8 @@ __device__ __forceinline__ bool split_reduce(v16f (&acc)[NTW], float& sum, float
 // GYP (D <= 64, FORM): E is not stored; instead each block also yields the
 // band's shares of dy for its 32 columns: P[b][band][j][d] = -sum over the
 // band's rows i of E[i,j] x_i[d] (d < D) and P[b][band][j][D] = sum of
-// E[i,j], into `esk` viewed as [B][nbands][M][D+1] (k_chain_gy adds the
-// bands up).  Wave w: d tile w >> 1, rows 32 (w & 1) .. +31; the two row
+// E[i,j], into `esk` viewed as [B][nbands][M][gy_pitch(D)] (k_chain_gy adds
+// the bands up).  Wave w: d tile w >> 1, rows 32 (w & 1) .. +31; the two row
 // halves meet in LDS.
 template <int NTW, bool GX, bool FORM, bool GYP>
 __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
 #pragma unroll
       for (int e = 0; e < 16; ++e) gacc[e] += gsum[(gdt * 17 + e) * 64 + l];
       gcs += gsum[(gdt * 17 + 16) * 64 + l];
-      const int64_t D1 = D + 1;
+      const int64_t D1 = gy_pitch(D);
       float* pb = esk + (b * nbands + band) * M * D1;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -518,29 +522,41 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
 }
 
 // dy[b,j,d] = 2 g_b (y[b,j,d] sum_k P[b][k][j][D] + sum_k P[b][k][j][d]),
-// the bands k added in order (the shares the row pass wrote with GYP).
+// the bands k added in order (the shares the row pass wrote with GYP).  A
+// thread takes four consecutive d of one row j (rows of gy_pitch(D) floats,
+// so every share row starts on 16 bytes and is read as whole 16-byte
+// words; the last word of a row holds the column sum).
 __global__ __launch_bounds__(256) void k_chain_gy(const float* __restrict__ P,
                                                   const float* __restrict__ y,
                                                   const float* __restrict__ gl,
                                                   float* __restrict__ gy, int64_t B, int64_t M,
                                                   int64_t D, int nbands) {
+  const int64_t D1 = gy_pitch(D), nq = (D + 3) / 4;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= B * M * D) return;
-  const int64_t b = i / (M * D), jd = i - b * M * D;
-  const int64_t j = jd / D, d = jd - j * D;
-  const int64_t D1 = D + 1;
+  if (i >= B * M * nq) return;
+  const int64_t bj = i / nq, q = i - bj * nq;
+  const int64_t b = bj / M, j = bj - b * M;
   const float* pp = P + (b * nbands * M + j) * D1;
-  float cs = 0.f, ex = 0.f;
+  float cs = 0.f;
+  v4f ex = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < nbands; ++k) {
-    cs += pp[(int64_t)k * M * D1 + D];
-    ex += pp[(int64_t)k * M * D1 + d];
+    const float* row = pp + (int64_t)k * M * D1;
+    cs += row[D];
+    ex += *reinterpret_cast<const v4f*>(row + 4 * q);
   }
-  gy[i] = 2.f * gl[b] * (cs * y[i] + ex);
+  const float g2 = 2.f * gl[b];
+  const float* yr = y + bj * D;
+  float* out = gy + bj * D;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t d = 4 * q + u;
+    if (d < D) out[d] = g2 * (cs * yr[d] + ex[u]);
+  }
 }
 
 // Whether the per-band shares of dy fit where the distances were.
 bool chain_gy_fits(int64_t M, int64_t D, int64_t S) {
-  return D <= 64 && M * (D + 1) <= S * 64;
+  return D <= 64 && M * gy_pitch(D) <= S * 64;
 }
 
 // Row-pass splits when it makes the dy shares.  Every part first loads a
@@ -558,7 +574,7 @@ int chain_splits_rows_gy(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S) 
   p2 = p2 < nblk / 4 ? p2 : nblk / 4;
   int64_t p = p1 > p2 ? p1 : p2;
   p = p < 1 ? 1 : (p > 8 ? 8 : p);
-  const int64_t room = groups * (S * 64 - M * (D + 1));
+  const int64_t room = groups * (S * 64 - M * gy_pitch(D));
   while (p > 1 && groups * p * 17 * 256 > room) --p;
   return (int)p;
 }
@@ -620,13 +636,13 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
     // a short pass adds the shares up.  Its split partial sums go after the
     // shares.
     const unsigned pg = (unsigned)chain_splits_rows_gy(B, N, M, D, S);
-    float* gpart = esk + B * nb * M * (D + 1);
+    float* gpart = esk + B * nb * M * gy_pitch(D);
     launch_rows<1, true, true>(B, pg, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, 0,
                                gpart, cnt_rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TimedLaunch timed_("chain_gy", s);
-    hipLaunchKernelGGL(k_chain_gy, dim3((unsigned)((B * M * D + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_chain_gy, dim3((unsigned)((B * M * ((D + 3) / 4) + 255) / 256)), dim3(256), 0, s,
                        esk, y, gl, gy, B, M, D, nb);
     return hipGetLastError();
   }
