@@ -169,6 +169,9 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
 
 bool gamma_ok(float g) { return isfinite(g) && g > 0.f; }
 
+// Hand-off row entries of the unfused and fused training layouts.
+int64_t hrow_doubles(const Layout& L, int64_t B, int64_t M) { return 2 * B * L.nseg * M; }
+
 // Control words: the unfused launch (both sweeps) uses them from the start;
 // the fused sweeps run as separate launches, the forward one on the first
 // half and the reverse one on the second.  Every launch leaves its words
@@ -324,12 +327,17 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
     }
     if (e == hipSuccess) e = sdtw::launch_infer(a, L.hcols, s);
   } else if (fused) {
-    e = sdtw::launch_zero_u32(ctrl, (int64_t)L.ctrl_words, s);
+    // The hand-off rows start as kHEmpty; every sweep leaves them so, which
+    // the backward's sweep relies on.
+    e = sdtw::launch_clear(ctrl, (int64_t)L.ctrl_words, a.H, hrow_doubles(L, B, M), s);
+    a.hvalid = 1;
     if (e == hipSuccess) e = sdtw::launch_dp_fused(a, false, s);
   } else {
     // Both sweeps at once: the loss comes from the forward one, and the
     // reverse one leaves what the backward needs besides the forward state.
-    e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, ctrl, (int64_t)L.ctrl_words, s);
+    e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, ctrl, (int64_t)L.ctrl_words, a.H,
+                               hrow_doubles(L, B, M), s);
+    a.hvalid = 1;
     if (e == hipSuccess) e = sdtw::launch_dp_both(a, s);
   }
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
@@ -362,6 +370,7 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
     a.gy = grad_y;
     a.align = align;
     hipError_t e = hipSuccess;
+    a.hvalid = 1;   // the forward left the hand-off rows at kHEmpty
     if (grad_y) e = sdtw::launch_zero_f32(grad_y, B * M * D, s);
     if (e == hipSuccess) e = sdtw::launch_dp_fused(a, true, s);
     return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;

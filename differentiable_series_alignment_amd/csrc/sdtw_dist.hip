@@ -30,14 +30,17 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
                                               float* __restrict__ dist,
                                               int64_t N, int64_t M, int64_t D,
                                               int64_t S, int nbands,
-                                              unsigned* __restrict__ zero, int64_t nzero) {
+                                              unsigned* __restrict__ zero, int64_t nzero,
+                                              uint64_t* __restrict__ empty, int64_t nempty) {
   __shared__ float smem[DistTile<TR>::kLds];
   // Words the next kernels of the step expect to find cleared (their
-  // control words; a fresh workspace holds garbage), spread over the grid.
+  // control words and hand-off rows; a fresh workspace holds garbage),
+  // spread over the grid.
   {
     const int64_t wg = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
     const int64_t stride = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
     for (int64_t k = wg * 256 + threadIdx.x; k < nzero; k += stride) zero[k] = 0u;
+    for (int64_t k = wg * 256 + threadIdx.x; k < nempty; k += stride) empty[k] = kHEmpty;
   }
   dist_block<TR, SKEW>(x, y, dist, blockIdx.z, (int64_t)blockIdx.y * TR,
                        (int64_t)blockIdx.x * kDT, N, M, D, S, nbands, smem);
@@ -66,24 +69,26 @@ hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
   {
     TimedLaunch timed_("dist", stream);
     hipLaunchKernelGGL((k_dist<128, false>), grid, dim3(256), 0, stream, x, y, dist, N, M, D,
-                       (int64_t)0, 0, (unsigned*)nullptr, (int64_t)0);
+                       (int64_t)0, 0, (unsigned*)nullptr, (int64_t)0, (uint64_t*)nullptr,
+                       (int64_t)0);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t B,
                             int64_t N, int64_t M, int64_t D, int64_t S, unsigned* zero,
-                            int64_t nzero, hipStream_t stream) {
+                            int64_t nzero, double* empty, int64_t nempty, hipStream_t stream) {
+  uint64_t* const eb = reinterpret_cast<uint64_t*>(empty);
   const int tr = dist_rows(B, N, M);
   dim3 grid((unsigned)((M + kDT - 1) / kDT), (unsigned)((N + tr - 1) / tr), (unsigned)B);
   {
     TimedLaunch timed_("dist_skew", stream);
     if (tr == 64)
       hipLaunchKernelGGL((k_dist<64, true>), grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S,
-                         (int)((N + 63) / 64), zero, nzero);
+                         (int)((N + 63) / 64), zero, nzero, eb, nempty);
     else
       hipLaunchKernelGGL((k_dist<128, true>), grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S,
-                         (int)((N + 63) / 64), zero, nzero);
+                         (int)((N + 63) / 64), zero, nzero, eb, nempty);
   }
   return hipGetLastError();
 }

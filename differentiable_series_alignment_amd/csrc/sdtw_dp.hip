@@ -252,9 +252,11 @@ __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a)
   if (w == W) {
     const int64_t pb = rev * per_sweep + (int64_t)b * a.nseg;
     const int64_t sin = pb + (seg > 0 ? seg - 1 : 0), sout = pb + seg;
+    GlobalRow gr{0u, nullptr, nullptr};
+    gr.valid_in = gr.valid_out = a.hvalid != 0;
     segment_io_wave(seg > 0, seg + 1 < a.nseg, a.ctrl + 2 + sin, a.ctrl + 2 + sout,
                     a.H + sin * a.M, a.H + sout * a.M, ring[0], &wr[0], &rd[0], ring[W],
-                    &wr[W], &rd[W], (unsigned)a.M, lane);
+                    &wr[W], &rd[W], (unsigned)a.M, lane, gr);
   } else if (w < nb_seg) {
     if (rev)
       band_sweep<true>(a, b, seg, w, nb_seg, ring, wr, rd, lane);
@@ -262,6 +264,26 @@ __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a)
       band_sweep<false>(a, b, seg, w, nb_seg, ring, wr, rd, lane);
   }
   release_ctrl(a.ctrl, 2 * per_sweep);
+}
+
+// Control words to zero and hand-off entries to kHEmpty, in one launch.
+__global__ void k_clear(unsigned* zero, int64_t nzero, uint64_t* empty, int64_t nempty) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nzero; i += stride)
+    zero[i] = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nempty; i += stride)
+    empty[i] = kHEmpty;
+}
+
+hipError_t launch_clear(unsigned* zero, int64_t nzero, double* empty, int64_t nempty,
+                        hipStream_t s) {
+  const int64_t n = nzero > nempty ? nzero : nempty;
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  TimedLaunch timed_("clear", s);
+  hipLaunchKernelGGL(k_clear, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s,
+                     zero, nzero, reinterpret_cast<uint64_t*>(empty), nempty);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s) {

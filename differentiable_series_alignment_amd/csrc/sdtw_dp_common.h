@@ -103,10 +103,21 @@ __device__ __forceinline__ void lds_publish(unsigned* p, unsigned v) {
 // the column in it (fetch_back); that wait points at a larger ticket, so
 // ring mode is only used where a pair's segments all fit on the GPU at once
 // and tickets run pair by pair.
+//
+// Whole rows can instead carry their own validity (`valid` set for a side):
+// the row starts filled with kHEmpty, a signalling-NaN pattern that no
+// arithmetic produces (computed NaNs are quiet), the producer only stores
+// the values, and the consumer polls the values themselves, takes the run
+// of columns that are no longer kHEmpty and writes kHEmpty back behind it,
+// so the row is ready for the next launch.  No count is stored and the
+// producer never waits for its stores to complete.  Values and markers are
+// single 8-byte atomic accesses, so a value is never seen torn.
 struct GlobalRow {
   unsigned hcols;             // 0: whole rows
   const unsigned* fetch_back; // consumer's fetched count (output side, ring mode)
   unsigned* fetch_out;        // own fetched count (input side, ring mode)
+  bool valid_in = false;      // whole input row carries its own validity
+  bool valid_out = false;     // whole output row carries its own validity
 };
 
 __device__ __forceinline__ void segment_io_wave(
@@ -116,12 +127,33 @@ __device__ __forceinline__ void segment_io_wave(
     unsigned* rd_out, unsigned M, int lane, GlobalRow gr = GlobalRow{0u, nullptr, nullptr}) {
   const unsigned hmask = gr.hcols ? gr.hcols - 1 : 0xffffffffu;
   unsigned fetched = 0, known_in = 0, pub = 0, known_back = 0;
+  // Only a validated input row (always a workspace row) is written back.
+  uint64_t* const hin_bits = reinterpret_cast<uint64_t*>(const_cast<double*>(Hin));
   for (uint32_t spin = 0; spin < kSpinCap; ++spin) {
     const bool in_left = do_in && fetched < M;
     const bool out_left = do_out && pub < M;
     if (!in_left && !out_left) break;
     bool moved = false;
-    if (in_left) {
+    if (in_left && gr.valid_in) {
+      const unsigned room =
+          __hip_atomic_load(rd_in, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + kRingC;
+      unsigned lim = fetched + 64 < M ? fetched + 64 : M;
+      lim = lim < room ? lim : room;
+      const unsigned c = fetched + lane;
+      uint64_t bits = kHEmpty;
+      if (c < lim) bits = __hip_atomic_load(hin_bits + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t okm = __ballot(c < lim && bits != kHEmpty);
+      const unsigned n = ~okm == 0 ? 64u : (unsigned)__builtin_ctzll(~okm);
+      if (n > 0) {
+        if ((unsigned)lane < n) {
+          ring_in[c & (kRingC - 1)] = __builtin_bit_cast(double, bits);
+          __hip_atomic_store(hin_bits + c, kHEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (lane == 0) lds_publish(wr_in, fetched + n);
+        fetched += n;
+        moved = true;
+      }
+    } else if (in_left) {
       if (known_in <= fetched)
         known_in = __hip_atomic_load(prog_in, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const unsigned room =
@@ -153,11 +185,13 @@ __device__ __forceinline__ void segment_io_wave(
           __hip_atomic_store(Hout + (c & hmask), ring_out[c & (kRingC - 1)], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         if (lane == 0) lds_publish(rd_out, avail);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (lane == 0)
-          __hip_atomic_store(prog_out, avail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!gr.valid_out) {
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __builtin_amdgcn_s_waitcnt(0);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if (lane == 0)
+            __hip_atomic_store(prog_out, avail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         pub = avail;
         moved = true;
       }

@@ -562,6 +562,10 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
     // and hands its last band's bottom row out through bot_row.
     const bool ext_in = band == 0 && a.top_row != nullptr;
     const bool ext_out = band + 1 == a.nseg && a.bot_row != nullptr;
+    if (!(INFER && hcols)) {
+      gr.valid_in = a.hvalid != 0 && !ext_in;
+      gr.valid_out = a.hvalid != 0 && !ext_out;
+    }
     segment_io_wave(band > 0 || ext_in, band + 1 < a.nseg || ext_out,
                     ext_in ? a.full_word : a.ctrl + 2 + sin,
                     ext_out ? a.sink_word : a.ctrl + 2 + sout,

@@ -32,6 +32,10 @@ __host__ __device__ inline int64_t sweep_steps(int64_t M) {
   return ((M + 63 + 15) / 16) * 16;
 }
 
+// Marker of a hand-off entry not written yet: a signalling-NaN pattern,
+// which no arithmetic produces (computed NaNs are quiet).
+constexpr uint64_t kHEmpty = 0xFFF05D7C0DE0A11FULL;
+
 // Arguments of the wavefront dynamic-programme kernels.  The forward sweep
 // walks the grid from (0,0) to (N-1,M-1); the reverse sweep walks it from
 // (N-1,M-1) back to (0,0), i.e. the forward recurrence on both sequences
@@ -43,6 +47,8 @@ struct DPArgs {
   double* R;            // band-step forward state X
   double* R2;           // band-step reverse soft-minimum parts T' (unfused)
   double* H;            // bottom rows handed between segments
+  int hvalid;           // whole H rows carry their own validity (start as
+                        // kHEmpty, which every launch leaves behind)
   unsigned* ctrl;       // ticket, finished count, per-segment progress
   double* loss64;       // [B] X[N-1,M-1] (forward writes, reverse reads)
   float* loss;          // [B] loss in natural units (forward)
@@ -102,10 +108,14 @@ hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
                        int64_t N, int64_t M, int64_t D, hipStream_t stream);
 // Band-step distances; also clears `nzero` words at `zero` (the step's
-// control words) for the kernels that follow on the stream.
+// control words) and sets `nempty` hand-off entries at `empty` to kHEmpty
+// for the kernels that follow on the stream.
 hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t B,
                             int64_t N, int64_t M, int64_t D, int64_t S, unsigned* zero,
-                            int64_t nzero, hipStream_t stream);
+                            int64_t nzero, double* empty, int64_t nempty, hipStream_t stream);
+// The same clearing alone.
+hipError_t launch_clear(unsigned* zero, int64_t nzero, double* empty, int64_t nempty,
+                        hipStream_t s);
 hipError_t launch_unskew(const float* esk, float* out, int64_t B, int64_t N,
                          int64_t M, int64_t S, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
