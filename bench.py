@@ -54,9 +54,9 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_dp_common.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h"],
-    "sha256": "74af352d0fad50fb3222c734cf5f813885f6c1661cff8258ad9c764a0b7ea1d6",
-    "fetch_kib": 37380, "fetch_scale": 2.0,
-    "write_kib": 147855, "write_scale": 1.0,
+    "sha256": "d782974859d70da7bd564b53698d671aa71a1cc5d8a8f68ab9222e8a015ec5dd",
+    "fetch_kib": 37585, "fetch_scale": 2.0,
+    "write_kib": 148109, "write_scale": 1.0,
 }
 
 
