@@ -516,3 +516,41 @@ def test_small_gamma_finite(S):
     x, y = pair_batch(4, 700, 650, 32, seed=8)
     l, gx, gy = gpu_value_and_grad(S, x, y, 0.01)
     assert np.isfinite(l).all() and np.isfinite(gx).all() and np.isfinite(gy).all()
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_workspace_contents_do_not_matter(S, mode):
+    """Rows handed between workgroups carry their own validity and every
+    forward sets them: a workspace left holding zeros (which read as valid
+    values) or all-ones bytes (NaNs) gives bitwise the same loss and dx, and
+    a second backward on one forward repeats the first (each sweep leaves
+    the rows as it found them)."""
+    from differentiable_series_alignment_amd import _lib as L
+    B, N, M, D = 2, 300, 150, 8      # 5 bands: two segments unfused, five fused
+    x, y = pair_batch(B, N, M, D, seed=5)
+    x, y = x.to(DEV), y.to(DEV)
+    nb = L.sdtw_workspace_bytes(B, N, M, D, mode)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    gl = torch.full((B,), 0.5, device=DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    runs = []
+    for fill in (0, 255):
+        ws.fill_(fill)
+        loss = torch.empty(B, device=DEV)
+        L.check(L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, 1.0, mode,
+                               ws.data_ptr(), nb, loss.data_ptr(), s), "sdtw_forward")
+        grads = []
+        for _ in range(2):
+            gx, gy = torch.empty_like(x), torch.empty_like(y)
+            L.check(L.sdtw_backward(x.data_ptr(), y.data_ptr(), B, N, M, D, 1.0, mode,
+                                    ws.data_ptr(), nb, gl.data_ptr(), gx.data_ptr(),
+                                    gy.data_ptr(), None, s), "sdtw_backward")
+            grads.append((gx, gy))
+        torch.cuda.synchronize()
+        assert torch.isfinite(loss).all()
+        torch.testing.assert_close(grads[1][0], grads[0][0], rtol=0, atol=0)
+        torch.testing.assert_close(grads[1][1], grads[0][1], rtol=1e-5, atol=1e-7)
+        runs.append((loss, grads[0]))
+    torch.testing.assert_close(runs[1][0], runs[0][0], rtol=0, atol=0)
+    torch.testing.assert_close(runs[1][1][0], runs[0][1][0], rtol=0, atol=0)
+    torch.testing.assert_close(runs[1][1][1], runs[0][1][1], rtol=1e-5, atol=1e-7)
