@@ -54,7 +54,7 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_dp_common.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h"],
-    "sha256": "d782974859d70da7bd564b53698d671aa71a1cc5d8a8f68ab9222e8a015ec5dd",
+    "sha256": "3b57d7e6cd041f91daa294b475f94ba30382173947935ce3c532cccdf4fdcbee",
     "fetch_kib": 37585, "fetch_scale": 2.0,
     "write_kib": 148109, "write_scale": 1.0,
 }

@@ -83,35 +83,31 @@ __device__ __forceinline__ void lds_publish(unsigned* p, unsigned v) {
 
 // The hand-off between consecutive workgroups of one pair ("segments") is
 // done by one extra wave per workgroup, so the band waves never wait on
-// global memory:
-//  - input: poll the previous segment's published column count, copy the
-//    new columns of its bottom row from global memory into ring_in (the top
-//    ring of band 0);
-//  - output: copy what the last band wrote into ring_out to global memory,
-//    wait for those stores, then publish the new column count.
-// Row values and counts are accessed with relaxed agent-scope atomics
-// (device-coherent loads and stores that bypass the per-XCD caches); the
-// explicit vmcnt(0) wait between the row stores and the count store orders
-// them, so no cache write-back or invalidation is needed.  A segment waits
-// only on a smaller ticket, which is running, so the loop ends; the poll cap
-// guarantees the wave exits regardless.
+// global memory: it copies the new columns of the previous segment's bottom
+// row from global memory into ring_in (the top ring of band 0), and what the
+// last band wrote into ring_out to global memory.  Rows are accessed with
+// relaxed agent-scope atomics (device-coherent loads and stores that bypass
+// the per-XCD caches), so no cache write-back or invalidation is needed.
+// The reader learns which columns are there in one of two ways:
+//  - self-validating rows (valid_in / valid_out, whole rows only): the row
+//    starts filled with kHEmpty, a signalling-NaN pattern that no
+//    arithmetic produces (computed NaNs are quiet); the writer only stores
+//    the values, and the reader polls the values themselves, takes the run
+//    of columns no longer kHEmpty and writes kHEmpty back behind it, so the
+//    row is ready for the next launch.  Values and markers are single
+//    8-byte atomic accesses, so a value is never seen torn;
+//  - counts: the writer waits for its stores (vmcnt(0)) and then publishes
+//    the column count, which the reader polls before loading.
+// A segment waits only on a smaller ticket, which is running, so the loop
+// ends; the poll cap guarantees the wave exits regardless.
 //
 // Global rows are either whole (hcols = 0: column c at H[c]) or rings of
-// hcols columns (a power of two; column c at H[c % hcols]).  With rings the
-// consumer also publishes how many columns it has fetched (fetch_out) and
-// the producer does not overwrite a slot before its consumer has fetched
-// the column in it (fetch_back); that wait points at a larger ticket, so
-// ring mode is only used where a pair's segments all fit on the GPU at once
-// and tickets run pair by pair.
-//
-// Whole rows can instead carry their own validity (`valid` set for a side):
-// the row starts filled with kHEmpty, a signalling-NaN pattern that no
-// arithmetic produces (computed NaNs are quiet), the producer only stores
-// the values, and the consumer polls the values themselves, takes the run
-// of columns that are no longer kHEmpty and writes kHEmpty back behind it,
-// so the row is ready for the next launch.  No count is stored and the
-// producer never waits for its stores to complete.  Values and markers are
-// single 8-byte atomic accesses, so a value is never seen torn.
+// hcols columns (a power of two; column c at H[c % hcols]), which use
+// counts.  With rings the consumer also publishes how many columns it has
+// fetched (fetch_out) and the producer does not overwrite a slot before its
+// consumer has fetched the column in it (fetch_back); that wait points at a
+// larger ticket, so ring mode is only used where a pair's segments all fit
+// on the GPU at once and tickets run pair by pair.
 struct GlobalRow {
   unsigned hcols;             // 0: whole rows
   const unsigned* fetch_back; // consumer's fetched count (output side, ring mode)
