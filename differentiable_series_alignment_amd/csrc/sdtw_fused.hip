@@ -30,7 +30,7 @@ namespace sdtw {
 constexpr int kFR = 128;     // distance/E ring columns per band (8 blocks of 16)
 constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
 constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
-constexpr int kRevHelpD = 2; // distance helpers, reverse sweep
+constexpr int kRevHelpD = 2; // distance helpers, reverse sweep (3 for 64 < D <= 128)
 constexpr int kRevHelpC = 2; // chain-rule helpers, reverse sweep (4 beyond D = 64)
 constexpr int kRevHelpCMax = 4;
 constexpr int kYB = 16;      // feature steps (of 4) per batch of y loads
@@ -598,8 +598,12 @@ hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   // D = 64, four of 32 up to 128, then four of 64 (wider helpers would not
   // keep their accumulators in registers, and more helpers share the work
   // of a block).
+  // Up to D = 64 two distance helpers keep ahead of the band wave; beyond,
+  // a third one (32x1024x1024, D=128: 826 us against 891; with 64-column
+  // chain helpers a third would push the registers into scratch).
   if (a.D <= 2 * 32) return launch_fused_one<true, false, false, kRevHelpD, kRevHelpC, 32>(a, s);
-  if (a.D <= 4 * 32) return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 32>(a, s);
+  if (a.D <= 4 * 32)
+    return launch_fused_one<true, false, false, kRevHelpD + 1, kRevHelpCMax, 32>(a, s);
   return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 64>(a, s);
 }
 
