@@ -60,6 +60,61 @@ TRAFFIC_RECORD = {
 }
 
 
+# Roofs of the per-configuration bounds (MI355X datasheet): fp64 and fp32
+# matrix rates, HBM bandwidth, and the dependency chain of the recurrence:
+# a sweep visits the N+M-1 anti-diagonals one after another, and one step of
+# the cell's chain (neighbour exchange, ordering, two exp2, a log2, the
+# state) is taken as CHAIN_CYCLES clocks.
+PEAK_F64_MFMA = 78.6e12
+PEAK_F32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12
+CHAIN_CYCLES = 100
+CLOCK = 2.4e9
+
+
+def step_bounds(B, N, M, D, fused):
+    """Lower bounds of one fwd+bwd step (microseconds).  Stages: distances
+    (2D flops per cell on fp64 MFMA; unfused also writes them, 4 B per
+    cell), the sweeps (both at once unfused: the chain of N+M-1 steps, 28
+    ALU operations and 24 B per cell), the chain rule (4D flops per cell on
+    fp32 MFMA; unfused reads the two fp64 states and writes E or the dy
+    shares, 20 B per cell).  Fused runs the sweeps one after the other and
+    recomputes the distances in each (8 B of state per cell written, then
+    read).  `per_stage` puts every stage at its own roof and adds them (the
+    stages run one after another); `ideal` overlaps everything (the largest
+    of the summed resource times and the chain)."""
+    cells = B * N * M
+    io = 4 * B * (N + M) * D
+    chain = (N + M - 1) * CHAIN_CYCLES / CLOCK
+    alu = 28 * cells / (PEAK_ALU_TOPS * 1e12)
+    if not fused:
+        t_dist = (2 * cells * D / PEAK_F64_MFMA, (4 * cells + io) / PEAK_HBM)
+        t_dp = (chain, alu, 24 * cells / PEAK_HBM)
+        t_rule = (4 * cells * D / PEAK_F32_MFMA, (20 * cells + 2 * io) / PEAK_HBM)
+        per_stage = max(t_dist) + max(t_dp) + max(t_rule)
+        mfma = t_dist[0] + t_rule[0]
+        hbm = t_dist[1] + t_dp[2] + t_rule[1]
+        ideal = max(mfma, hbm, alu, chain)
+    else:
+        t_fwd = (chain, 2 * cells * D / PEAK_F64_MFMA, (8 * cells + io) / PEAK_HBM, alu / 2)
+        t_rev = (chain, 2 * cells * D / PEAK_F64_MFMA + 4 * cells * D / PEAK_F32_MFMA,
+                 (8 * cells + 2 * io) / PEAK_HBM, alu / 2)
+        per_stage = max(t_fwd) + max(t_rev)
+        ideal = max(2 * chain, t_fwd[1] + t_rev[1], t_fwd[2] + t_rev[2])
+    return {"per_stage_us": per_stage * 1e6, "ideal_us": ideal * 1e6}
+
+
+def with_bounds(entry, B, N, M, D, fused):
+    """Adds the bounds and the measured step's fractions of them."""
+    bd = step_bounds(B, N, M, D, fused)
+    t = entry["ms_per_step"] * 1e3
+    entry["bound_per_stage_us"] = bd["per_stage_us"]
+    entry["bound_ideal_us"] = bd["ideal_us"]
+    entry["frac_per_stage"] = bd["per_stage_us"] / t
+    entry["frac_ideal"] = bd["ideal_us"] / t
+    return entry
+
+
 def recorded_traffic():
     """Bytes per launch of the dominant kernel, or None once its sources
     differ from those the counters were taken on."""
@@ -307,6 +362,8 @@ def main():
                                    mode == L.SDTW_MODE_CHECKPOINT)
                 entry[name] = {"ms_per_step": t, "cells_per_s": b_ * n_ * m_ / (t * 1e-3),
                                "peak_mib": pk, "peak_mib_over_io": pko}
+                if mode != L.SDTW_MODE_CHECKPOINT:
+                    with_bounds(entry[name], b_, n_, m_, d_, mode == L.SDTW_MODE_FUSED)
             entry["inference"] = measure_inference(L, torch, x2, y2, g_, 5, 2)
             per_config.append(entry)
             del x2, y2
@@ -330,8 +387,10 @@ def main():
                    "B": B, "N": N, "M": M, "D": D, "gamma": gamma, "mode": "unfused"},
         "peak_mib": peak,
         "peak_mib_over_io": peak_over,
-        "fused": {"ms_per_step": ms_f, "cells_per_s": cells / (ms_f * 1e-3),
-                  "peak_mib": peak_f, "peak_mib_over_io": peak_over_f},
+        "fused": with_bounds({"ms_per_step": ms_f, "cells_per_s": cells / (ms_f * 1e-3),
+                              "peak_mib": peak_f, "peak_mib_over_io": peak_over_f},
+                             B, N, M, D, True),
+        "bounds": with_bounds({"ms_per_step": ms}, B, N, M, D, False),
         "inference": infer,
         "roofline": {"kernel": "both sweeps of the dynamic programme (k_dp_unfused)",
                      "bound": "alu", "achieved": achieved, "peak": PEAK_ALU_TOPS,
