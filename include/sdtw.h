@@ -125,7 +125,9 @@ int sdtw_dist(const float *x, const float *y, float *dist, int64_t B,
 
 /* Forward pass: loss[b] = Soft-DTW(x[b], y[b]) (fp32, [B]).  Leaves in the
  * workspace what sdtw_backward needs (README "Usage": loss_fn(x, y) returns a
- * per-pair loss).  Soft-DTW can be negative (README "Notes"). */
+ * per-pair loss).  Soft-DTW can be negative (README "Notes").  The workspace
+ * needs no clearing beforehand: the forward itself sets the control words and
+ * hand-off rows its kernels and the backward's rely on. */
 int sdtw_forward(const float *x, const float *y, int64_t B, int64_t N,
                  int64_t M, int64_t D, float gamma, int mode, void *workspace,
                  size_t workspace_bytes, float *loss, void *stream);
