@@ -67,7 +67,7 @@ __device__ __forceinline__ unsigned umin_u(unsigned a, unsigned b) { return a < 
 // ---------------------------------------------------------------------------
 // Band wave.
 // ---------------------------------------------------------------------------
-template <bool REV, bool STORE, bool CKPT>
+template <bool REV, bool STORE, bool CKPT, bool SPLIT>
 __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, float* dr, int b,
                                            int band, int lane) {
   const int64_t N = a.N, M = a.M, S = a.S;
@@ -138,28 +138,55 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
     double bottom[kCH];
     double* sp = rbase + (int64_t)t0 * dir;
     double* sp8 = sp + 8 * dir;
-    const bool mask = t0 < 64;
+    // MASK: the chunk holds cells of columns < 0 (only the first 64 steps
+    // do); ALIGN: E also goes to the optional alignment output.  With SPLIT
+    // both are fixed per chunk (four copies of the step loop), so most
+    // chunks carry no per-step test for them: 3-5 % off the reverse sweep,
+    // at the cost of ~40 more VGPRs, which only workgroups of up to eight
+    // waves can afford (nine waves would spill).
+    auto run_steps = [&](auto mask_c, auto align_c) {
+      constexpr bool MASK = decltype(mask_c)::value;
+      constexpr bool ALIGN = decltype(align_c)::value;
 #pragma unroll
-    for (int u = 0; u < kCH; ++u) {
-      const int t = t0 + u;
-      const bool boundary = mask && t < lane;   // column < 0
-      double d = (double)dn[u] * k2;
-      d = boundary ? kBig : d;
-      const double upn = wave_shr1(cur, top[u]);
-      double tp;
-      const double c = softmin2_cell(up, upn, cur, d, tp);
-      up = upn;
-      cur = c;
-      bottom[u] = c;
-      if (!REV) {
-        if (STORE) __builtin_nontemporal_store(c, (u < 8 ? sp : sp8) + (u & 7) * dir);
-        if (CKPT && band_ck && ckp) ckp[t] = c;
-      } else if (!boundary) {
-        const float ev = align_entry(xnm, rn[u], tp);
-        dr[((t - lane) & (kFR - 1)) * kFPitch + lane] = ev;
-        const int col = t - lane;
-        if (alignp && col < M) alignp[M - 1 - col] = ev;
+      for (int u = 0; u < kCH; ++u) {
+        const int t = t0 + u;
+        const bool boundary = MASK && t < lane;   // column < 0
+        double d = (double)dn[u] * k2;
+        if (MASK) d = boundary ? kBig : d;
+        const double upn = wave_shr1(cur, top[u]);
+        double tp;
+        const double c = softmin2_cell(up, upn, cur, d, tp);
+        up = upn;
+        cur = c;
+        bottom[u] = c;
+        if (!REV) {
+          if (STORE) __builtin_nontemporal_store(c, (u < 8 ? sp : sp8) + (u & 7) * dir);
+          if (CKPT && band_ck && ckp) ckp[t] = c;
+        } else if (!boundary) {
+          const float ev = align_entry(xnm, rn[u], tp);
+          dr[((t - lane) & (kFR - 1)) * kFPitch + lane] = ev;
+          if (ALIGN) {
+            const int col = t - lane;
+            if (alignp && col < M) alignp[M - 1 - col] = ev;
+          }
+        }
       }
+    };
+    if constexpr (SPLIT) {
+      const bool want_align = REV && a.align != nullptr;
+      if (t0 < 64) {
+        if (want_align)
+          run_steps(std::true_type{}, std::true_type{});
+        else
+          run_steps(std::true_type{}, std::false_type{});
+      } else {
+        if (want_align)
+          run_steps(std::false_type{}, std::true_type{});
+        else
+          run_steps(std::false_type{}, std::false_type{});
+      }
+    } else {
+      run_steps(std::true_type{}, std::true_type{});   // tests kept per step
     }
     if (lane == 0) lds_publish(&sh.dp_done, (unsigned)q + 1);
 
@@ -539,7 +566,7 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
   __syncthreads();
 
   if (w == 0) {
-    fused_band<REV, !INFER, CKPT>(a, sh, dr, b, band, lane);
+    fused_band<REV, !INFER, CKPT, (HD + HC + 2 <= 8)>(a, sh, dr, b, band, lane);
   } else if (w <= HD) {
     fused_dist_helper<REV, HC>(a, sh, xs, dr, b, w - 1, HD, lane);
   } else if (w < kIO) {
