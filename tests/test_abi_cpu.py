@@ -181,3 +181,27 @@ def test_inference_mode_workspace_and_backward():
     assert ws(40, 500, 600, 3) >= 40 * 8 * 600 * 8
     assert ws(2, 10, 10, 257) == 0
     assert _bwd(mode=L.SDTW_MODE_INFERENCE, D=3) == L.SDTW_ERR_UNSUPPORTED
+
+
+def test_bench_step_bounds():
+    """The per-configuration bounds bench.py reports, recomputed by hand for
+    the headline workload (B=32, N=M=512, D=64): unfused distances 13.7 us
+    (fp64 matrix), sweeps 42.6 us (1023 steps x 100 clocks at 2.4 GHz),
+    chain rule 23.1 us (HBM, 20 B per cell plus twice the inputs); fused two
+    sweeps of 42.6 us each.  And the JSON helpers add the fractions."""
+    import bench
+    B, N, M, D = 32, 512, 512, 64
+    cells = B * N * M
+    t_dist = 2 * cells * D / 78.6e12
+    t_dp = (N + M - 1) * 100 / 2.4e9
+    t_rule = (20 * cells + 2 * 4 * B * (N + M) * D) / 8e12
+    u = bench.step_bounds(B, N, M, D, fused=False)
+    assert abs(u["per_stage_us"] - 1e6 * (t_dist + t_dp + t_rule)) < 1e-6
+    hbm = ((4 * cells + 4 * B * (N + M) * D) + 24 * cells
+           + (20 * cells + 2 * 4 * B * (N + M) * D)) / 8e12
+    assert abs(u["ideal_us"] - 1e6 * max(hbm, t_dp)) < 1e-6
+    f = bench.step_bounds(B, N, M, D, fused=True)
+    assert abs(f["per_stage_us"] - 2e6 * t_dp) < 1e-6
+    e = bench.with_bounds({"ms_per_step": 0.2}, B, N, M, D, False)
+    assert abs(e["frac_per_stage"] - u["per_stage_us"] / 200.0) < 1e-12
+    assert abs(e["frac_ideal"] - u["ideal_us"] / 200.0) < 1e-12
