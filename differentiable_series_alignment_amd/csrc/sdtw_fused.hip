@@ -76,6 +76,11 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
   const int qcount = (int)(sweep_steps(M) / kCH);
   const bool top_ring = band > 0 || a.top_row != nullptr;
   const bool out_used = band + 1 < a.nseg || a.bot_row != nullptr;
+  // A whole-grid training launch hands the bottom row straight to the next
+  // band's self-validating row in global memory (no LDS ring, no copy by
+  // the hand-off wave).
+  const bool direct_out = a.hvalid != 0 && band + 1 < a.nseg && a.bot_row == nullptr;
+  double* const hout = direct_out ? a.H + ((int64_t)b * a.nseg + band) * M : nullptr;
   const unsigned Mu = (unsigned)M;
   const LaneCursor cu = lane_cursor_rows(REV, b, i, lane, N, M, a.nbands, S, a.xrow0);
   double* const rbase = (REV || STORE) ? a.R + cu.base : nullptr;
@@ -200,7 +205,22 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
       }
     }
     if (top_ring && lane == 0) lds_publish(&sh.rd_in, umin_u((unsigned)t0 + kCH, Mu));
-    if (out_used) {
+    if (direct_out) {
+      if (lane == 63) {
+        const int c0 = t0 - 63;                  // column of step t0
+        if (c0 >= 0 && c0 + kCH <= M) {
+#pragma unroll
+          for (int u = 0; u < kCH; ++u)
+            __hip_atomic_store(hout + c0 + u, bottom[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+#pragma unroll
+          for (int u = 0; u < kCH; ++u)
+            if (c0 + u >= 0 && c0 + u < M)
+              __hip_atomic_store(hout + c0 + u, bottom[u], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    } else if (out_used) {
       const int cmax = t0 + kCH - 1 - 63;
       if (cmax >= kRingC) {
         const unsigned need = (unsigned)(cmax - kRingC + 1);
@@ -593,7 +613,8 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
       gr.valid_in = a.hvalid != 0 && !ext_in;
       gr.valid_out = a.hvalid != 0 && !ext_out;
     }
-    segment_io_wave(band > 0 || ext_in, band + 1 < a.nseg || ext_out,
+    const bool direct_out = a.hvalid != 0 && !ext_out;   // the band wave writes the row
+    segment_io_wave(band > 0 || ext_in, (band + 1 < a.nseg && !direct_out) || ext_out,
                     ext_in ? a.full_word : a.ctrl + 2 + sin,
                     ext_out ? a.sink_word : a.ctrl + 2 + sout,
                     ext_in ? a.top_row + (int64_t)b * a.top_ld : a.H + sin * row,
