@@ -318,7 +318,14 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
         return SDTW_ERR_HIP;
       if ((int64_t)cus < L.nseg) return SDTW_ERR_UNSUPPORTED;
     }
-    e = sdtw::launch_zero_u32(ctrl, (int64_t)L.ctrl_words, s);
+    if (L.hcols == 0) {
+      // Whole hand-off rows carry their own validity (set to kHEmpty here;
+      // the checkpointed backward's launches use counts and overwrite them).
+      e = sdtw::launch_clear(ctrl, (int64_t)L.ctrl_words, a.H, B * L.nseg * M, s);
+      a.hvalid = 1;
+    } else {
+      e = sdtw::launch_zero_u32(ctrl, (int64_t)L.ctrl_words, s);
+    }
     if (mode == SDTW_MODE_CHECKPOINT) {
       a.R = nullptr;
       a.ckpt = reinterpret_cast<double*>(ws + L.ckpt);
