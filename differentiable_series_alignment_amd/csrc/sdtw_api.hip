@@ -223,7 +223,13 @@ int backward_checkpointed(const Layout& L, char* ws, const float* x, const float
   // full word tells a range launch that its top row is complete.
   if (e == hipSuccess) e = sdtw::launch_zero_u32(gctrl, 2 + B * G, s);
   if (e == hipSuccess) e = sdtw::launch_fill_u32(full, 1, (unsigned)M, s);
+  // The rows handed between the bands of a group launch carry their own
+  // validity: whole rows come back from the forward set to kHEmpty; after a
+  // forward through rings they are set here.  Every launch leaves them so.
+  if (e == hipSuccess && L.hcols != 0)
+    e = sdtw::launch_clear(nullptr, 0, reinterpret_cast<double*>(ws + L.H), B * G * M, s);
   DPArgs base = dp_args(L, ws, x, y, B, N, M, D, gamma, false);
+  base.hvalid = 1;
   base.ctrl = gctrl;
   base.nbands = (int)G;                      // bands of the X buffer
   base.full_word = full;

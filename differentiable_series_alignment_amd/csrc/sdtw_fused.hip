@@ -76,10 +76,11 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
   const int qcount = (int)(sweep_steps(M) / kCH);
   const bool top_ring = band > 0 || a.top_row != nullptr;
   const bool out_used = band + 1 < a.nseg || a.bot_row != nullptr;
-  // A whole-grid training launch hands the bottom row straight to the next
-  // band's self-validating row in global memory (no LDS ring, no copy by
-  // the hand-off wave).
-  const bool direct_out = a.hvalid != 0 && band + 1 < a.nseg && a.bot_row == nullptr;
+  // With self-validating rows a band hands its bottom row straight to the
+  // next band's row in global memory (no LDS ring, no copy by the hand-off
+  // wave); the last band of a range launch still goes through the hand-off
+  // wave to bot_row.  The hand-off wave makes the same choice.
+  const bool direct_out = a.hvalid != 0 && band + 1 < a.nseg;
   double* const hout = direct_out ? a.H + ((int64_t)b * a.nseg + band) * M : nullptr;
   const unsigned Mu = (unsigned)M;
   const LaneCursor cu = lane_cursor_rows(REV, b, i, lane, N, M, a.nbands, S, a.xrow0);
@@ -614,6 +615,7 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
       gr.valid_out = a.hvalid != 0 && !ext_out;
     }
     const bool direct_out = a.hvalid != 0 && !ext_out;   // the band wave writes the row
+    // (for band + 1 < nseg, ext_out is false: the band wave's own choice)
     segment_io_wave(band > 0 || ext_in, (band + 1 < a.nseg && !direct_out) || ext_out,
                     ext_in ? a.full_word : a.ctrl + 2 + sin,
                     ext_out ? a.sink_word : a.ctrl + 2 + sout,
