@@ -31,7 +31,6 @@ constexpr int kFR = 128;     // distance/E ring columns per band (8 blocks of 16
 constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
 constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
 constexpr int kRevHelpD = 2; // distance helpers, reverse sweep (3 for 64 < D <= 128)
-constexpr int kRevHelpC = 2; // chain-rule helpers, reverse sweep (4 beyond D = 64)
 constexpr int kRevHelpCMax = 4;
 constexpr int kYB = 16;      // feature steps (of 4) per batch of y loads
 
@@ -59,6 +58,7 @@ struct FusedShared {
   unsigned d_ready;               // distance blocks published, in order
   unsigned dp_done;               // chunks completed by the band wave
   unsigned e_free[kRevHelpCMax];  // blocks released by each chain-rule helper
+  unsigned x_done[kRevHelpCMax];  // dx partials handed over (helper pairs)
   unsigned ticket;
 };
 
@@ -343,15 +343,29 @@ __device__ __forceinline__ void fused_dist_helper(const DPArgs& a, FusedShared& 
 }
 
 // ---------------------------------------------------------------------------
-// Chain-rule helper c (reverse sweep): columns [c*DC, (c+1)*DC) of D.  The y
-// rows of block p+1 are requested while block p is processed and staged in
-// the helper's LDS area `ys` (two blocks), so a block never waits on memory.
+// Chain-rule helper c of nhc (reverse sweep).  D is cut into slices of DC
+// columns; when there are helpers to spare, two helpers share a slice and
+// take its blocks in turn (each keeps its part of dx; the second hands its
+// part over through LDS at the end, the first adds it and writes dx, always
+// in that order).  The y rows of a helper's next block are requested while
+// a block is processed and staged in the helper's LDS area `ys` (two
+// blocks), so a block never waits on memory.
 // ---------------------------------------------------------------------------
+__host__ __device__ inline int chain_phases(int64_t D, int DC, int nhc) {
+  const int nsl = (int)((D + DC - 1) / DC);
+  const int nph = nhc / nsl;
+  return nph >= 2 ? 2 : 1;
+}
+// LDS floats for the dx hand-over between the helpers of a slice.
+__host__ __device__ inline int chain_xch_floats(int64_t D, int DC, int nhc) {
+  return chain_phases(D, DC, nhc) > 1 ? (int)((D + DC - 1) / DC) * 64 * (32 * (DC / 32) + 2) : 0;
+}
+
 template <int DC>
 __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared& sh,
                                                    const float* xs, const float* dr,
-                                                   float* ys, int b, int band, int c,
-                                                   int lane) {
+                                                   float* ys, float* xch, int b, int band,
+                                                   int c, int nhc, int lane) {
   constexpr int NT = DC / 32;
   constexpr int YP = DC + 2;            // staged row pitch
   constexpr int YL = 16 * DC / 64;      // staged values per lane per block
@@ -359,12 +373,17 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
   const int P = fused_pitch(D);
   const int qcount = (int)(sweep_steps(M) / kCH);
   const int64_t r0 = a.row0 + (int64_t)band * 64;
-  const int64_t dbeg = (int64_t)c * DC;
+  const int nsl = (int)((D + DC - 1) / DC);
+  const int nph = chain_phases(D, DC, nhc);
+  const int slice = c % nsl, phase = c / nsl;
+  const int64_t dbeg = (int64_t)slice * DC;
   const bool want_gx = a.gx != nullptr, want_gy = a.gy != nullptr;
-  if ((!want_gx && !want_gy) || dbeg >= D) {
+  if ((!want_gx && !want_gy) || phase >= nph || dbeg >= D) {
     if (lane == 0) lds_publish(&sh.e_free[c], (unsigned)qcount);
     return;
   }
+  // Blocks of the other phase are never this helper's to release.
+  if (phase > 0 && lane == 0) lds_publish(&sh.e_free[c], (unsigned)phase);
   const int64_t dend = dbeg + DC < D ? dbeg + DC : D;
   const float g2 = 2.f * a.gl[b];
   const float* yb = a.y + (int64_t)b * M * D;
@@ -393,8 +412,8 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
       yreg[k] = yb[oc * D + (dc < D ? dc : D - 1)];
     }
   };
-  auto stage_y = [&](int p) {
-    float* yd = ys + (p & 1) * 16 * YP;
+  auto stage_y = [&](int k) {             // k: the helper's own block count
+    float* yd = ys + (k & 1) * 16 * YP;
 #pragma unroll
     for (int k = 0; k < YL; ++k) {
       const int idx = lane + 64 * k;
@@ -403,18 +422,18 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
   };
 
   const int nreal = (int)((M + kCH - 1) / kCH);
-  load_y(0);
+  load_y(phase);
   stage_y(0);
   unsigned seen_dp = 0;
-  for (int p = 0; p < nreal; ++p) {
-    const bool more = p + 1 < nreal;
-    if (more) load_y(p + 1);
+  for (int p = phase, k = 0; p < nreal; p += nph, ++k) {
+    const bool more = p + nph < nreal;
+    if (more) load_y(p + nph);
     // Block p is complete once the band wave has finished chunk p+4 (the
     // last chunk completes every remaining block).
     const unsigned need = umin_u((unsigned)p + 5, (unsigned)qcount);
     if (seen_dp < need) seen_dp = lds_wait_ge(&sh.dp_done, need);
     const int64_t c0 = (int64_t)p * kCH;
-    const float* yc = ys + (p & 1) * 16 * YP;
+    const float* yc = ys + (k & 1) * 16 * YP;
     if (want_gx) {
       // dx += E[64 x 16] . Y[16 x DC] on v_mfma_f32_32x32x2_f32.  Up to
       // DC = 64 the block's E entries are read as one batch (unconditional
@@ -493,9 +512,9 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
       cs += __shfl_xor(cs, 16, 64);
       cs += __shfl_xor(cs, 32, 64);
     }
-    // Block p+1's y rows go into the other staging slot (last read in block
-    // p-1) before this block's atomics are issued.
-    if (more) stage_y(p + 1);
+    // The next block's y rows go into the other staging slot (last read in
+    // the block before this one) before this block's atomics are issued.
+    if (more) stage_y(k + 1);
     if (want_gy) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -514,9 +533,36 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
         }
       }
     }
-    if (lane == 0) lds_publish(&sh.e_free[c], (unsigned)p + 1);
+    if (lane == 0) lds_publish(&sh.e_free[c], umin_u((unsigned)(p + nph), (unsigned)qcount));
   }
   if (lane == 0) lds_publish(&sh.e_free[c], (unsigned)qcount);
+  if (want_gx && nph > 1) {
+    // The second helper of the slice hands its part of dx (products and row
+    // sums) to the first, which adds it to its own.
+    constexpr int XW = 32 * NT + 2;
+    float* xd = xch + slice * 64 * XW;
+    if (phase == 1) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) xd[((rt * NT + t) * 16 + e) * 64 + lane] = gxa[rt][t][e];
+        xd[(32 * NT + rt) * 64 + lane] = rsum[rt];
+      }
+      if (lane == 0) lds_publish(&sh.x_done[slice], 1u);
+      return;
+    }
+    (void)lds_wait_ge(&sh.x_done[slice], 1u);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) gxa[rt][t][e] += xd[((rt * NT + t) * 16 + e) * 64 + lane];
+      rsum[rt] += xd[(32 * NT + rt) * 64 + lane];
+    }
+  }
 
   if (want_gx) {
 #pragma unroll
@@ -560,7 +606,7 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
   if (threadIdx.x == 0) {
     sh.wr_in = sh.rd_in = sh.wr_out = sh.rd_out = 0u;
     sh.d_ready = sh.dp_done = 0u;
-    for (int c = 0; c < kRevHelpCMax; ++c) sh.e_free[c] = 0u;
+    for (int c = 0; c < kRevHelpCMax; ++c) sh.e_free[c] = sh.x_done[c] = 0u;
   }
   __syncthreads();
   const unsigned ticket = sh.ticket;
@@ -594,7 +640,8 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
     if (REV) {
       const int c = w - 1 - HD;
       float* ys = dr + kFR * kFPitch + c * chain_y_floats(DC);
-      fused_chain_helper<DC>(a, sh, xs, dr, ys, b, band, c, lane);
+      float* xch = dr + kFR * kFPitch + HC * chain_y_floats(DC);
+      fused_chain_helper<DC>(a, sh, xs, dr, ys, xch, b, band, c, HC, lane);
     }
   } else {
     const int64_t pb = (int64_t)b * a.nseg;
@@ -631,7 +678,8 @@ template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC>
 static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcols = 0) {
   auto kern = k_dp_fused<REV, INFER, CKPT, HD, HC, DC>;
   static_assert(HC <= kRevHelpCMax, "chain-rule helpers");
-  const size_t lds = fused_lds_bytes(a.D, REV ? DC : 0, HC);
+  const size_t lds = fused_lds_bytes(a.D, REV ? DC : 0, HC) +
+                     (REV ? (size_t)chain_xch_floats(a.D, DC, HC) * 4 : 0);
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -644,14 +692,15 @@ static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcol
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
   if (!reverse) return launch_fused_one<false, false, false, kFwdHelpD, 0, 32>(a, s);
-  // Each chain-rule helper owns DC columns of D: two of 32 columns up to
-  // D = 64, four of 32 up to 128, then four of 64 (wider helpers would not
-  // keep their accumulators in registers, and more helpers share the work
-  // of a block).
+  // Four chain-rule helpers on slices of DC columns of D: 32 up to D = 128,
+  // then 64 (wider helpers would not keep their accumulators in registers).
+  // Up to D = 64 the slices are one or two, and two helpers share each
+  // slice's blocks (the helpers, not the band wave, set the pace there).
   // Up to D = 64 two distance helpers keep ahead of the band wave; beyond,
   // a third one (32x1024x1024, D=128: 826 us against 891; with 64-column
   // chain helpers a third would push the registers into scratch).
-  if (a.D <= 2 * 32) return launch_fused_one<true, false, false, kRevHelpD, kRevHelpC, 32>(a, s);
+  if (a.D <= 2 * 32)
+    return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 32>(a, s);
   if (a.D <= 4 * 32)
     return launch_fused_one<true, false, false, kRevHelpD + 1, kRevHelpCMax, 32>(a, s);
   return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 64>(a, s);
