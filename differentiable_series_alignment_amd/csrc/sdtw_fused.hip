@@ -344,21 +344,21 @@ __device__ __forceinline__ void fused_dist_helper(const DPArgs& a, FusedShared& 
 
 // ---------------------------------------------------------------------------
 // Chain-rule helper c of nhc (reverse sweep).  D is cut into slices of DC
-// columns; when there are helpers to spare, two helpers share a slice and
-// take its blocks in turn (each keeps its part of dx; the second hands its
-// part over through LDS at the end, the first adds it and writes dx, always
-// in that order).  The y rows of a helper's next block are requested while
+// columns; when there are helpers to spare, the helpers of a slice (its
+// "phases") take its blocks in turn (each keeps its part of dx; the others
+// hand their parts over through LDS at the end, and the first adds them in
+// phase order and writes dx).  The y rows of a helper's next block are requested while
 // a block is processed and staged in the helper's LDS area `ys` (two
 // blocks), so a block never waits on memory.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int chain_phases(int64_t D, int DC, int nhc) {
   const int nsl = (int)((D + DC - 1) / DC);
   const int nph = nhc / nsl;
-  return nph >= 2 ? 2 : 1;
+  return nph < 1 ? 1 : nph;
 }
 // LDS floats for the dx hand-over between the helpers of a slice.
 __host__ __device__ inline int chain_xch_floats(int64_t D, int DC, int nhc) {
-  return chain_phases(D, DC, nhc) > 1 ? (int)((D + DC - 1) / DC) * 64 * (32 * (DC / 32) + 2) : 0;
+  return (int)((D + DC - 1) / DC) * (chain_phases(D, DC, nhc) - 1) * 64 * (32 * (DC / 32) + 2);
 }
 
 template <int DC>
@@ -537,11 +537,12 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
   }
   if (lane == 0) lds_publish(&sh.e_free[c], (unsigned)qcount);
   if (want_gx && nph > 1) {
-    // The second helper of the slice hands its part of dx (products and row
-    // sums) to the first, which adds it to its own.
+    // The other helpers of the slice hand their parts of dx (products and
+    // row sums) to the first, which adds them to its own in phase order.
     constexpr int XW = 32 * NT + 2;
-    float* xd = xch + slice * 64 * XW;
-    if (phase == 1) {
+    float* const xs0 = xch + slice * (nph - 1) * 64 * XW;
+    if (phase > 0) {
+      float* xd = xs0 + (phase - 1) * 64 * XW;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
@@ -550,17 +551,20 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
           for (int e = 0; e < 16; ++e) xd[((rt * NT + t) * 16 + e) * 64 + lane] = gxa[rt][t][e];
         xd[(32 * NT + rt) * 64 + lane] = rsum[rt];
       }
-      if (lane == 0) lds_publish(&sh.x_done[slice], 1u);
+      if (lane == 0) lds_publish(&sh.x_done[c], 1u);
       return;
     }
-    (void)lds_wait_ge(&sh.x_done[slice], 1u);
+    for (int f = 1; f < nph; ++f) {
+      const float* xd = xs0 + (f - 1) * 64 * XW;
+      (void)lds_wait_ge(&sh.x_done[slice + f * nsl], 1u);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) gxa[rt][t][e] += xd[((rt * NT + t) * 16 + e) * 64 + lane];
-      rsum[rt] += xd[(32 * NT + rt) * 64 + lane];
+          for (int e = 0; e < 16; ++e) gxa[rt][t][e] += xd[((rt * NT + t) * 16 + e) * 64 + lane];
+        rsum[rt] += xd[(32 * NT + rt) * 64 + lane];
+      }
     }
   }
 
@@ -694,8 +698,8 @@ hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   if (!reverse) return launch_fused_one<false, false, false, kFwdHelpD, 0, 32>(a, s);
   // Four chain-rule helpers on slices of DC columns of D: 32 up to D = 128,
   // then 64 (wider helpers would not keep their accumulators in registers).
-  // Up to D = 64 the slices are one or two, and two helpers share each
-  // slice's blocks (the helpers, not the band wave, set the pace there).
+  // Up to D = 64 the slices are one or two, and four or two helpers share
+  // each slice's blocks (the helpers, not the band wave, set the pace there).
   // Up to D = 64 two distance helpers keep ahead of the band wave; beyond,
   // a third one (32x1024x1024, D=128: 826 us against 891; with 64-column
   // chain helpers a third would push the registers into scratch).
