@@ -518,7 +518,7 @@ def test_small_gamma_finite(S):
     assert np.isfinite(l).all() and np.isfinite(gx).all() and np.isfinite(gy).all()
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 3])
 def test_workspace_contents_do_not_matter(S, mode):
     """Rows handed between workgroups carry their own validity and every
     forward sets them: a workspace left holding zeros (which read as valid
@@ -554,3 +554,26 @@ def test_workspace_contents_do_not_matter(S, mode):
     torch.testing.assert_close(runs[1][0], runs[0][0], rtol=0, atol=0)
     torch.testing.assert_close(runs[1][1][0], runs[0][1][0], rtol=0, atol=0)
     torch.testing.assert_close(runs[1][1][1], runs[0][1][1], rtol=1e-5, atol=1e-7)
+
+
+def test_inference_workspace_contents_do_not_matter(S):
+    """The loss-only forward with whole hand-off rows: a workspace holding
+    zeros or all-ones bytes gives bitwise the same loss, equal to the
+    training forward's."""
+    from differentiable_series_alignment_amd import _lib as L
+    B, N, M, D = 2, 300, 150, 8
+    x, y = pair_batch(B, N, M, D, seed=6)
+    x, y = x.to(DEV), y.to(DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    losses = []
+    for mode, fill in ((L.SDTW_MODE_INFERENCE, 0), (L.SDTW_MODE_INFERENCE, 255),
+                       (L.SDTW_MODE_UNFUSED, 0)):
+        nb = L.sdtw_workspace_bytes(B, N, M, D, mode)
+        ws = torch.full((nb,), fill, dtype=torch.uint8, device=DEV)
+        loss = torch.empty(B, device=DEV)
+        L.check(L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, 1.0, mode,
+                               ws.data_ptr(), nb, loss.data_ptr(), s), "sdtw_forward")
+        torch.cuda.synchronize()
+        losses.append(loss)
+    torch.testing.assert_close(losses[1], losses[0], rtol=0, atol=0)
+    torch.testing.assert_close(losses[2], losses[0], rtol=0, atol=0)
