@@ -141,7 +141,23 @@ def parse():
     p.add_argument("--counter-pass", action="store_true",
                    help="for rocprofv3 --pmc runs: three headline steps and three "
                         "copies of 256 MiB (the counters' calibration), no output")
+    p.add_argument("--profile-workload", default=None, metavar="B,N,M,D,GAMMA",
+                   help="for rocprofv3 --kernel-trace runs: a few unfused and "
+                        "fused steps of this workload, one summary line each")
     return p.parse_args()
+
+
+def profile_workload(torch, L, pair_batch, spec, steps):
+    """Unfused and fused fwd+bwd steps of one workload (kernel traces of
+    configurations other than the headline one)."""
+    b_, n_, m_, d_, g_ = spec.split(",")
+    B, N, M, D, gamma = int(b_), int(n_), int(m_), int(d_), float(g_)
+    xc, yc = pair_batch(B, N, M, D, seed=0)
+    x, y = xc.to("cuda:0"), yc.to("cuda:0")
+    for name, mode in (("unfused", L.SDTW_MODE_UNFUSED), ("fused", L.SDTW_MODE_FUSED)):
+        ms = measure(L, torch, x, y, gamma, mode, steps, 2)[0]
+        print(f"B={B} N={N} M={M} D={D} gamma={gamma} {name}: {ms:.3f} ms per step",
+              flush=True)
 
 
 def counter_pass(torch, L, x, y, gamma):
@@ -307,6 +323,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.profile_workload:
+        profile_workload(torch, L, pair_batch, args.profile_workload, 5)
+        return
     dev = torch.device("cuda:0")
     W = WORKLOAD
     B, N, M, D, gamma = W["B"], W["N"], W["M"], W["D"], W["gamma"]
