@@ -205,3 +205,28 @@ def test_bench_step_bounds():
     e = bench.with_bounds({"ms_per_step": 0.2}, B, N, M, D, False)
     assert abs(e["frac_per_stage"] - u["per_stage_us"] / 200.0) < 1e-12
     assert abs(e["frac_ideal"] - u["ideal_us"] / 200.0) < 1e-12
+
+
+def test_profile_summaries_name_their_commands():
+    """Every rocprofv3 summary under profiles/ states the command that made
+    it, and that command runs committed files only (bench.py with one of its
+    own options)."""
+    import sys
+    import bench
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    prof = os.path.join(root, "profiles")
+    names = sorted(f for f in os.listdir(prof) if f.endswith(".md"))
+    assert names
+    for name in names:
+        text = open(os.path.join(prof, name)).read()
+        cmds = re.findall(r"rocprofv3 [^\n]*-- python3 bench\.py([^\n]*)", text)
+        assert cmds, name
+        for tail in cmds:
+            argv = sys.argv
+            try:
+                sys.argv = ["bench.py"] + tail.split()
+                bench.parse()
+            except SystemExit as e:   # argparse rejects an unknown option
+                raise AssertionError(f"{name}: bench.py {tail}") from e
+            finally:
+                sys.argv = argv
