@@ -112,6 +112,15 @@ def test_seeds(O, S, seed):
     check_against_oracle(O, S, x, y, 0.5, what=f"seed {seed}")
 
 
+@pytest.mark.parametrize("seed", [1, 2])
+@pytest.mark.parametrize("B,N,M,D", [(2, 16, 16, 1), (32, 512, 512, 64), (32, 256, 256, 64)])
+def test_seeds_on_workloads(O, S, seed, B, N, M, D):
+    """Seeds 1 and 2 on the tiny, headline and feature-sweep (D=64) shapes,
+    every pair against the oracle, unfused mode."""
+    x, y = pair_batch(B, N, M, D, seed=seed)
+    check_against_oracle(O, S, x, y, 1.0, what=f"{B}x{N}x{M} D={D} seed {seed}")
+
+
 def test_alignment_matrix(O, S):
     x, y = pair_batch(2, 70, 45, 4, seed=21)
     l, E = S.alignment(x.to(DEV), y.to(DEV), 0.7)
@@ -165,9 +174,12 @@ def test_feature_sweep(O, S, D, fused):
 @pytest.mark.parametrize("gamma", [1.0, 0.01])
 @pytest.mark.parametrize("fused", [False, True])
 def test_long_sequences(O, S, N, M, gamma, fused):
-    """B=32, D=128 at full size on the GPU; the oracle checks sampled pairs
-    (first and last, or the first at 4096^2) and every pair must be finite
-    with gradients summing to zero over both sequences."""
+    """B=32, D=128 at full size on the GPU.  Sampling rule (the oracle would
+    take minutes per pair at 4096^2): the oracle checks pairs 0 and 31
+    elementwise, or pair 0 alone at 4096x4096; every one of the 32 pairs must
+    be finite and have gradients summing to zero over both sequences
+    (translation invariance of the squared distance), which holds at any
+    size."""
     x, y = pair_batch(32, N, M, 128, seed=0)
     pairs = [0] if N * M > 5_000_000 else [0, 31]
     l, gx, gy = check_against_oracle(O, S, x, y, gamma, fused=fused, pairs=pairs,
@@ -311,6 +323,26 @@ def test_checkpoint_against_oracle(O, S, B, N, M, D, gamma):
     assert_loss(l, l0, "checkpoint")
     assert_grad(gx, gx0, "checkpoint dx")
     assert_grad(gy, gy0, "checkpoint dy")
+
+
+@pytest.mark.parametrize("gamma", [0.01])
+def test_checkpoint_long_unequal_against_oracle(O, S, gamma):
+    """Checkpointed training at the long unequal workload it exists for
+    (B=32, N=4096, M=1000, D=128, gamma=0.01): the first and last pairs
+    against the oracle, every pair finite with gradients summing to zero
+    over both sequences (translation invariance)."""
+    x, y = pair_batch(32, 4096, 1000, 128, seed=0)
+    l, gx, gy = gpu_value_and_grad(S, x, y, gamma, checkpoint=True)
+    assert np.isfinite(l).all() and np.isfinite(gx).all() and np.isfinite(gy).all()
+    idx = [0, 31]
+    l0, gx0, gy0 = O.value_and_grad(x[idx].numpy(), y[idx].numpy(), gamma,
+                                    np.full(2, 1.0 / 32))
+    assert_loss(l[idx], l0, "checkpoint 4096x1000")
+    assert_grad(gx[idx], gx0, "checkpoint 4096x1000 dx")
+    assert_grad(gy[idx], gy0, "checkpoint 4096x1000 dy")
+    s = gx.sum(axis=1) + gy.sum(axis=1)
+    scale = np.abs(gx).sum(axis=1) + np.abs(gy).sum(axis=1) + 1e-30
+    assert (np.abs(s) <= 1e-4 * scale).all()
 
 
 def test_checkpoint_workspace_is_smaller():
@@ -496,6 +528,41 @@ def test_inference_mode_matches_training_loss(S, B, N, M, D):
     with torch.no_grad():
         torch.testing.assert_close(S.soft_dtw(x, y, 0.6), out[L.SDTW_MODE_UNFUSED],
                                    rtol=0, atol=0)
+
+
+def inference_loss(S, x, y, gamma):
+    """Loss through the C ABI in inference mode (no state kept)."""
+    from differentiable_series_alignment_amd import _lib as L
+    B, N, D = x.shape
+    M = y.shape[1]
+    xd, yd = x.to(DEV), y.to(DEV)
+    nb = L.sdtw_workspace_bytes(B, N, M, D, L.SDTW_MODE_INFERENCE)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    loss = torch.empty(B, device=DEV)
+    L.check(L.sdtw_forward(xd.data_ptr(), yd.data_ptr(), B, N, M, D, gamma,
+                           L.SDTW_MODE_INFERENCE, ws.data_ptr(), nb, loss.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream), "sdtw_forward")
+    torch.cuda.synchronize()
+    return loss.cpu().double().numpy()
+
+
+@pytest.mark.parametrize("B,N,M,D,pairs", [
+    (3, 70, 45, 3, None),            # whole hand-off rows
+    (3, 1100, 700, 5, None),         # 512-column rings
+    (9, 2048, 8192, 2, [0, 8]),      # rings, more bands than the GPU has CUs
+])
+@pytest.mark.parametrize("gamma", [1.0, 0.1])
+def test_inference_mode_against_oracle(O, S, B, N, M, D, pairs, gamma):
+    """The loss-only inference mode (the README's "When to Use Each Mode":
+    speed-critical inference) against the oracle's loss on random N(0,1)
+    inputs, for whole-row and ring hand-off; the largest shape checks the
+    first and last pairs."""
+    x, y = pair_batch(B, N, M, D, seed=B * 13 + N + M + D)
+    l = inference_loss(S, x, y, gamma)
+    assert np.isfinite(l).all()
+    idx = list(range(B)) if pairs is None else pairs
+    l0, _, _ = O.value_and_grad(x[idx].numpy(), y[idx].numpy(), gamma)
+    assert_loss(l[idx], l0, f"inference {B}x{N}x{M} g={gamma}")
 
 
 def test_normalized_is_one_batch(S):

@@ -387,3 +387,57 @@ def test_block_waves_recipe():
     assert ((frac > 0.35) & (frac < 0.65)).all()
     resid = X - torch.where(X > 0, 1.0, -1.0)
     assert 0.07 < resid.std().item() < 0.13
+
+
+def test_barycenter_loop_matches_torch_optim_loop(O):
+    """The oracle's barycenter loop assembled from pieces that are pinned one
+    by one (objective and gradient, clipping, cosine schedule, Adam) against
+    an independent loop built from torch's own optimiser pieces in fp64:
+    torch.optim.Adam, CosineAnnealingLR and clip_grad_norm_, driven by the
+    same objective.  Both keep the iterate in fp32 between steps and take
+    the Adam step in fp64 (the oracle's reading), so the two histories and
+    the final iterate must agree to rounding (1e-12)."""
+    X = block_waves(4, 30, 2, seed=3).numpy()
+    T, lr, clip = 40, 0.1, 1.0
+    z_or, h_or = O.barycenter(X, 1.0, T, lr, cosine=True, clip=clip)
+    z = torch.tensor(X.astype(np.float64).mean(axis=0), requires_grad=True)
+    opt = torch.optim.Adam([z], lr=lr)
+    sched = torch.optim.lr_scheduler.CosineAnnealingLR(opt, T_max=T)
+    hist = []
+    for _ in range(T):
+        zf = z.detach().numpy().astype(np.float32)
+        f, g = O.barycenter_objective_and_grad(zf, X, 1.0)
+        hist.append(f)
+        with torch.no_grad():
+            z.copy_(torch.from_numpy(zf.astype(np.float64)))
+        z.grad = torch.from_numpy(np.asarray(g, dtype=np.float64).copy())
+        torch.nn.utils.clip_grad_norm_([z], clip)
+        opt.step()
+        sched.step()
+    np.testing.assert_allclose(np.array(hist), np.array(h_or), rtol=1e-12, atol=0)
+    np.testing.assert_allclose(z.detach().numpy().astype(np.float32), z_or, rtol=1e-6,
+                               atol=1e-7)
+
+
+@pytest.mark.parametrize("gamma", [1.0, 0.05])
+def test_value_and_grad_matches_composition(O, gamma):
+    """The fused fp64 entry point that the GPU tests compare against (the
+    distance rounded once to fp32, forward, log-space backward, chain rule,
+    all inside one C call) against the composition of the separately pinned
+    steps: sqeuclid(round_f32) -> forward -> backward -> sqeuclid_vjp."""
+    x, y = pair_batch(3, 23, 17, 5, seed=4)
+    xs, ys = x.numpy(), y.numpy()
+    gl = np.array([0.5, -1.25, 2.0])
+    l0, gx0, gy0, E0 = O.value_and_grad(xs, ys, gamma, gl, round_dist_f32=True,
+                                        want_E=True)
+    dist = O.sqeuclid(xs, ys, round_f32=True)
+    loss, R = O.forward(dist, gamma)
+    E = O.backward(dist, R, gamma)
+    gx, gy = O.sqeuclid_vjp(xs, ys, E, gl)
+    np.testing.assert_allclose(l0, loss, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(E0, E, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(gx0, gx, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gy0, gy, rtol=1e-12, atol=1e-13)
+    # and the unrounded reading differs from it (the flag is not ignored)
+    l1, _, _ = O.value_and_grad(xs, ys, gamma, gl, round_dist_f32=False)
+    assert np.any(l1 != l0)
