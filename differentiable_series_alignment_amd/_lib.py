@@ -39,6 +39,7 @@ SIGNATURES = {
                           ctypes.c_size_t, _P, _P]),
     "sdtw_backward": (_I, [_P, _P, _I64, _I64, _I64, _I64, _F, _I, _P,
                            ctypes.c_size_t, _P, _P, _P, _P, _P]),
+    "sdtw_forward_static": (_I, [_P, _P, _I64, _I64, _I64, _I64, _F, _P, _P]),
     "sdtw_timing": (_I, [_I]),
     "sdtw_timing_collect": (_I, [ctypes.POINTER(ctypes.c_char_p),
                                  ctypes.POINTER(ctypes.c_float), _I]),
@@ -100,6 +101,14 @@ def sdtw_backward(x: int, y: int, B: int, N: int, M: int, D: int, gamma: float,
     return lib().sdtw_backward(x, y, B, N, M, D, gamma, mode, workspace,
                                workspace_bytes, grad_loss, grad_x, grad_y, align,
                                stream)
+
+
+SDTW_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def sdtw_forward_static(x: int, y: int, B: int, N: int, M: int, D: int, gamma: float,
+                        loss: int, stream: int = 0) -> int:
+    return lib().sdtw_forward_static(x, y, B, N, M, D, gamma, loss, stream)
 
 
 def sdtw_timing(on: bool) -> int:

@@ -268,37 +268,12 @@ int check_ws(const Layout& L, void* ws, size_t bytes) {
 
 }  // namespace
 
-extern "C" {
+namespace sdtw {
 
-int sdtw_abi_version(void) { return SDTW_ABI_VERSION; }
-
-const char* sdtw_status_string(int status) {
-  switch (status) {
-    case SDTW_OK: return "ok";
-    case SDTW_ERR_INVALID_ARG: return "invalid argument";
-    case SDTW_ERR_WORKSPACE: return "workspace too small";
-    case SDTW_ERR_HIP: return "HIP runtime error";
-    case SDTW_ERR_UNSUPPORTED: return "unsupported request";
-    default: return "unknown status";
-  }
-}
-
-size_t sdtw_workspace_bytes(int64_t B, int64_t N, int64_t M, int64_t D, int mode) {
-  Layout L;
-  if (!make_layout(B, N, M, D, mode, &L)) return 0;
-  return L.total;
-}
-
-int sdtw_dist(const float* x, const float* y, float* dist, int64_t B, int64_t N,
-              int64_t M, int64_t D, void* stream) {
-  if (!x || !y || !dist || !sizes_ok(B, N, M, D)) return SDTW_ERR_INVALID_ARG;
-  hipError_t e = sdtw::launch_dist(x, y, dist, B, N, M, D, (hipStream_t)stream);
-  return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
-}
-
-int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M,
-                 int64_t D, float gamma, int mode, void* workspace,
-                 size_t workspace_bytes, float* loss, void* stream) {
+// Body of sdtw_forward (also behind the allocation-free loss-only entry point).
+int forward_impl(const float* x, const float* y, int64_t B, int64_t N, int64_t M, int64_t D,
+                 float gamma, int mode, void* workspace, size_t workspace_bytes, float* loss,
+                 void* stream) {
   if (!x || !y || !loss || !gamma_ok(gamma)) return SDTW_ERR_INVALID_ARG;
   Layout L;
   if (!make_layout(B, N, M, D, mode, &L)) return SDTW_ERR_INVALID_ARG;
@@ -354,6 +329,43 @@ int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M
     if (e == hipSuccess) e = sdtw::launch_dp_both(a, s);
   }
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
+}
+
+}  // namespace sdtw
+
+extern "C" {
+
+int sdtw_abi_version(void) { return SDTW_ABI_VERSION; }
+
+const char* sdtw_status_string(int status) {
+  switch (status) {
+    case SDTW_OK: return "ok";
+    case SDTW_ERR_INVALID_ARG: return "invalid argument";
+    case SDTW_ERR_WORKSPACE: return "workspace too small";
+    case SDTW_ERR_HIP: return "HIP runtime error";
+    case SDTW_ERR_UNSUPPORTED: return "unsupported request";
+    default: return "unknown status";
+  }
+}
+
+size_t sdtw_workspace_bytes(int64_t B, int64_t N, int64_t M, int64_t D, int mode) {
+  Layout L;
+  if (!make_layout(B, N, M, D, mode, &L)) return 0;
+  return L.total;
+}
+
+int sdtw_dist(const float* x, const float* y, float* dist, int64_t B, int64_t N,
+              int64_t M, int64_t D, void* stream) {
+  if (!x || !y || !dist || !sizes_ok(B, N, M, D)) return SDTW_ERR_INVALID_ARG;
+  hipError_t e = sdtw::launch_dist(x, y, dist, B, N, M, D, (hipStream_t)stream);
+  return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
+}
+
+int sdtw_forward(const float* x, const float* y, int64_t B, int64_t N, int64_t M,
+                 int64_t D, float gamma, int mode, void* workspace,
+                 size_t workspace_bytes, float* loss, void* stream) {
+  return sdtw::forward_impl(x, y, B, N, M, D, gamma, mode, workspace, workspace_bytes, loss,
+                            stream);
 }
 
 int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t M,

@@ -104,6 +104,21 @@ class TimedLaunch {
   hipEvent_t end_ = nullptr;
 };
 
+// While one exists on a host thread, launches on that thread are not timed
+// (the allocation-free entry point creates no events).
+class NoTimingScope {
+ public:
+  NoTimingScope();
+  ~NoTimingScope();
+  NoTimingScope(const NoTimingScope&) = delete;
+  NoTimingScope& operator=(const NoTimingScope&) = delete;
+};
+
+// Body of sdtw_forward (include/sdtw.h), also behind sdtw_forward_static.
+int forward_impl(const float* x, const float* y, int64_t B, int64_t N, int64_t M, int64_t D,
+                 float gamma, int mode, void* workspace, size_t workspace_bytes, float* loss,
+                 void* stream);
+
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
                        int64_t N, int64_t M, int64_t D, hipStream_t stream);

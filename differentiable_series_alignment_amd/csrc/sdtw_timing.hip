@@ -25,11 +25,15 @@ struct TimingState {
 };
 
 TimingState g_timing;
+thread_local int t_no_timing = 0;
 
 }  // namespace
 
+NoTimingScope::NoTimingScope() { ++t_no_timing; }
+NoTimingScope::~NoTimingScope() { --t_no_timing; }
+
 TimedLaunch::TimedLaunch(const char* name, hipStream_t s) : stream_(s), index_(-1) {
-  if (!g_timing.on) return;
+  if (!g_timing.on || t_no_timing) return;
   TimingRecord r{name, nullptr, nullptr, false};
   if (hipEventCreate(&r.begin) != hipSuccess) return;
   if (hipEventCreate(&r.end) != hipSuccess) {

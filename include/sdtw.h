@@ -73,9 +73,12 @@
  *    without host synchronisation.  Arguments are validated on the host before
  *    any HIP call; invalid calls return an error and enqueue nothing.  Faults
  *    inside kernels surface at the caller's next synchronisation.
- *  - The library never allocates device memory and keeps no global mutable
- *    state; the caller owns every buffer.  Calls on distinct workspaces may
- *    run concurrently on distinct streams.  Nothing is printed.
+ *  - The library never allocates device memory; the caller owns every buffer
+ *    passed in.  Process-wide state is limited to: the launch-timing record
+ *    list (sdtw_timing, off by default, guarded by a mutex) and the
+ *    per-device scratch array of sdtw_forward_static with its resolved
+ *    addresses.  Calls on distinct workspaces may run concurrently on
+ *    distinct streams.  Nothing is printed.
  */
 #ifndef SDTW_H
 #define SDTW_H
@@ -148,6 +151,28 @@ int sdtw_backward(const float *x, const float *y, int64_t B, int64_t N,
                   int64_t M, int64_t D, float gamma, int mode, void *workspace,
                   size_t workspace_bytes, const float *grad_loss,
                   float *grad_x, float *grad_y, float *align, void *stream);
+
+/* Size of the device array behind sdtw_forward_static (per GPU). */
+#define SDTW_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* Loss-only forward (the same computation and result, bitwise, as
+ * sdtw_forward in SDTW_MODE_INFERENCE) that allocates nothing and takes no
+ * workspace: its workspace is a file-scope device array of
+ * SDTW_STATIC_SCRATCH_BYTES per GPU, which the library's code object holds
+ * on every GPU it runs on until the process ends.  For callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  x, y, loss and stream as for
+ * sdtw_forward.  Returns SDTW_ERR_WORKSPACE when the inference workspace of
+ * this problem (sdtw_workspace_bytes(..., SDTW_MODE_INFERENCE)) exceeds
+ * SDTW_STATIC_SCRATCH_BYTES, and the other statuses as sdtw_forward.  Every
+ * call on one GPU uses that GPU's single array: calls that overlap on one
+ * GPU (other streams, other host threads) race and must be serialised by
+ * the caller.  Calls that follow one another on a stream are safe: each
+ * clears the control words it needs with kernels of its own (no memset
+ * node).  Launches of this call are never timed (sdtw_timing). */
+int sdtw_forward_static(const float *x, const float *y, int64_t B, int64_t N,
+                        int64_t M, int64_t D, float gamma, float *loss,
+                        void *stream);
 
 /* Launch timing, off by default.  sdtw_timing(1) makes every kernel that
  * later sdtw_* calls (from any host thread of the process) enqueue be
