@@ -19,6 +19,7 @@ SDTW_ERR_INVALID_ARG = 1
 SDTW_ERR_WORKSPACE = 2
 SDTW_ERR_HIP = 3
 SDTW_ERR_UNSUPPORTED = 4
+SDTW_ERR_STALLED = 5
 
 SDTW_MODE_UNFUSED = 0
 SDTW_MODE_FUSED = 1
@@ -39,6 +40,8 @@ SIGNATURES = {
                           ctypes.c_size_t, _P, _P]),
     "sdtw_backward": (_I, [_P, _P, _I64, _I64, _I64, _I64, _F, _I, _P,
                            ctypes.c_size_t, _P, _P, _P, _P, _P]),
+    "sdtw_workspace_status": (_I, [_P, ctypes.c_size_t, _I64, _I64, _I64, _I64, _I, _P]),
+    "sdtw_debug_wait_limit": (_I, [_I64]),
     "sdtw_forward_static": (_I, [_P, _P, _I64, _I64, _I64, _I64, _F, _P, _P]),
     "sdtw_timing": (_I, [_I]),
     "sdtw_timing_collect": (_I, [ctypes.POINTER(ctypes.c_char_p),
@@ -103,6 +106,15 @@ def sdtw_backward(x: int, y: int, B: int, N: int, M: int, D: int, gamma: float,
                                stream)
 
 
+def sdtw_workspace_status(workspace: int, workspace_bytes: int, B: int, N: int, M: int,
+                          D: int, mode: int, stream: int = 0) -> int:
+    return lib().sdtw_workspace_status(workspace, workspace_bytes, B, N, M, D, mode, stream)
+
+
+def sdtw_debug_wait_limit(polls: int) -> int:
+    return lib().sdtw_debug_wait_limit(int(polls))
+
+
 SDTW_STATIC_SCRATCH_BYTES = 16 << 20
 
 
@@ -117,7 +129,8 @@ def sdtw_timing(on: bool) -> int:
 
 def sdtw_timing_collect(cap: int = 4096) -> list[tuple[str, float]]:
     """(kernel name, milliseconds) of the launches recorded since the last
-    collect on this thread, in launch order."""
+    collect, in launch order.  The record list is process-wide: a collect
+    drains the launches of every host thread and stream."""
     names = (ctypes.c_char_p * cap)()
     ms = (ctypes.c_float * cap)()
     n = lib().sdtw_timing_collect(names, ms, cap)

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "sdtw.h"
 #include "sdtw_kernels.h"
 
@@ -19,6 +21,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   int64_t nbands = 0, nseg = 0, S = 0;
   size_t ctrl = 0, ctrl_words = 0;  // ticket, done, per-segment progress
+  size_t err_word = 0;              // index of the error word among the control words
   size_t loss64 = 0;                // fp64 [B]
   size_t H = 0;                     // fp64 [2, B, nseg, M] segment hand-off rows
   size_t R = 0;                     // fp64 band-step forward state
@@ -105,6 +108,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
     L->ctrl = off;
     L->gctrl = 2 + 2 * (size_t)B * (size_t)L->nseg;
     L->ctrl_words = L->gctrl + 2 + (size_t)B * (size_t)L->G + 2;
+    L->err_word = L->ctrl_words++;
     off += align_up(L->ctrl_words * 4);
     L->loss64 = off;
     off += align_up((size_t)B * 8);
@@ -128,6 +132,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
     size_t off = 0;
     L->ctrl = off;
     L->ctrl_words = 2 + 2 * (size_t)B * (size_t)L->nseg;
+    L->err_word = L->ctrl_words++;
     off += align_up(L->ctrl_words * 4);
     L->loss64 = off;
     off += align_up((size_t)B * 8);
@@ -148,6 +153,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   L->cnt_rows = 2 * (2 + (size_t)B * (size_t)L->nseg);
   L->cnt_cols = L->cnt_rows + (size_t)B * (size_t)L->nbands;
   L->ctrl_words = L->cnt_cols + (size_t)B * (size_t)((M + 63) / 64);
+  L->err_word = L->ctrl_words++;
   off += align_up(L->ctrl_words * 4);
   L->loss64 = off;
   off += align_up((size_t)B * 8);
@@ -168,6 +174,10 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
 }
 
 bool gamma_ok(float g) { return isfinite(g) && g > 0.f; }
+
+// Test hook of sdtw_debug_wait_limit: replaces the kernels' wait caps (0 =
+// the built-in caps).
+std::atomic<unsigned> g_wait_cap{0};
 
 // Hand-off row entries of the unfused and fused training layouts.
 int64_t hrow_doubles(const Layout& L, int64_t B, int64_t M) { return 2 * B * L.nseg * M; }
@@ -196,6 +206,8 @@ DPArgs dp_args(const Layout& L, char* ws, const float* x, const float* y,
   a.B = (int)B;
   a.nbands = (int)L.nbands;
   a.nseg = (int)L.nseg;
+  a.err = reinterpret_cast<unsigned*>(ws + L.ctrl) + L.err_word;
+  a.wait_cap = g_wait_cap.load(std::memory_order_relaxed);
   const double g = (double)gamma;
   a.k2 = M_LOG2E / g;
   a.g_ln2 = g * M_LN2;
@@ -344,6 +356,7 @@ const char* sdtw_status_string(int status) {
     case SDTW_ERR_WORKSPACE: return "workspace too small";
     case SDTW_ERR_HIP: return "HIP runtime error";
     case SDTW_ERR_UNSUPPORTED: return "unsupported request";
+    case SDTW_ERR_STALLED: return "a hand-off wait inside a kernel gave up; outputs set to NaN";
     default: return "unknown status";
   }
 }
@@ -411,6 +424,27 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
                                     ctrl + L.cnt_rows, ctrl + L.cnt_cols, align != nullptr, s);
   if (e == hipSuccess && align) e = sdtw::launch_unskew(a.dsk, align, B, N, M, L.S, s);
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
+}
+
+int sdtw_workspace_status(const void* workspace, size_t workspace_bytes, int64_t B,
+                          int64_t N, int64_t M, int64_t D, int mode, void* stream) {
+  Layout L;
+  if (!make_layout(B, N, M, D, mode, &L)) return SDTW_ERR_INVALID_ARG;
+  int st = check_ws(L, const_cast<void*>(workspace), workspace_bytes);
+  if (st != SDTW_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned word = 0;
+  const char* src = static_cast<const char*>(workspace) + L.ctrl + 4 * L.err_word;
+  if (hipMemcpyAsync(&word, src, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SDTW_ERR_HIP;
+  return word ? SDTW_ERR_STALLED : SDTW_OK;
+}
+
+int sdtw_debug_wait_limit(int64_t polls) {
+  if (polls < 0 || polls > (int64_t)0xffffffffLL) return SDTW_ERR_INVALID_ARG;
+  g_wait_cap.store((unsigned)polls, std::memory_order_relaxed);
+  return SDTW_OK;
 }
 
 }  // extern "C"

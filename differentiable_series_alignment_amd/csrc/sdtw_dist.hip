@@ -52,13 +52,10 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
 // per CU, so one block's stores drain while others compute, and small
 // batches still spread over every CU.
 static int dist_rows(int64_t B, int64_t N, int64_t M) {
-  static const int cus = [] {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 256;
-    return n;
-  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
   const int64_t blocks128 = B * ((N + 127) / 128) * ((M + kDT - 1) / kDT);
   return (blocks128 > cus && blocks128 <= 2 * (int64_t)cus) ? 128 : 64;
 }

@@ -230,7 +230,10 @@ __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a)
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  if (threadIdx.x == 0) s_ticket = atomicAdd(&a.ctrl[0], 1u);
+  if (threadIdx.x == 0) {
+    s_ticket = atomicAdd(&a.ctrl[0], 1u);
+    launch_shared_init(a);
+  }
   __syncthreads();
   const unsigned ticket = s_ticket;
   const int rev = (int)(ticket & 1u);

@@ -7,45 +7,111 @@
 namespace sdtw {
 
 constexpr int kCH = 16;                      // steps per chunk
-constexpr uint32_t kSpinCap = 1u << 25;      // polls before a wait gives up
-constexpr uint32_t kLdsSpinCap = 1u << 22;   // the same for waits on LDS counters
+constexpr uint32_t kSpinCap = 1u << 25;      // idle polls of a global row before a wait gives up
+constexpr uint32_t kLdsSpinCap = 1u << 22;   // polls of an LDS counter before a wait gives up
 static_assert(kCH == 16, "band_chunk unrolls 16 steps");
+
+// Wait limits and the error word.  Every wait below is a bounded poll: if
+// the value it waits for does not come within a cap of polls (about 0.1 s
+// for LDS counters, seconds for global rows), it gives up so that every wave
+// still exits, and records that in the workspace's error word (an
+// agent-scope atomic OR, waited for, so the launch's last workgroup sees
+// it).  That workgroup then sets the launch's outputs to NaN (release_ctrl),
+// and sdtw_workspace_status reports the error on the host.  A nonzero
+// DPArgs::wait_cap replaces both caps (a test hook).
+//
+// What the waits and the end of the launch need (the error word, the cap,
+// the outputs to poison) is copied into LDS by thread 0 at the start of a
+// launch (launch_shared_init, before the kernel's first barrier), so no
+// register holds it across the sweep: waits read the cap only once they
+// have to wait.
+struct LaunchShared {
+  unsigned* err;
+  unsigned cap;
+  float* loss;
+  double* loss64;
+  float* gx;
+  float* gy;
+  float* align;
+  int64_t nb, nx, ny, na;   // element counts of loss, gx, gy, align
+};
+__device__ __forceinline__ LaunchShared& launch_shared() {
+  __shared__ LaunchShared ls;
+  return ls;
+}
+__device__ __forceinline__ void launch_shared_init(const DPArgs& a) {
+  LaunchShared& ls = launch_shared();
+  ls.err = a.err;
+  ls.cap = a.wait_cap;
+  ls.loss = a.loss;
+  ls.loss64 = a.loss64;
+  ls.gx = a.gx;
+  ls.gy = a.gy;
+  ls.align = a.align;
+  ls.nb = a.B;
+  ls.nx = (int64_t)a.B * a.N * a.D;
+  ls.ny = (int64_t)a.B * a.M * a.D;
+  ls.na = (int64_t)a.B * a.N * a.M;
+}
+__device__ __forceinline__ uint32_t lds_cap() {
+  const unsigned c = launch_shared().cap;
+  return c ? c : kLdsSpinCap;
+}
+__device__ __forceinline__ uint32_t glob_cap() {
+  const unsigned c = launch_shared().cap;
+  return c ? c : kSpinCap;
+}
+__device__ __forceinline__ void note_giveup() {
+  unsigned* err = launch_shared().err;
+  if (err) {
+    __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+}
+
+// NaN over every output the launch writes (the loss and the fp64 final
+// state that later launches start from; gradients and the alignment matrix
+// of a reverse sweep), by the threads of one workgroup.
+__device__ __forceinline__ void poison_outputs() {
+  const LaunchShared& ls = launch_shared();
+  const float qnan = __builtin_nanf("");
+  const int64_t t0 = threadIdx.x, nt = blockDim.x;
+  for (int64_t i = t0; i < ls.nb; i += nt) {
+    if (ls.loss) ls.loss[i] = qnan;
+    if (ls.loss64) ls.loss64[i] = __builtin_nan("");
+  }
+  if (ls.gx)
+    for (int64_t i = t0; i < ls.nx; i += nt) ls.gx[i] = qnan;
+  if (ls.gy)
+    for (int64_t i = t0; i < ls.ny; i += nt) ls.gy[i] = qnan;
+  if (ls.align)
+    for (int64_t i = t0; i < ls.na; i += nt) ls.align[i] = qnan;
+}
 
 // Control words of one sweep: [0] ticket, [1] finished workgroups,
 // [2 + b*nseg + s] columns published by segment s of pair b.  The last
 // workgroup to finish returns them to zero, so the next launch on the same
 // workspace starts clean without a separate clearing launch (every other
-// workgroup has stopped touching them once it has counted itself finished).
+// workgroup has stopped touching them once it has counted itself finished),
+// and, if any wait of the launch gave up, poisons the launch's outputs.
 __device__ __forceinline__ void release_ctrl(unsigned* ctrl, int64_t nprog) {
+  __shared__ unsigned s_last;
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned done = __hip_atomic_fetch_add(&ctrl[1], 1u, __ATOMIC_ACQ_REL,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-    if (done == gridDim.x - 1) {
+    s_last = done == gridDim.x - 1;
+    if (s_last) {
       for (int64_t k = 0; k < nprog; ++k)
         __hip_atomic_store(&ctrl[2 + k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&ctrl[1], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-}
-
-// Bounded wait until *prog >= need (columns published by the segment above).
-// The polls are relaxed; one agent-scope acquire fence follows the poll that
-// succeeds, so waiting does not invalidate caches on every poll.  The producer
-// holds a smaller ticket and is running, so it publishes within one sweep; the
-// cap only guarantees that every wave exits even if that ever failed (the
-// result would be garbage, never a hang).  Returns the value to record as
-// available.
-__device__ __forceinline__ unsigned await_progress(const unsigned* prog, unsigned need) {
-  unsigned v = 0;
-  for (uint32_t spin = 0; spin < kSpinCap; ++spin) {
-    v = __hip_atomic_load(prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (v >= need) break;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return v < need ? need : v;
+  __syncthreads();
+  unsigned* const err = launch_shared().err;
+  if (s_last && err && __hip_atomic_load(err, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+    poison_outputs();
 }
 
 // ---------------------------------------------------------------------------
@@ -60,11 +126,17 @@ __device__ __forceinline__ unsigned await_progress(const unsigned* prog, unsigne
 constexpr int kRingC = 256;                  // columns per LDS ring (power of 2)
 
 // Bounded wait until *p >= need; returns the last value read (>= need unless
-// the cap was hit, in which case the caller proceeds on stale data rather
-// than hang).
+// the cap was hit: then the give-up is recorded (note_giveup) and the caller
+// proceeds on stale data rather than hang; the launch's outputs become NaN).
 __device__ __forceinline__ unsigned lds_wait_ge(const unsigned* p, unsigned need) {
   unsigned v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  for (uint32_t spin = 0; v < need && spin < kLdsSpinCap; ++spin) {
+  if (v >= need) return v;
+  const uint32_t cap = lds_cap();
+  for (uint32_t spin = 0; v < need; ++spin) {
+    if (spin >= cap) {
+      note_giveup();
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
     v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
@@ -99,7 +171,7 @@ __device__ __forceinline__ void lds_publish(unsigned* p, unsigned v) {
 //  - counts: the writer waits for its stores (vmcnt(0)) and then publishes
 //    the column count, which the reader polls before loading.
 // A segment waits only on a smaller ticket, which is running, so the loop
-// ends; the poll cap guarantees the wave exits regardless.
+// ends; the poll cap (per wait) guarantees the wave exits regardless.
 //
 // Global rows are either whole (hcols = 0: column c at H[c]) or rings of
 // hcols columns (a power of two; column c at H[c % hcols]), which use
@@ -125,10 +197,17 @@ __device__ __forceinline__ void segment_io_wave(
   unsigned fetched = 0, known_in = 0, pub = 0, known_back = 0;
   // Only a validated input row (always a workspace row) is written back.
   uint64_t* const hin_bits = reinterpret_cast<uint64_t*>(const_cast<double*>(Hin));
-  for (uint32_t spin = 0; spin < kSpinCap; ++spin) {
+  // `idle` counts the polls since data last moved: the cap bounds each wait,
+  // not the wave's lifetime (a long row moves data many times).
+  const uint32_t cap = glob_cap();
+  for (uint32_t idle = 0;;) {
     const bool in_left = do_in && fetched < M;
     const bool out_left = do_out && pub < M;
     if (!in_left && !out_left) break;
+    if (idle >= cap) {
+      note_giveup();
+      break;
+    }
     bool moved = false;
     if (in_left && gr.valid_in) {
       const unsigned room =
@@ -192,7 +271,12 @@ __device__ __forceinline__ void segment_io_wave(
         moved = true;
       }
     }
-    if (!moved) __builtin_amdgcn_s_sleep(2);
+    if (moved) {
+      idle = 0;
+    } else {
+      __builtin_amdgcn_s_sleep(2);
+      ++idle;
+    }
   }
 }
 

@@ -608,6 +608,7 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
   const int w = threadIdx.x >> 6;
   if (threadIdx.x == 0) sh.ticket = atomicAdd(&a.ctrl[0], 1u);
   if (threadIdx.x == 0) {
+    launch_shared_init(a);
     sh.wr_in = sh.rd_in = sh.wr_out = sh.rd_out = 0u;
     sh.d_ready = sh.dp_done = 0u;
     for (int c = 0; c < kRevHelpCMax; ++c) sh.e_free[c] = sh.x_done[c] = 0u;

@@ -76,6 +76,10 @@ struct DPArgs {
   double* ckpt;
   int64_t ck_span;
   int nck;
+  // Error word of the workspace (a wait gave up) and the test hook that
+  // replaces the wait caps (0: built-in caps; sdtw_debug_wait_limit).
+  unsigned* err;
+  unsigned wait_cap;
 };
 // Padding on each side of a stored checkpoint row (columns the band wave
 // touches outside 0..M-1 land there).

@@ -73,12 +73,24 @@
  *    without host synchronisation.  Arguments are validated on the host before
  *    any HIP call; invalid calls return an error and enqueue nothing.  Faults
  *    inside kernels surface at the caller's next synchronisation.
+ *  - Hand-offs between workgroups and waves are bounded waits: a wave that
+ *    polls a counter or a hand-off row far longer than any normal run needs
+ *    (about 0.1 s on chip, seconds on a global row) gives up so that every
+ *    kernel still exits.  Such a call cannot have correct results: the
+ *    launch sets its outputs (loss, grad_x, grad_y, align, and the kept
+ *    final state, so a later backward is NaN too) to NaN, and
+ *    sdtw_workspace_status reports SDTW_ERR_STALLED until the next forward
+ *    on the workspace.  The ring hand-off of the inference and checkpointed
+ *    forwards (see the modes) needs every band of a pair resident at once:
+ *    kernels of other streams holding the CUs for longer than the cap make
+ *    it stall this way instead of hanging.
  *  - The library never allocates device memory; the caller owns every buffer
  *    passed in.  Process-wide state is limited to: the launch-timing record
- *    list (sdtw_timing, off by default, guarded by a mutex) and the
+ *    list (sdtw_timing, off by default, guarded by a mutex), the
  *    per-device scratch array of sdtw_forward_static with its resolved
- *    addresses.  Calls on distinct workspaces may run concurrently on
- *    distinct streams.  Nothing is printed.
+ *    addresses, and the wait limit of sdtw_debug_wait_limit.  Calls on
+ *    distinct workspaces may run concurrently on distinct streams.  Nothing
+ *    is printed.
  */
 #ifndef SDTW_H
 #define SDTW_H
@@ -90,14 +102,15 @@
 extern "C" {
 #endif
 
-#define SDTW_ABI_VERSION 1
+#define SDTW_ABI_VERSION 2
 
 typedef enum {
     SDTW_OK = 0,
     SDTW_ERR_INVALID_ARG = 1, /* bad size, gamma, pointer or mode          */
     SDTW_ERR_WORKSPACE = 2,   /* workspace_bytes below sdtw_workspace_bytes */
     SDTW_ERR_HIP = 3,         /* a HIP runtime call or launch failed        */
-    SDTW_ERR_UNSUPPORTED = 4  /* request outside what the library supports  */
+    SDTW_ERR_UNSUPPORTED = 4, /* request outside what the library supports  */
+    SDTW_ERR_STALLED = 5      /* a hand-off wait inside a kernel gave up    */
 } sdtw_status_t;
 
 typedef enum {
@@ -151,6 +164,23 @@ int sdtw_backward(const float *x, const float *y, int64_t B, int64_t N,
                   int64_t M, int64_t D, float gamma, int mode, void *workspace,
                   size_t workspace_bytes, const float *grad_loss,
                   float *grad_x, float *grad_y, float *align, void *stream);
+
+/* Waits for `stream`, then reports whether a hand-off wait of the last
+ * sdtw_forward / sdtw_backward on this workspace (same sizes and mode) gave
+ * up: SDTW_OK, SDTW_ERR_STALLED (the outputs of that call were set to NaN),
+ * SDTW_ERR_INVALID_ARG / SDTW_ERR_WORKSPACE as for sdtw_forward, or
+ * SDTW_ERR_HIP if the copy of the workspace's error word failed.  The word
+ * is cleared by every forward and kept by backwards. */
+int sdtw_workspace_status(const void *workspace, size_t workspace_bytes,
+                          int64_t B, int64_t N, int64_t M, int64_t D,
+                          int mode, void *stream);
+
+/* Test hook: a nonzero `polls` replaces the kernels' wait caps (polls of a
+ * counter or of a hand-off row) for later calls from any thread; 0 restores
+ * the built-in caps.  A tiny limit makes waits give up deliberately (every
+ * kernel still exits; see SDTW_ERR_STALLED).  SDTW_ERR_INVALID_ARG for a
+ * negative value or one above 2^32-1. */
+int sdtw_debug_wait_limit(int64_t polls);
 
 /* Size of the device array behind sdtw_forward_static (per GPU). */
 #define SDTW_STATIC_SCRATCH_BYTES (16u << 20)

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = L.lib()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert L.sdtw_abi_version() == 1
+    assert L.sdtw_abi_version() == 2
 
 
 def test_status_strings():
@@ -230,3 +230,37 @@ def test_profile_summaries_name_their_commands():
                 raise AssertionError(f"{name}: bench.py {tail}") from e
             finally:
                 sys.argv = argv
+
+
+def test_status_query_and_wait_limit_validation():
+    """The error-word query and the wait-limit hook reject bad arguments on
+    the host; a valid query on a machine without a GPU fails in HIP, not
+    silently."""
+    B, N, M, D = 2, 100, 90, 3
+    nb = L.sdtw_workspace_bytes(B, N, M, D, L.SDTW_MODE_UNFUSED)
+    assert L.sdtw_workspace_status(FAKE, nb, 0, N, M, D, L.SDTW_MODE_UNFUSED, 0) == \
+        L.SDTW_ERR_INVALID_ARG
+    assert L.sdtw_workspace_status(FAKE, nb, B, N, M, D, 9, 0) == L.SDTW_ERR_INVALID_ARG
+    assert L.sdtw_workspace_status(FAKE, nb - 256, B, N, M, D, L.SDTW_MODE_UNFUSED, 0) == \
+        L.SDTW_ERR_WORKSPACE
+    assert L.sdtw_workspace_status(None, nb, B, N, M, D, L.SDTW_MODE_UNFUSED, 0) == \
+        L.SDTW_ERR_INVALID_ARG
+    if not torch.cuda.is_available():
+        assert L.sdtw_workspace_status(FAKE, nb, B, N, M, D, L.SDTW_MODE_UNFUSED, 0) == \
+            L.SDTW_ERR_HIP
+    assert L.sdtw_debug_wait_limit(-1) == L.SDTW_ERR_INVALID_ARG
+    assert L.sdtw_debug_wait_limit(1 << 32) == L.SDTW_ERR_INVALID_ARG
+    assert L.sdtw_debug_wait_limit(0) == L.SDTW_OK
+    assert "gave up" in L.sdtw_status_string(L.SDTW_ERR_STALLED)
+
+
+def test_static_forward_validation_on_host():
+    """sdtw_forward_static rejects null pointers, bad sizes and problems whose
+    inference workspace exceeds its device array before any HIP call."""
+    assert L.sdtw_forward_static(None, FAKE, 1, 1, 1, 1, 1.0, FAKE, 0) == L.SDTW_ERR_INVALID_ARG
+    assert L.sdtw_forward_static(FAKE, FAKE, 0, 1, 1, 1, 1.0, FAKE, 0) == L.SDTW_ERR_INVALID_ARG
+    assert L.sdtw_forward_static(FAKE, FAKE, 2, 8, 8, 300, 1.0, FAKE, 0) == L.SDTW_ERR_INVALID_ARG
+    assert L.sdtw_workspace_bytes(64, 8192, 500, 2, L.SDTW_MODE_INFERENCE) > \
+        L.SDTW_STATIC_SCRATCH_BYTES
+    assert L.sdtw_forward_static(FAKE, FAKE, 64, 8192, 500, 2, 1.0, FAKE, 0) == \
+        L.SDTW_ERR_WORKSPACE
