@@ -32,13 +32,22 @@ if HERE not in sys.path:
 WORKLOAD = dict(B=32, N=512, M=512, D=64, gamma=1.0)
 # Plain ALU peak of the MI355X: 256 CUs x 4 SIMDs x 16 lanes, one operation
 # per lane per clock at 2.4 GHz (the datasheet's 78.6 TFLOP/s fp64 counts an
-# FMA as two), i.e. 39.3 T operations/s.
+# FMA as two), i.e. 39.3 T lane-operation slots/s.
 PEAK_ALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# Algorithmic work of one cell in one sweep: d = Dist*log2(e)/g (1 mul), the
-# two minima and two maxima that order the three predecessors (4), the two
+# Algorithmic ALU work of one cell, forward and backward dynamic programme
+# together (the survey's per-cell estimate): about 13 transcendentals (exp,
+# log), each taking four issue slots at quarter rate, and about 45 other
+# operations, i.e. 97 lane-operation slots per cell.  At the headline
+# workload that is 20.7 us at PEAK_ALU_TOPS.
+TRANS_PER_CELL = 13
+OTHER_OPS_PER_CELL = 45
+ALU_SLOTS_PER_CELL = 4 * TRANS_PER_CELL + OTHER_OPS_PER_CELL
+# A narrower count, beside it: the operations of one cell in one sweep when
+# the recurrence is written in base 2 -- d = Dist*log2(e)/g (1 mul), the two
+# minima and two maxima that order the three predecessors (4), the two
 # differences to the minimum (2), two exp2 (2), their sum with 1 (2), log2
-# (1), the soft-minimum m - log2 (1) and the state t + d (1): 14 operations.
-# The dominant launch runs both sweeps over every cell.
+# (1), the soft-minimum m - log2 (1) and the state t + d (1): 14 operations,
+# 28 for the two sweeps, transcendentals counted once.
 DP_OPS_PER_CELL = 2 * 14
 # Bytes the two sweeps must move per cell: each reads Dist (4) and writes
 # its fp64 state (8).
@@ -54,8 +63,8 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_dp_common.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h"],
-    "sha256": "3b57d7e6cd041f91daa294b475f94ba30382173947935ce3c532cccdf4fdcbee",
-    "fetch_kib": 37585, "fetch_scale": 2.0,
+    "sha256": "4a268bf7f9759586c351cb1e310480d991145ee424cfebf27a406d09b1bef452",
+    "fetch_kib": 37593, "fetch_scale": 2.0,
     "write_kib": 148109, "write_scale": 1.0,
 }
 
@@ -72,11 +81,20 @@ CHAIN_CYCLES = 100
 CLOCK = 2.4e9
 
 
+# The other configurations (tiny; feature-dimension sweep; long sequences at
+# two temperatures), reported beside the headline one.
+CONFIGS = ([(2, 16, 16, 1, 1.0)]
+           + [(32, 256, 256, d, 1.0) for d in (1, 4, 16, 64, 128, 256)]
+           + [(32, n, m, 128, g) for (n, m) in ((1024, 1024), (2048, 2048), (4096, 4096),
+                                               (4096, 1000))
+              for g in (1.0, 0.01)])
+
+
 def step_bounds(B, N, M, D, fused):
     """Lower bounds of one fwd+bwd step (microseconds).  Stages: distances
     (2D flops per cell on fp64 MFMA; unfused also writes them, 4 B per
-    cell), the sweeps (both at once unfused: the chain of N+M-1 steps, 28
-    ALU operations and 24 B per cell), the chain rule (4D flops per cell on
+    cell), the sweeps (both at once unfused: the chain of N+M-1 steps,
+    ALU_SLOTS_PER_CELL issue slots and 24 B per cell), the chain rule (4D flops per cell on
     fp32 MFMA; unfused reads the two fp64 states and writes E or the dy
     shares, 20 B per cell).  Fused runs the sweeps one after the other and
     recomputes the distances in each (8 B of state per cell written, then
@@ -86,7 +104,7 @@ def step_bounds(B, N, M, D, fused):
     cells = B * N * M
     io = 4 * B * (N + M) * D
     chain = (N + M - 1) * CHAIN_CYCLES / CLOCK
-    alu = 28 * cells / (PEAK_ALU_TOPS * 1e12)
+    alu = ALU_SLOTS_PER_CELL * cells / (PEAK_ALU_TOPS * 1e12)
     if not fused:
         t_dist = (2 * cells * D / PEAK_F64_MFMA, (4 * cells + io) / PEAK_HBM)
         t_dp = (chain, alu, 24 * cells / PEAK_HBM)
@@ -138,9 +156,17 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--headline-only", action="store_true",
                    help="skip the per-configuration table")
-    p.add_argument("--counter-pass", action="store_true",
-                   help="for rocprofv3 --pmc runs: three headline steps and three "
+    p.add_argument("--counter-pass", nargs="?", const="32,512,512,64,1.0", default=None,
+                   metavar="B,N,M,D,GAMMA",
+                   help="for rocprofv3 --pmc runs: three unfused and three fused steps "
+                        "of this workload (default: the headline one), then three "
                         "copies of 256 MiB (the counters' calibration), no output")
+    p.add_argument("--summarize-counters", nargs="+", default=None, metavar="CSV",
+                   help="print per-kernel averages of rocprofv3 counter_collection.csv "
+                        "files (no GPU needed)")
+    p.add_argument("--cells", type=float, default=None,
+                   help="with --summarize-counters: DP cells per dispatch, for the "
+                        "per-cell figures")
     p.add_argument("--profile-workload", default=None, metavar="B,N,M,D,GAMMA",
                    help="for rocprofv3 --kernel-trace runs: a few unfused and "
                         "fused steps of this workload, one summary line each")
@@ -160,10 +186,15 @@ def profile_workload(torch, L, pair_batch, spec, steps):
               flush=True)
 
 
-def counter_pass(torch, L, x, y, gamma):
-    """Three unfused headline steps, then three copies of a 256 MiB fp32
-    tensor whose bytes are known, for scaling the traffic counters."""
-    measure(L, torch, x, y, gamma, L.SDTW_MODE_UNFUSED, 3, 0)
+def counter_pass(torch, L, pair_batch, spec):
+    """Three unfused and three fused steps of one workload, then three copies
+    of a 256 MiB fp32 tensor whose bytes are known, for scaling the traffic
+    counters."""
+    b_, n_, m_, d_, g_ = spec.split(",")
+    xc, yc = pair_batch(int(b_), int(n_), int(m_), int(d_), seed=0)
+    x, y = xc.to("cuda:0"), yc.to("cuda:0")
+    measure(L, torch, x, y, float(g_), L.SDTW_MODE_UNFUSED, 3, 0)
+    measure(L, torch, x, y, float(g_), L.SDTW_MODE_FUSED, 3, 0)
     src = torch.ones(64 * 2**20, dtype=torch.float32, device=x.device)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -171,31 +202,124 @@ def counter_pass(torch, L, x, y, gamma):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(x, y, gamma, budget_s):
+def cpu_baseline(x, y, gamma, budget_s, warm=True):
     """The fp64 oracle on the host cores, on a bounded sample (whole pairs of
-    the same workload) sized to about `budget_s` seconds of CPU work."""
+    the same workload) sized to about `budget_s` seconds of wall time: calls
+    of min(B, threads) pairs, one pair per OpenMP thread, at least one call."""
     from oracle import oracle as O
     O.lib()
     xs, ys = x.numpy(), y.numpy()
     B, N, D = xs.shape
     M = ys.shape[1]
-    O.value_and_grad(xs[:1], ys[:1], gamma, [1.0 / B])  # warm-up
     threads = O.num_threads()
-    # Whole batches of the workload's pairs (spread over the OpenMP threads)
-    # until about budget_s seconds of wall time have passed.
-    npairs = B
+    if warm:
+        O.value_and_grad(xs[:1, :min(N, 64)], ys[:1, :min(M, 64)], gamma, [1.0])
+    npairs = min(B, threads)
     t0 = time.perf_counter()
     done = 0
     while True:
-        O.value_and_grad(xs[:npairs], ys[:npairs], gamma, [1.0 / B] * npairs)
-        done += npairs
+        lo = done % B
+        hi = min(lo + npairs, B)
+        O.value_and_grad(xs[lo:hi], ys[lo:hi], gamma, [1.0 / B] * (hi - lo))
+        done += hi - lo
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": done * N * M / dt, "unit": "cells/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{done} pairs of {N}x{M}, D={D} (fp64 distances, forward, "
-                      f"log-space backward, chain rule), {dt:.1f} s wall"}
+            "sample": f"{done} pairs of {N}x{M}, D={D}, gamma={gamma} (fp64 distances, "
+                      f"forward, log-space backward, chain rule), {dt:.1f} s wall"}
+
+
+def cpu_one_core(x, y, gamma, budget_s):
+    """The oracle on one core (OpenMP limited to one thread for the call)."""
+    from oracle import oracle as O
+    prev = O.num_threads()
+    O.set_num_threads(1)
+    try:
+        return cpu_baseline(x, y, gamma, budget_s, warm=False)
+    finally:
+        O.set_num_threads(prev)
+
+
+# Counter arithmetic of the MI355X (gfx950): 8 XCDs (GRBM counters are kept
+# per XCD), 256 CUs, 1024 SIMDs; one MFMA "MOP" is 512 flops; FETCH_SIZE and
+# WRITE_SIZE are KiB, scaled by what they read for a copy of known size
+# (FETCH_SIZE reads half the bytes a 256 MiB copy moves, WRITE_SIZE all).
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+
+
+def derived_counters(c, cells):
+    """Figures per dispatch from the mean counter values `c` of one kernel:
+    MFMA busy share of the SIMDs' cycles, VALU busy (rocprofv3's VALUBusy),
+    MFMA flops, and per DP cell the VALU lane slots (non-MFMA VALU
+    instructions x 64), transcendentals (x 64) and HBM bytes."""
+    d = {}
+    gui = c.get("GRBM_GUI_ACTIVE")
+    if gui:
+        cyc = gui / N_XCD
+        d["cycles"] = cyc
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            d["mfma_busy_pct"] = 100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD)
+        if "SQ_ACTIVE_INST_VALU" in c:
+            d["valu_busy_pct"] = 100 * c["SQ_ACTIVE_INST_VALU"] / N_CU / cyc
+    flops = 512 * (c.get("SQ_INSTS_VALU_MFMA_MOPS_F64", 0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0))
+    if "SQ_INSTS_VALU_MFMA_MOPS_F64" in c:
+        d["mfma_gflop"] = flops / 1e9
+    if cells:
+        if "SQ_INSTS_VALU" in c and "SQ_INSTS_MFMA" in c:
+            d["valu_slots_per_cell"] = 64 * (c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]) / cells
+        if "SQ_INSTS_VALU_TRANS_F32" in c:
+            d["trans_per_cell"] = 64 * (c["SQ_INSTS_VALU_TRANS_F32"]
+                                        + c.get("SQ_INSTS_VALU_TRANS_F64", 0)) / cells
+        if "FETCH_SIZE" in c and "WRITE_SIZE" in c:
+            d["hbm_bytes_per_cell"] = 1024 * (FETCH_SCALE * c["FETCH_SIZE"]
+                                              + WRITE_SCALE * c["WRITE_SIZE"]) / cells
+    if "FETCH_SIZE" in c and "WRITE_SIZE" in c:
+        d["hbm_mb"] = 1024 * (FETCH_SCALE * c["FETCH_SIZE"] + WRITE_SCALE * c["WRITE_SIZE"]) / 1e6
+    return d
+
+
+def summarize_counters(paths, cells=None):
+    """Per-kernel averages of rocprofv3 --pmc output (counter_collection.csv:
+    one row per dispatch and counter, the value summed over the GPU's
+    instances).  Prints one markdown row per kernel: dispatches and the mean
+    value of every counter per dispatch; then the derived figures."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                key = (r["Dispatch_Id"], r["Counter_Name"])
+                vals[name][key].append(float(r["Counter_Value"]))
+    counters = sorted({c for k in vals.values() for (_, c) in k})
+    means = {}
+    print("| kernel | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|" + "---|" * len(counters))
+    for name, kv in sorted(vals.items()):
+        per = defaultdict(list)
+        disp = set()
+        for (d, c), v in kv.items():
+            per[c].append(sum(v))
+            disp.add(d)
+        short = name if len(name) <= 60 else name[:57] + "..."
+        cols = [f"{sum(per[c]) / len(per[c]):.6g}" if per[c] else "" for c in counters]
+        print(f"| `{short}` | {len(disp)} | " + " | ".join(cols) + " |")
+        means[short] = {c: sum(per[c]) / len(per[c]) for c in counters if per[c]}
+    rows = {k: derived_counters(v, cells) for k, v in means.items()}
+    keys = [k for k in ("cycles", "mfma_busy_pct", "valu_busy_pct", "mfma_gflop",
+                        "valu_slots_per_cell", "trans_per_cell", "hbm_mb",
+                        "hbm_bytes_per_cell") if any(k in r for r in rows.values())]
+    if keys:
+        print()
+        print("| kernel | " + " | ".join(keys) + " |")
+        print("|---|" + "---|" * len(keys))
+        for name, r in rows.items():
+            print(f"| `{name}` | " + " | ".join(f"{r[k]:.4g}" if k in r else ""
+                                                for k in keys) + " |")
 
 
 def measure(L, torch, x, y, gamma, mode, steps, warmup):
@@ -308,8 +432,32 @@ def barycenter_rate(torch, softdtw_barycenter, block_waves):
             "cells_per_s": 100 * 10 * 100 * 100 / dt}
 
 
+def barycenter_cpu_rate(block_waves, budget_s):
+    """The oracle's barycenter objective and gradient (10 pairs of 100 x 100,
+    D = 3, the work of one iteration) repeated for about budget_s seconds."""
+    from oracle import oracle as O
+    X = block_waves(10, 100, 3, seed=0).numpy()
+    z = X.mean(axis=0)
+    threads = O.num_threads()
+    t0 = time.perf_counter()
+    it = 0
+    while True:
+        O.barycenter_objective_and_grad(z, X, 1.0)
+        it += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"workload": "barycenter K=10 N=M=100 D=3 gamma=1.0, objective and gradient",
+            "value": it * 10 * 100 * 100 / dt, "unit": "cells/s", "cores": threads,
+            "kind": "oracle", "ms_per_iteration": dt * 1e3 / it,
+            "sample": f"{it} iterations, {dt:.1f} s wall"}
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.cells)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the workload runs on a single MI355X)", file=sys.stderr)
@@ -333,7 +481,7 @@ def main():
     x, y = xc.to(dev), yc.to(dev)
     cells = B * N * M
     if args.counter_pass:
-        counter_pass(torch, L, x, y, gamma)
+        counter_pass(torch, L, pair_batch, args.counter_pass)
         return
 
     ms, fwd, bwd, stream = measure(L, torch, x, y, gamma, L.SDTW_MODE_UNFUSED,
@@ -355,7 +503,7 @@ def main():
     kernels = {k: {"launches_per_step": len(v) / args.steps, "avg_us": 1e3 * sum(v) / len(v)}
                for k, v in per_kernel.items()}
     dom_ms = sum(per_kernel[DOMINANT]) / len(per_kernel[DOMINANT])
-    achieved = DP_OPS_PER_CELL * cells / (dom_ms * 1e-3) / 1e12
+    achieved = ALU_SLOTS_PER_CELL * cells / (dom_ms * 1e-3) / 1e12
 
     peak, peak_over = peak_mib(torch, SoftDTW, x, y, gamma, False)
     ms_f, _, _, _ = measure(L, torch, x, y, gamma, L.SDTW_MODE_FUSED,
@@ -365,12 +513,7 @@ def main():
 
     per_config = []
     if not args.headline_only:
-        cfgs = [(2, 16, 16, 1, 1.0)]
-        cfgs += [(32, 256, 256, d, 1.0) for d in (1, 4, 16, 64, 128, 256)]
-        cfgs += [(32, n, m, 128, g) for (n, m) in ((1024, 1024), (2048, 2048),
-                                                   (4096, 4096), (4096, 1000))
-                 for g in (1.0, 0.01)]
-        for (b_, n_, m_, d_, g_) in cfgs:
+        for (b_, n_, m_, d_, g_) in CONFIGS:
             xc2, yc2 = pair_batch(b_, n_, m_, d_, seed=0)
             x2, y2 = xc2.to(dev), yc2.to(dev)
             entry = {"workload": f"B={b_} N={n_} M={m_} D={d_} gamma={g_}"}
@@ -414,6 +557,12 @@ def main():
         "roofline": {"kernel": "both sweeps of the dynamic programme (k_dp_unfused)",
                      "bound": "alu", "achieved": achieved, "peak": PEAK_ALU_TOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_ALU_TOPS,
+                     "ops_per_cell": ALU_SLOTS_PER_CELL,
+                     "ops_note": f"{TRANS_PER_CELL} transcendentals x 4 issue slots + "
+                                 f"{OTHER_OPS_PER_CELL} other lane operations per cell "
+                                 "(fwd+bwd DP), against 39.3 T lane slots/s",
+                     "frac_at_28_ops": DP_OPS_PER_CELL * cells / (dom_ms * 1e-3) / 1e12
+                                       / PEAK_ALU_TOPS,
                      "traffic": recorded_traffic(), "traffic_unit": "bytes per launch",
                      "launch_us": dom_ms * 1e3,
                      "algorithmic_gbs": DP_BYTES_PER_CELL * cells / (dom_ms * 1e-3) / 1e9},
@@ -421,7 +570,19 @@ def main():
         "per_config": per_config,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(xc, yc, gamma, args.cpu_seconds)
+        cb = cpu_baseline(xc, yc, gamma, args.cpu_seconds)
+        cb["one_core"] = cpu_one_core(xc, yc, gamma, args.cpu_seconds)
+        if not args.headline_only:
+            # Every other configuration, at least one call of min(B, threads)
+            # pairs each (the long ones take a few seconds).
+            cb["per_config"] = []
+            for (b_, n_, m_, d_, g_) in CONFIGS:
+                xc2, yc2 = pair_batch(b_, n_, m_, d_, seed=0)
+                r = cpu_baseline(xc2, yc2, g_, 1.0, warm=False)
+                r["workload"] = f"B={b_} N={n_} M={m_} D={d_} gamma={g_}"
+                cb["per_config"].append(r)
+            cb["per_config"].append(barycenter_cpu_rate(block_waves, 2.0))
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

@@ -67,6 +67,8 @@ def lib():
         L.oracle_dtw.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -89,6 +91,11 @@ def _check(rc: int):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP regions from now on (timing)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def sqeuclid(x, y, round_f32: bool = False) -> np.ndarray:

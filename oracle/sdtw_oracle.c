@@ -372,6 +372,18 @@ int oracle_dtw(const double *dist, int64_t B, int64_t N, int64_t M,
     return err;
 }
 
+/* Sets the thread count of the OpenMP regions that follow (timing the
+ * oracle on a chosen number of cores); n < 1 is ignored. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void)
 {
     int n = 1;
