@@ -284,35 +284,67 @@ def softdtw_barycenter(sequences: torch.Tensor, gamma: float = 1.0,
     ``early_stopping`` (EarlyStopping(patience, tol)); ``cosine_annealing``
     (the learning rate follows lr*(1+cos(pi*t/max_iter))/2 over the
     iterations, torch's CosineAnnealingLR); ``grad_clip`` (the gradient's L2
-    norm is clipped to this value before each step, torch's
-    clip_grad_norm_).  The pages give no values for these; all are off by
+    norm is clipped to this value before each step, as torch's
+    clip_grad_norm_ does).  The optimizer is torch's Adam in its fused form.  The pages give no values for these; all are off by
     default so the plain loop is Adam alone."""
     if sequences.dim() != 3:
         raise ValueError("sequences must be (K, N, D)")
     if grad_clip is not None and not (float(grad_clip) > 0.0):
         raise ValueError("grad_clip must be > 0 or None")
     X = sequences.detach().contiguous()
+    _validate(X, X, gamma)              # once: every iteration sees the same shapes
     K, N, D = X.shape
+    g = float(gamma)
+    dev = X.device
+    use_fused = choose_fused(fused, K, N, N, D, dev)
+    mode = L.SDTW_MODE_FUSED if use_fused else L.SDTW_MODE_UNFUSED
     z = X.mean(dim=0).clone().requires_grad_(True)
-    opt = torch.optim.Adam([z], lr=lr)
+    # torch's single-kernel Adam: the same update as the default one, with a
+    # fraction of its host time (which bounds this loop: its kernels take
+    # about 30 us per iteration).
+    opt = torch.optim.Adam([z], lr=lr, fused=True)
     sched = (torch.optim.lr_scheduler.CosineAnnealingLR(opt, T_max=int(max_iter))
              if cosine_annealing and int(max_iter) > 0 else None)
     stop = EarlyStopping(patience, tol) if early_stopping else None
-    loss_fn = SoftDTW(gamma=gamma, fused=choose_fused(fused, K, N, N, D, X.device))
-    hist = []
-    for _ in range(int(max_iter)):
-        opt.zero_grad(set_to_none=True)
-        loss = loss_fn(z.unsqueeze(0).expand_as(X), X).mean()
-        loss.backward()
-        if grad_clip is not None:
-            torch.nn.utils.clip_grad_norm_([z], float(grad_clip))
-        opt.step()
-        if sched is not None:
-            sched.step()
-        hist.append(loss.detach())
-        if stop is not None and stop.step(loss.item()):
-            break
+    clip = None if grad_clip is None else float(grad_clip)
+    T = int(max_iter)
+    # One set of buffers for the whole loop: the iterate broadcast to the K
+    # pairs, workspace, per-pair losses, the upstream gradient of the batch
+    # mean (1/K per pair), dz per pair and summed, and the objective history.
+    # Each iteration is then sdtw_forward + sdtw_backward through the C ABI
+    # (the gradient of mean_k SoftDTW(z, X_k) that autograd would assemble
+    # from the same calls), a sum over k and the optimizer step.
+    with torch.cuda.device(dev):
+        ws = _workspace(K, N, N, D, mode, dev)
+        loss = torch.empty(K, dtype=torch.float32, device=dev)
+        gl = torch.full((K,), 1.0 / K, dtype=torch.float32, device=dev)
+        zb = torch.empty_like(X)
+        gx = torch.empty_like(X)
+        gz = torch.empty_like(z)
+        hist = torch.empty(max(T, 1), dtype=torch.float32, device=dev)
+        s = _stream(dev)
+        args = (zb.data_ptr(), X.data_ptr(), K, N, N, D, g, mode, ws.data_ptr(), ws.numel())
+        n = 0
+        for it in range(T):
+            with torch.no_grad():
+                zb.copy_(z.unsqueeze(0).expand_as(X))
+            L.check(L.sdtw_forward(*args, loss.data_ptr(), s), "sdtw_forward")
+            L.check(L.sdtw_backward(*args, gl.data_ptr(), gx.data_ptr(), None, None, s),
+                    "sdtw_backward")
+            torch.sum(gx, dim=0, out=gz)
+            torch.mean(loss, dim=0, keepdim=True, out=hist[it:it + 1])
+            z.grad = gz
+            if clip is not None:
+                # clip_grad_norm_ for one tensor: scale by min(1, c / (|g| + 1e-6))
+                nrm = torch.linalg.vector_norm(gz)
+                gz.mul_(torch.clamp(clip / (nrm + 1e-6), max=1.0))
+            opt.step()
+            if sched is not None:
+                sched.step()
+            n = it + 1
+            if stop is not None and stop.step(hist[it].item()):
+                break
     z = z.detach()
     if return_history:
-        return z, torch.stack(hist).cpu() if hist else torch.empty(0)
+        return z, hist[:n].cpu()
     return z

@@ -255,6 +255,40 @@ def test_fused_auto_select(S):
     torch.testing.assert_close(la, lu, rtol=0, atol=0)
 
 
+@pytest.mark.parametrize("fused,opts", [(False, {}),
+                                        (False, {"cosine_annealing": True, "grad_clip": 1.0}),
+                                        (True, {})])
+def test_barycenter_loop_matches_autograd_loop(S, fused, opts):
+    """softdtw_barycenter drives the C ABI directly on buffers it keeps for
+    the whole loop; its objective history and final iterate equal those of
+    the plain autograd loop (SoftDTW(...)(z expanded, X).mean().backward(),
+    torch's fused Adam, clip_grad_norm_, the same options) started from the
+    same iterate, to rounding (the gradient norm of the clipping is reduced
+    by a different kernel there)."""
+    X = block_waves(10, 100, 3, seed=2).to(DEV)
+    T = 40
+    z, hist = S.softdtw_barycenter(X, 1.0, T, 0.1, fused=fused, return_history=True, **opts)
+    z0 = X.mean(dim=0).clone().requires_grad_(True)
+    opt = torch.optim.Adam([z0], lr=0.1, fused=True)
+    sched = (torch.optim.lr_scheduler.CosineAnnealingLR(opt, T_max=T)
+             if opts.get("cosine_annealing") else None)
+    loss_fn = S.SoftDTW(gamma=1.0, fused=fused)
+    ref = []
+    for _ in range(T):
+        opt.zero_grad(set_to_none=True)
+        loss = loss_fn(z0.unsqueeze(0).expand_as(X), X).mean()
+        loss.backward()
+        if "grad_clip" in opts:
+            torch.nn.utils.clip_grad_norm_([z0], opts["grad_clip"])
+        opt.step()
+        if sched is not None:
+            sched.step()
+        ref.append(loss.item())
+    assert len(hist) == T
+    np.testing.assert_allclose(hist.double().numpy(), np.array(ref), rtol=1e-5)
+    torch.testing.assert_close(z, z0.detach(), rtol=1e-4, atol=1e-5)
+
+
 def test_barycenter_api(S):
     X = block_waves(10, 100, 3, seed=1).to(DEV)
     z, hist = S.softdtw_barycenter(X, gamma=1.0, max_iter=30, lr=0.1, return_history=True)
