@@ -114,6 +114,34 @@ __device__ __forceinline__ void release_ctrl(unsigned* ctrl, int64_t nprog) {
     poison_outputs();
 }
 
+// Hand-off stress (debug builds only: SDTW_STRESS=1, built as
+// libsdtw_stress.so).  Every producer's publish, every consumer's wait and
+// every pass of a hand-off wave first sleeps a pseudo-random time: mostly
+// 0-3 sleeps of 8 x 64 clocks, one time in eight up to 63 of them (about
+// 13 us).  The hash mixes the clock with the site, workgroup and wave, so
+// producers and consumers drift against each other differently on every
+// run; results must not change, only timings.  In normal builds it is empty.
+#ifndef SDTW_STRESS
+#define SDTW_STRESS 0
+#endif
+__device__ __forceinline__ void stress_delay(unsigned site) {
+#if SDTW_STRESS
+  const uint64_t t = __builtin_readcyclecounter();
+  uint32_t h = (uint32_t)t ^ (uint32_t)(t >> 32) ^ (site * 0x9E3779B9u) ^
+               (blockIdx.x * 0x85EBCA6Bu) ^ ((threadIdx.x >> 6) * 0xC2B2AE35u);
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  h *= 0x297A2D39u;
+  h ^= h >> 15;
+  h = __builtin_amdgcn_readfirstlane(h);
+  const uint32_t n = (h & 7u) == 0u ? (h >> 3) & 63u : (h >> 3) & 3u;
+  for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
+#else
+  (void)site;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // Decoupled bands.  Inside a workgroup every band wave runs at its own pace;
 // the row a band hands to the band below travels through an LDS ring of
@@ -129,6 +157,7 @@ constexpr int kRingC = 256;                  // columns per LDS ring (power of 2
 // the cap was hit: then the give-up is recorded (note_giveup) and the caller
 // proceeds on stale data rather than hang; the launch's outputs become NaN).
 __device__ __forceinline__ unsigned lds_wait_ge(const unsigned* p, unsigned need) {
+  stress_delay(1);
   unsigned v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   if (v >= need) return v;
   const uint32_t cap = lds_cap();
@@ -149,6 +178,7 @@ __device__ __forceinline__ unsigned lds_wait_ge(const unsigned* p, unsigned need
 // visible before the data written ahead of it; only the compiler has to be
 // kept from reordering, and no wait for completion is needed.
 __device__ __forceinline__ void lds_publish(unsigned* p, unsigned v) {
+  stress_delay(2);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -208,6 +238,7 @@ __device__ __forceinline__ void segment_io_wave(
       note_giveup();
       break;
     }
+    stress_delay(3);
     bool moved = false;
     if (in_left && gr.valid_in) {
       const unsigned room =
@@ -261,6 +292,7 @@ __device__ __forceinline__ void segment_io_wave(
                              __HIP_MEMORY_SCOPE_AGENT);
         if (lane == 0) lds_publish(rd_out, avail);
         if (!gr.valid_out) {
+          stress_delay(4);
           __atomic_signal_fence(__ATOMIC_SEQ_CST);
           __builtin_amdgcn_s_waitcnt(0);
           __atomic_signal_fence(__ATOMIC_SEQ_CST);

@@ -207,6 +207,7 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
     }
     if (top_ring && lane == 0) lds_publish(&sh.rd_in, umin_u((unsigned)t0 + kCH, Mu));
     if (direct_out) {
+      stress_delay(5);
       if (lane == 63) {
         const int c0 = t0 - 63;                  // column of step t0
         if (c0 >= 0 && c0 + kCH <= M) {

@@ -33,6 +33,18 @@ def test_library_exports_every_declared_symbol():
     assert L.sdtw_abi_version() == 2
 
 
+def test_stress_build_exports_the_same_symbols():
+    """The hand-off stress build (same sources, SDTW_STRESS=1) loads and
+    exports every declared entry point, with the same workspace sizes."""
+    h = L.load(L.STRESS_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(h, name), name
+    assert h.sdtw_abi_version() == L.sdtw_abi_version()
+    for mode in range(4):
+        assert (h.sdtw_workspace_bytes(32, 512, 512, 64, mode)
+                == L.sdtw_workspace_bytes(32, 512, 512, 64, mode))
+
+
 def test_status_strings():
     for st in range(0, 6):
         s = L.sdtw_status_string(st)
