@@ -16,15 +16,19 @@
 // lanes: A[r][k] sits in lane r + 16k, B[k][c] in lane c + 16k; the
 // accumulator's element (4*e + l/16, l%16) sits in lane l, register e
 // (checked on the hardware).  The contraction index k of step s is
-// d = 4s + k.  The x and y rows pass through LDS in slabs of 16 features,
-// (the next slab is fetched into registers while the current one feeds the
-// MFMAs); the finished block is staged in LDS (over the slabs) and leaves
-// either row-major or in the band-step layout of the dynamic programme.
+// d = 4s + k.  The x and y rows pass through LDS: where D is a multiple of
+// 4 (and the rows are 16-byte aligned) in chunks of 64 features moved as
+// 16-byte vectors, every load of a chunk issued before any is stored and one
+// barrier before the matrix loop; otherwise in double-buffered slabs of 16
+// features (the next slab fetched into registers while the current one feeds
+// the MFMAs).  The finished block is staged in LDS (over the operands) and
+// leaves either row-major or in the band-step layout of the dynamic
+// programme.
 #include "sdtw_dist_block.h"
 
 namespace sdtw {
 
-template <int TR, bool SKEW>
+template <int TR, bool SKEW, int KC>
 __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
                                               const float* __restrict__ y,
                                               float* __restrict__ dist,
@@ -32,7 +36,7 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
                                               int64_t S, int nbands,
                                               unsigned* __restrict__ zero, int64_t nzero,
                                               uint64_t* __restrict__ empty, int64_t nempty) {
-  __shared__ float smem[DistTile<TR>::kLds];
+  __shared__ __align__(16) float smem[DistTile<TR, KC>::kLds];
   // Words the next kernels of the step expect to find cleared (their
   // control words and hand-off rows; a fresh workspace holds garbage),
   // spread over the grid.
@@ -42,7 +46,7 @@ __global__ __launch_bounds__(256, 2) void k_dist(const float* __restrict__ x,
     for (int64_t k = wg * 256 + threadIdx.x; k < nzero; k += stride) zero[k] = 0u;
     for (int64_t k = wg * 256 + threadIdx.x; k < nempty; k += stride) empty[k] = kHEmpty;
   }
-  dist_block<TR, SKEW>(x, y, dist, blockIdx.z, (int64_t)blockIdx.y * TR,
+  dist_block<TR, SKEW, KC>(x, y, dist, blockIdx.z, (int64_t)blockIdx.y * TR,
                        (int64_t)blockIdx.x * kDT, N, M, D, S, nbands, smem);
 }
 
@@ -60,14 +64,26 @@ static int dist_rows(int64_t B, int64_t N, int64_t M) {
   return (blocks128 > cus && blocks128 <= 2 * (int64_t)cus) ? 128 : 64;
 }
 
+// 64-feature chunks of 16-byte vectors (KC = 64) where rows are whole,
+// aligned vectors.
+static bool stage_all(const float* x, const float* y, int64_t D) {
+  return D % 4 == 0 &&
+         ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
+}
+
 hipError_t launch_dist(const float* x, const float* y, float* dist, int64_t B,
                        int64_t N, int64_t M, int64_t D, hipStream_t stream) {
   dim3 grid((unsigned)((M + kDT - 1) / kDT), (unsigned)((N + kDT - 1) / kDT), (unsigned)B);
   {
     TimedLaunch timed_("dist", stream);
-    hipLaunchKernelGGL((k_dist<128, false>), grid, dim3(256), 0, stream, x, y, dist, N, M, D,
-                       (int64_t)0, 0, (unsigned*)nullptr, (int64_t)0, (uint64_t*)nullptr,
-                       (int64_t)0);
+    if (stage_all(x, y, D))
+      hipLaunchKernelGGL((k_dist<128, false, 64>), grid, dim3(256), 0, stream, x, y, dist, N,
+                         M, D, (int64_t)0, 0, (unsigned*)nullptr, (int64_t)0,
+                         (uint64_t*)nullptr, (int64_t)0);
+    else
+      hipLaunchKernelGGL((k_dist<128, false, 16>), grid, dim3(256), 0, stream, x, y, dist, N,
+                         M, D, (int64_t)0, 0, (unsigned*)nullptr, (int64_t)0,
+                         (uint64_t*)nullptr, (int64_t)0);
   }
   return hipGetLastError();
 }
@@ -80,12 +96,19 @@ hipError_t launch_dist_skew(const float* x, const float* y, float* dsk, int64_t 
   dim3 grid((unsigned)((M + kDT - 1) / kDT), (unsigned)((N + tr - 1) / tr), (unsigned)B);
   {
     TimedLaunch timed_("dist_skew", stream);
-    if (tr == 64)
-      hipLaunchKernelGGL((k_dist<64, true>), grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S,
-                         (int)((N + 63) / 64), zero, nzero, eb, nempty);
+    const int nb = (int)((N + 63) / 64);
+    if (tr == 64 && stage_all(x, y, D))
+      hipLaunchKernelGGL((k_dist<64, true, 64>), grid, dim3(256), 0, stream, x, y, dsk, N, M, D,
+                         S, nb, zero, nzero, eb, nempty);
+    else if (tr == 64)
+      hipLaunchKernelGGL((k_dist<64, true, 16>), grid, dim3(256), 0, stream, x, y, dsk, N, M, D,
+                         S, nb, zero, nzero, eb, nempty);
+    else if (stage_all(x, y, D))
+      hipLaunchKernelGGL((k_dist<128, true, 64>), grid, dim3(256), 0, stream, x, y, dsk, N, M,
+                         D, S, nb, zero, nzero, eb, nempty);
     else
-      hipLaunchKernelGGL((k_dist<128, true>), grid, dim3(256), 0, stream, x, y, dsk, N, M, D, S,
-                         (int)((N + 63) / 64), zero, nzero, eb, nempty);
+      hipLaunchKernelGGL((k_dist<128, true, 16>), grid, dim3(256), 0, stream, x, y, dsk, N, M,
+                         D, S, nb, zero, nzero, eb, nempty);
   }
   return hipGetLastError();
 }

@@ -7,17 +7,26 @@
 namespace sdtw {
 
 constexpr int kDT = 128;                 // output block width (columns)
-constexpr int kDKC = 16;                 // features per slab
-constexpr int kDPK = kDKC + 4;           // slab row pitch (floats)
 constexpr int kDTP = kDT + 16;           // output block row pitch (floats)
 
-// LDS floats of a block of TR rows (64 or 128) x kDT columns: two slab
+// Staging of the operands.  KC = 16: slabs of 16 features, double-buffered,
+// any D.  KC = 64 (D a multiple of 4, at most 64): all features at once,
+// single-buffered, loaded as 16-byte vectors; one barrier before the
+// matrix loop instead of one per slab.
+template <int KC>
+struct DistStage {
+  static constexpr int kPK = KC + 4;     // row pitch (floats)
+  static constexpr int kBufs = KC == 16 ? 2 : 1;
+};
+
+// LDS floats of a block of TR rows (64 or 128) x kDT columns: the slab
 // buffers of TR x rows and kDT y rows each, which the finished block
 // [TR][kDTP] overlays at the end.
-template <int TR>
+template <int TR, int KC = 16>
 struct DistTile {
-  static constexpr int kSlab = (TR + kDT) * kDPK;
-  static constexpr int kLds = (2 * kSlab > TR * kDTP ? 2 * kSlab : TR * kDTP);
+  static constexpr int kSlab = (TR + kDT) * DistStage<KC>::kPK;
+  static constexpr int kLds = (DistStage<KC>::kBufs * kSlab > TR * kDTP
+                                   ? DistStage<KC>::kBufs * kSlab : TR * kDTP);
 };
 
 // One TR x 128 block (rows bi0.., columns bj0..) of pair b, computed by a
@@ -25,18 +34,21 @@ struct DistTile {
 // parts of 64 rows each (64 x 64 for TR = 128, 64 x 32 for TR = 64).
 // SKEW: band-step output (else row-major [B,N,M]).  smem: DistTile<TR>::kLds
 // floats.
-template <int TR, bool SKEW>
+template <int TR, bool SKEW, int KC = 16>
 __device__ __forceinline__ void dist_block(const float* __restrict__ x,
                                            const float* __restrict__ y,
                                            float* __restrict__ dist, int64_t b, int64_t bi0,
                                            int64_t bj0, int64_t N, int64_t M, int64_t D,
                                            int64_t S, int nbands, float* smem) {
   static_assert(TR == 64 || TR == 128, "block height");
+  static_assert(KC == 16 || KC == 64, "features per slab");
+  constexpr int kDKC = KC;
+  constexpr int kDPK = DistStage<KC>::kPK;
   constexpr int WR = TR / 64;            // wave rows
   constexpr int WC = 4 / WR;             // wave columns
   constexpr int CW = kDT / WC;           // columns per wave
   constexpr int NJ = CW / 16;            // 16-column tiles per wave
-  constexpr int kSlab = DistTile<TR>::kSlab;
+  constexpr int kSlab = DistTile<TR, KC>::kSlab;
   float* const tile = smem;
   const int l = lane_id();
   const int w = threadIdx.x >> 6;
@@ -45,10 +57,10 @@ __device__ __forceinline__ void dist_block(const float* __restrict__ x,
   const float* xb = x + b * N * D;
   const float* yb = y + b * M * D;
 
-  // Staging: thread t moves elements t + 256q of the TR x 16 x slab and of
-  // the 128 x 16 y slab; rows outside the grid and features >= D are stored
-  // as zeros.
-  constexpr int kQX = TR * kDKC / 256, kQY = kDT * kDKC / 256;
+  // Staging (KC = 16): thread t moves elements t + 256q of the TR x 16 x
+  // slab and of the 128 x 16 y slab; rows outside the grid and features >= D
+  // are stored as zeros.  (KC = 64: see stage_all below.)
+  constexpr int kQX = KC == 16 ? TR * kDKC / 256 : 1, kQY = KC == 16 ? kDT * kDKC / 256 : 1;
   float sx[kQX], sy[kQY];
   auto fetch = [&](int64_t k0) {
 #pragma unroll
@@ -87,17 +99,68 @@ __device__ __forceinline__ void dist_block(const float* __restrict__ x,
 #pragma unroll
   for (int j = 0; j < NJ; ++j) ny[j] = 0.0;
   const int64_t steps = (D + 3) / 4;
-  // Double-buffered slabs: slab k is read from buffer k & 1 while slab k+1
-  // is written into the other one, and slab k+2 is fetched into registers;
-  // one barrier per slab.
+  // KC = 64: chunks of 64 features (D a multiple of 4), single-buffered:
+  // thread t moves 16-byte vectors t + 256q (row v / 16, features c0 + 4 (v %
+  // 16) ..) of the block's TR x rows and 128 y rows, all loads issued before
+  // any is stored; rows outside the grid and features >= D are stored as
+  // zeros.  A later chunk is loaded once every wave is done with the
+  // previous one (two barriers per chunk; other workgroups on the CU hide
+  // the load; nothing is held in registers across the matrix loop).
+  constexpr int kVX = KC == 64 ? TR * 16 / 256 : 1, kVY = KC == 64 ? kDT * 16 / 256 : 1;
+  float4 vx[kVX], vy[kVY];
+  auto load64 = [&](int64_t c0) {
+#pragma unroll
+    for (int q = 0; q < kVX; ++q) {
+      const int v = (int)threadIdx.x + 256 * q;
+      const int row = v >> 4;
+      const int64_t d = c0 + 4 * (v & 15);
+      const int64_t gi = bi0 + row;
+      const bool ok = gi < N && d < D;
+      const float4 t = *reinterpret_cast<const float4*>(xb + (ok ? gi * D + d : 0));
+      vx[q] = ok ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < kVY; ++q) {
+      const int v = (int)threadIdx.x + 256 * q;
+      const int row = v >> 4;
+      const int64_t d = c0 + 4 * (v & 15);
+      const int64_t gj = bj0 + row;
+      const bool ok = gj < M && d < D;
+      const float4 t = *reinterpret_cast<const float4*>(yb + (ok ? gj * D + d : 0));
+      vy[q] = ok ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store64 = [&]() {
+    float* xs = smem;
+    float* ys = xs + TR * kDPK;
+#pragma unroll
+    for (int q = 0; q < kVX; ++q) {
+      const int v = (int)threadIdx.x + 256 * q;
+      *reinterpret_cast<float4*>(xs + (v >> 4) * kDPK + 4 * (v & 15)) = vx[q];
+    }
+#pragma unroll
+    for (int q = 0; q < kVY; ++q) {
+      const int v = (int)threadIdx.x + 256 * q;
+      *reinterpret_cast<float4*>(ys + (v >> 4) * kDPK + 4 * (v & 15)) = vy[q];
+    }
+  };
   const int nslab = (int)((D + kDKC - 1) / kDKC);
-  fetch(0);
-  stash(0);
-  if (nslab > 1) fetch(kDKC);
+  if constexpr (KC == 64) {
+    load64(0);
+    store64();
+  } else {
+    // Double-buffered slabs: slab k is read from buffer k & 1 while slab k+1
+    // is written into the other one, and slab k+2 is fetched into registers;
+    // one barrier per slab.
+    fetch(0);
+    stash(0);
+    if (nslab > 1) fetch(kDKC);
+  }
   __syncthreads();
   for (int k = 0; k < nslab; ++k) {
-    const float* xa = smem + (k & 1) * kSlab + (wr * 64 + r) * kDPK + kk;
-    const float* yb_l = smem + (k & 1) * kSlab + TR * kDPK + (wc * CW + r) * kDPK + kk;
+    const int buf = KC == 16 ? (k & 1) : 0;
+    const float* xa = smem + buf * kSlab + (wr * 64 + r) * kDPK + kk;
+    const float* yb_l = smem + buf * kSlab + TR * kDPK + (wc * CW + r) * kDPK + kk;
     const int64_t s0 = (int64_t)k * (kDKC / 4);
     const int ns = (int)(steps - s0 < kDKC / 4 ? steps - s0 : kDKC / 4);
     for (int sl = 0; sl < ns; ++sl) {  // step s = s0 + sl, feature d = 4s + kk
@@ -118,8 +181,16 @@ __device__ __forceinline__ void dist_block(const float* __restrict__ x,
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bv[j], acc[i][j], 0, 0, 0);
     }
-    if (k + 1 < nslab) stash((k + 1) & 1);
-    if (k + 2 < nslab) fetch((int64_t)(k + 2) * kDKC);
+    if constexpr (KC == 16) {
+      if (k + 1 < nslab) stash((k + 1) & 1);
+      if (k + 2 < nslab) fetch((int64_t)(k + 2) * kDKC);
+    } else {
+      if (k + 1 < nslab) {
+        __syncthreads();   // every wave is done with chunk k
+        load64((int64_t)(k + 1) * kDKC);
+        store64();
+      }
+    }
     __syncthreads();
   }
   // Complete the norms over the four k lane groups (lanes r, r+16, r+32, r+48).
