@@ -398,7 +398,7 @@ def measure_inference(L, torch, x, y, gamma, steps, warmup):
             "workspace_mib": nbytes / 2**20}
 
 
-def peak_mib(torch, SoftDTW, x, y, gamma, fused, checkpoint=False):
+def peak_mib(torch, SoftDTW, x, y, gamma, fused, checkpoint=False, low_memory=False):
     """Peak device memory of one autograd fwd+bwd (SoftDTW(...)(x, y).mean()
     .backward()) above what was allocated before, and the part of it taken
     by x, y and their gradients."""
@@ -409,7 +409,8 @@ def peak_mib(torch, SoftDTW, x, y, gamma, fused, checkpoint=False):
     torch.cuda.reset_peak_memory_stats(dev)
     xg = x.clone().requires_grad_(True)
     yg = y.clone().requires_grad_(True)
-    SoftDTW(gamma=gamma, fused=fused, checkpoint=checkpoint)(xg, yg).mean().backward()
+    SoftDTW(gamma=gamma, fused=fused, checkpoint=checkpoint,
+            low_memory=low_memory)(xg, yg).mean().backward()
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated(dev) - base
     io = 2 * (xg.numel() + yg.numel()) * 4
@@ -509,6 +510,9 @@ def main():
     ms_f, _, _, _ = measure(L, torch, x, y, gamma, L.SDTW_MODE_FUSED,
                             max(5, args.steps // 5), 2)
     peak_f, peak_over_f = peak_mib(torch, SoftDTW, x, y, gamma, True)
+    ms_lm, _, _, _ = measure(L, torch, x, y, gamma, L.SDTW_MODE_UNFUSED_LOWMEM,
+                             max(5, args.steps // 5), 2)
+    peak_lm, peak_over_lm = peak_mib(torch, SoftDTW, x, y, gamma, False, low_memory=True)
     infer = measure_inference(L, torch, x, y, gamma, max(5, args.steps // 5), 2)
 
     per_config = []
@@ -518,13 +522,15 @@ def main():
             x2, y2 = xc2.to(dev), yc2.to(dev)
             entry = {"workload": f"B={b_} N={n_} M={m_} D={d_} gamma={g_}"}
             for mode, name in ((L.SDTW_MODE_UNFUSED, "unfused"), (L.SDTW_MODE_FUSED, "fused"),
-                               (L.SDTW_MODE_CHECKPOINT, "checkpoint")):
+                               (L.SDTW_MODE_CHECKPOINT, "checkpoint"),
+                               (L.SDTW_MODE_UNFUSED_LOWMEM, "unfused_low_memory")):
                 t, _, _, _ = measure(L, torch, x2, y2, g_, mode, 5, 2)
                 pk, pko = peak_mib(torch, SoftDTW, x2, y2, g_, mode == L.SDTW_MODE_FUSED,
-                                   mode == L.SDTW_MODE_CHECKPOINT)
+                                   mode == L.SDTW_MODE_CHECKPOINT,
+                                   mode == L.SDTW_MODE_UNFUSED_LOWMEM)
                 entry[name] = {"ms_per_step": t, "cells_per_s": b_ * n_ * m_ / (t * 1e-3),
                                "peak_mib": pk, "peak_mib_over_io": pko}
-                if mode != L.SDTW_MODE_CHECKPOINT:
+                if mode in (L.SDTW_MODE_UNFUSED, L.SDTW_MODE_FUSED):
                     with_bounds(entry[name], b_, n_, m_, d_, mode == L.SDTW_MODE_FUSED)
             entry["inference"] = measure_inference(L, torch, x2, y2, g_, 5, 2)
             per_config.append(entry)
@@ -552,6 +558,8 @@ def main():
         "fused": with_bounds({"ms_per_step": ms_f, "cells_per_s": cells / (ms_f * 1e-3),
                               "peak_mib": peak_f, "peak_mib_over_io": peak_over_f},
                              B, N, M, D, True),
+        "unfused_low_memory": {"ms_per_step": ms_lm, "cells_per_s": cells / (ms_lm * 1e-3),
+                               "peak_mib": peak_lm, "peak_mib_over_io": peak_over_lm},
         "bounds": with_bounds({"ms_per_step": ms}, B, N, M, D, False),
         "inference": infer,
         "roofline": {"kernel": "both sweeps of the dynamic programme (k_dp_unfused)",

@@ -26,6 +26,7 @@ SDTW_MODE_UNFUSED = 0
 SDTW_MODE_FUSED = 1
 SDTW_MODE_INFERENCE = 2
 SDTW_MODE_CHECKPOINT = 3
+SDTW_MODE_UNFUSED_LOWMEM = 4
 
 # (name, restype, argtypes) for every entry point declared in include/sdtw.h.
 _I64 = ctypes.c_int64

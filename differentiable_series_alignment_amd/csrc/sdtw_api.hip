@@ -25,7 +25,9 @@ struct Layout {
   size_t loss64 = 0;                // fp64 [B]
   size_t H = 0;                     // fp64 [2, B, nseg, M] segment hand-off rows
   size_t R = 0;                     // fp64 band-step forward state
-  size_t R2 = 0;                    // fp64 band-step reverse soft-min parts (unfused)
+  size_t R2 = 0;                    // fp64 band-step reverse soft-min parts (unfused, concurrent)
+  bool seq = false;                 // low-memory unfused: sweeps in turn, E formed by the reverse
+  size_t eflag = 0;                 // index of the E-formed flag among the control words (seq)
   size_t part = 0;                  // fp32 split partial sums of the chain rule (unfused)
   size_t cnt_rows = 0, cnt_cols = 0;  // word offsets of the chain split counters
   size_t dist = 0;                  // fp32 band-step distances, then E (unfused)
@@ -89,7 +91,7 @@ bool sizes_ok(int64_t B, int64_t N, int64_t M, int64_t D) {
 bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L) {
   if (!sizes_ok(B, N, M, D) ||
       (mode != SDTW_MODE_UNFUSED && mode != SDTW_MODE_FUSED && mode != SDTW_MODE_INFERENCE &&
-       mode != SDTW_MODE_CHECKPOINT))
+       mode != SDTW_MODE_CHECKPOINT && mode != SDTW_MODE_UNFUSED_LOWMEM))
     return false;
   L->nbands = (N + 63) / 64;
   if (mode == SDTW_MODE_CHECKPOINT) {
@@ -153,6 +155,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   L->cnt_rows = 2 * (2 + (size_t)B * (size_t)L->nseg);
   L->cnt_cols = L->cnt_rows + (size_t)B * (size_t)L->nbands;
   L->ctrl_words = L->cnt_cols + (size_t)B * (size_t)((M + 63) / 64);
+  L->eflag = L->ctrl_words++;
   L->err_word = L->ctrl_words++;
   off += align_up(L->ctrl_words * 4);
   L->loss64 = off;
@@ -161,9 +164,14 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   off += align_up(2 * (size_t)B * (size_t)L->nseg * (size_t)M * 8);
   L->R = off;
   off += align_up(cells * 8);
-  if (mode == SDTW_MODE_UNFUSED) {
-    L->R2 = off;
-    off += align_up(cells * 8);
+  if (mode == SDTW_MODE_UNFUSED || mode == SDTW_MODE_UNFUSED_LOWMEM) {
+    // Low-memory unfused: the sweeps one after the other, the reverse one
+    // forming E over the distances, so T' is never stored.
+    L->seq = mode == SDTW_MODE_UNFUSED_LOWMEM;
+    if (!L->seq) {
+      L->R2 = off;
+      off += align_up(cells * 8);
+    }
     L->part = off;
     off += align_up(sdtw::chain_part_floats(B, N, M, D, L->S) * 4);
     L->dist = off;
@@ -208,6 +216,8 @@ DPArgs dp_args(const Layout& L, char* ws, const float* x, const float* y,
   a.nseg = (int)L.nseg;
   a.err = reinterpret_cast<unsigned*>(ws + L.ctrl) + L.err_word;
   a.wait_cap = g_wait_cap.load(std::memory_order_relaxed);
+  a.sweeps = sdtw::kSweepsBoth;
+  a.eflag = reinterpret_cast<unsigned*>(ws + L.ctrl) + L.eflag;
   const double g = (double)gamma;
   a.k2 = M_LOG2E / g;
   a.g_ln2 = g * M_LN2;
@@ -333,11 +343,15 @@ int forward_impl(const float* x, const float* y, int64_t B, int64_t N, int64_t M
     a.hvalid = 1;
     if (e == hipSuccess) e = sdtw::launch_dp_fused(a, false, s);
   } else {
-    // Both sweeps at once: the loss comes from the forward one, and the
-    // reverse one leaves what the backward needs besides the forward state.
+    // Unfused: both sweeps at once; the loss comes from the forward one, and
+    // the reverse one leaves what the backward needs besides the forward
+    // state.  Low-memory unfused: the forward sweep alone (the backward runs
+    // the reverse).  The distance kernel also clears the control words,
+    // E-formed flag included.
     e = sdtw::launch_dist_skew(x, y, a.dsk, B, N, M, D, L.S, ctrl, (int64_t)L.ctrl_words, a.H,
                                hrow_doubles(L, B, M), s);
     a.hvalid = 1;
+    a.sweeps = L.seq ? sdtw::kSweepForward : sdtw::kSweepsBoth;
     if (e == hipSuccess) e = sdtw::launch_dp_both(a, s);
   }
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
@@ -414,14 +428,23 @@ int sdtw_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t 
     return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
   }
   // Unfused: both sweeps ran in the forward; the chain rule forms E from
-  // their states (the distances are not read again), so repeated backward
-  // calls on one forward are all valid.
+  // their states (the distances are not read again).  Low-memory unfused:
+  // the reverse sweep forms E over the distances, once per forward (a
+  // repeated backward finds the E-formed flag set and reuses E); the chain
+  // rule reads it.  Either way repeated backward calls on one forward are
+  // all valid.
   if (!grad_x && !grad_y && !align) return SDTW_OK;
   unsigned* ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl);
-  hipError_t e = sdtw::launch_chain(a.dsk, a.R, a.R2, a.loss64, x, y, grad_loss, grad_x,
-                                    grad_y, B, N, M, D, L.S,
-                                    reinterpret_cast<float*>(ws + L.part),
-                                    ctrl + L.cnt_rows, ctrl + L.cnt_cols, align != nullptr, s);
+  hipError_t e = hipSuccess;
+  if (L.seq) {
+    a.sweeps = sdtw::kSweepReverseE;
+    a.hvalid = 1;   // the reverse half of the hand-off rows is still at kHEmpty
+    e = sdtw::launch_dp_both(a, s);
+  }
+  if (e == hipSuccess)
+    e = sdtw::launch_chain(a.dsk, a.R, a.R2, a.loss64, x, y, grad_loss, grad_x, grad_y, B, N,
+                           M, D, L.S, reinterpret_cast<float*>(ws + L.part), ctrl + L.cnt_rows,
+                           ctrl + L.cnt_cols, align != nullptr, L.seq, s);
   if (e == hipSuccess && align) e = sdtw::launch_unskew(a.dsk, align, B, N, M, L.S, s);
   return e == hipSuccess ? SDTW_OK : SDTW_ERR_HIP;
 }

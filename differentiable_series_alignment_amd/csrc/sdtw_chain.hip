@@ -627,11 +627,11 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
                         const double* loss64, const float* x, const float* y,
                         const float* gl, float* gx, float* gy, int64_t B, int64_t N,
                         int64_t M, int64_t D, int64_t S, float* part, unsigned* cnt_rows,
-                        unsigned* cnt_cols, bool keep_e, hipStream_t s) {
+                        unsigned* cnt_cols, bool keep_e, bool e_ready, hipStream_t s) {
   const int nb = (int)((N + 63) / 64);
   const unsigned pr = (unsigned)chain_splits_rows(B, N, M, D, S);
   const unsigned pc = (unsigned)chain_splits_cols(B, N, M);
-  if (gy && !keep_e && chain_gy_fits(M, D, S)) {
+  if (gy && !keep_e && !e_ready && chain_gy_fits(M, D, S)) {
     // One row pass makes dx and the bands' shares of dy (in place of E);
     // a short pass adds the shares up.  Its split partial sums go after the
     // shares.
@@ -651,7 +651,7 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
     if (d0 > 0 && !gx) break;
     const int64_t dw = D - d0 < 128 ? D - d0 : 128;
     const bool two = dw > 64;  // more than two 32-wide d tiles
-    if (d0 == 0) {
+    if (d0 == 0 && !e_ready) {
       if (two)
         launch_rows<2, true>(B, pr, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, d0, part, cnt_rows);
       else

@@ -53,16 +53,23 @@ __global__ void k_zero_u32(unsigned* p, int64_t n) {
 // enters through the initial state of lane 0 of the first band.  Cells past
 // the last column or below the last row compute unused values in padding
 // storage; no real cell depends on them.  The forward sweep stores X, the
-// reverse sweep its soft-minimum part T'.
-template <bool REV, bool MASK>
+// reverse sweep its soft-minimum part T'.  EFORM (reverse sweep after a
+// completed forward): the cell's X comes in xn and the reverse sweep stores
+// E = 2^(Xnm - X - T') in place of its distance (ep), 0 outside the grid
+// (sweep column t0 + u - lane outside 0..M-1, or a padding row).
+template <bool REV, bool MASK, bool EFORM = false>
 __device__ __forceinline__ void band_chunk(double& cur, double& up, const double (&top)[16],
                                            const float (&dn)[16], double (&bottom)[16],
                                            int t0, int lane, double k2,
-                                           double* __restrict__ sp) {
+                                           double* __restrict__ sp,
+                                           const double (&xn)[EFORM ? 16 : 1],
+                                           float* __restrict__ ep, double xnm, bool row_ok,
+                                           int M) {
   constexpr int dir = REV ? -64 : 64;
   // Steps 8..15 address from a second base so every store of the chunk is
   // base + immediate offset.
   double* const sp8 = sp + 8 * dir;
+  float* const ep8 = ep + 8 * dir;
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     double d = (double)dn[u] * k2;
@@ -73,7 +80,14 @@ __device__ __forceinline__ void band_chunk(double& cur, double& up, const double
     up = upn;
     cur = c;
     bottom[u] = c;
-    __builtin_nontemporal_store(REV ? t : c, (u < 8 ? sp : sp8) + (u & 7) * dir);
+    if (EFORM) {
+      const int jc = t0 + u - lane;
+      const bool ok = row_ok && jc >= 0 && jc < M;
+      const float e = ok ? align_entry(xnm, xn[EFORM ? u : 0], t) : 0.f;
+      __builtin_nontemporal_store(e, (u < 8 ? ep : ep8) + (u & 7) * dir);
+    } else {
+      __builtin_nontemporal_store(REV ? t : c, (u < 8 ? sp : sp8) + (u & 7) * dir);
+    }
   }
 }
 
@@ -91,6 +105,15 @@ __device__ __forceinline__ void load_chunk(const float* dbase, int64_t off, floa
 #pragma unroll
   for (int u = 0; u < 16; ++u) dn[u] = (u < 8 ? d0 : d8)[(u & 7) * dir];
 }
+// The same for the forward states X the E-forming reverse sweep reads.
+template <bool REV>
+__device__ __forceinline__ void load_xchunk(const double* xbase, int64_t off, double (&xn)[16]) {
+  constexpr int dir = REV ? -64 : 64;
+  const double* x0 = xbase + off;
+  const double* x8 = x0 + 8 * dir;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) xn[u] = (u < 8 ? x0 : x8)[(u & 7) * dir];
+}
 
 // One band of one pair, swept column chunk by column chunk.  The band's top
 // row comes from LDS ring `w`: the previous band's bottom row, the row the
@@ -104,7 +127,7 @@ __device__ __forceinline__ void load_chunk(const float* dbase, int64_t off, floa
 // without touching LDS, otherwise it polls and reads them again.  LDS
 // operations of one wave complete in issue order, so entries read after a
 // count that covers them are the published ones.
-template <bool REV>
+template <bool REV, bool EFORM = false>
 __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int w, int nb_seg,
                                            double (*ring)[kRingC + kCH], unsigned* wr,
                                            unsigned* rd, int lane) {
@@ -119,7 +142,12 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
 
   const LaneCursor cu = lane_cursor(REV, b, i, lane, N, M, a.nbands, S);
   const float* const dbase = a.dsk + cu.base;
-  double* const sbase = (REV ? a.R2 : a.R) + cu.base;
+  // EFORM: X of the same cells (same element index), E over the distances.
+  double* const sbase = EFORM ? nullptr : (REV ? a.R2 : a.R) + cu.base;
+  const double* const xsrc = EFORM ? a.R + cu.base : nullptr;
+  float* const ebase = EFORM ? a.dsk + cu.base : nullptr;
+  const double xnm = EFORM ? a.loss64[b] : 0.0;
+  const bool row_ok = i < N;
   const double k2 = a.k2;
 
   // Final cell (forward sweep): row N-1, column M-1.
@@ -135,7 +163,9 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
   // Chunk inputs alternate between two register sets: chunk q computes from
   // one while the requests for chunk q+1 fill the other.
   float dnA[kCH], dnB[kCH];
+  double xA[EFORM ? kCH : 1], xB[EFORM ? kCH : 1];
   load_chunk<REV>(dbase, 0, dnA);
+  if constexpr (EFORM) load_xchunk<REV>(xsrc, 0, xA);
   // Top entries of the first chunk and the count they were read under.
   double top[kCH];
   unsigned seen_wr = __hip_atomic_load(&wr[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -144,7 +174,8 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
   for (int u = 0; u < kCH; ++u) top[u] = ring[w][u];
   __builtin_amdgcn_s_waitcnt(0);
 
-  auto chunk = [&](int q, const float (&dn)[kCH], float (&dn2)[kCH]) {
+  auto chunk = [&](int q, const float (&dn)[kCH], float (&dn2)[kCH],
+                   const double (&xn)[EFORM ? kCH : 1], double (&xn2)[EFORM ? kCH : 1]) {
     const int t0 = q * kCH;
     // This chunk's loads were issued before the previous chunk's 16 stores;
     // the vector-memory counter retires in issue order, so allowing 16
@@ -159,13 +190,27 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
     }
     // Unconditional (the last chunk re-reads its own cells), so the
     // compiler's wait bookkeeping stays exact across the loop.
-    load_chunk<REV>(dbase, (int64_t)(q + 1 < qcount ? t0 + kCH : t0) * cu.dir, dn2);
+    const int64_t noff = (int64_t)(q + 1 < qcount ? t0 + kCH : t0) * cu.dir;
+    load_chunk<REV>(dbase, noff, dn2);
     double bottom[kCH];
-    double* sp = sbase + (int64_t)t0 * cu.dir;
-    if (t0 < 64)
-      band_chunk<REV, true>(cur, up, top, dn, bottom, t0, lane, k2, sp);
-    else
-      band_chunk<REV, false>(cur, up, top, dn, bottom, t0, lane, k2, sp);
+    if constexpr (EFORM) {
+      load_xchunk<REV>(xsrc, noff, xn2);
+      float* ep = ebase + (int64_t)t0 * cu.dir;
+      if (t0 < 64)
+        band_chunk<REV, true, true>(cur, up, top, dn, bottom, t0, lane, k2, nullptr, xn, ep,
+                                    xnm, row_ok, (int)M);
+      else
+        band_chunk<REV, false, true>(cur, up, top, dn, bottom, t0, lane, k2, nullptr, xn, ep,
+                                     xnm, row_ok, (int)M);
+    } else {
+      double* sp = sbase + (int64_t)t0 * cu.dir;
+      if (t0 < 64)
+        band_chunk<REV, true>(cur, up, top, dn, bottom, t0, lane, k2, sp, xn, nullptr, 0.0,
+                              true, 0);
+      else
+        band_chunk<REV, false>(cur, up, top, dn, bottom, t0, lane, k2, sp, xn, nullptr, 0.0,
+                               true, 0);
+    }
 
     if (has_last && q == qlast) {
       double v = 0.0;
@@ -211,33 +256,43 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
   };
 
   for (int q = 0; q < qcount; q += 2) {
-    chunk(q, dnA, dnB);
-    if (q + 1 < qcount) chunk(q + 1, dnB, dnA);
+    chunk(q, dnA, dnB, xA, xB);
+    if (q + 1 < qcount) chunk(q + 1, dnB, dnA, xB, xA);
   }
 }
 
-// Both sweeps in one launch.  Tickets alternate between the sweeps, so the
-// forward and reverse workgroups of a pair start together; within a sweep a
-// segment waits only on the previous segment, which holds a smaller ticket.
-// Control words: [0] ticket, [1] finished workgroups, [2 + sweep*B*nseg +
-// b*nseg + s] columns published by segment s of pair b; H holds one bottom
-// row per (sweep, pair, segment).
+// Both sweeps in one launch (a.sweeps == kSweepsBoth), or one of them.  With
+// both, tickets alternate between the sweeps, so the forward and reverse
+// workgroups of a pair start together; within a sweep a segment waits only
+// on the previous segment, which holds a smaller ticket.  Control words: [0]
+// ticket, [1] finished workgroups, [2 + sweep*B*nseg + b*nseg + s] columns
+// published by segment s of pair b; H holds one bottom row per (sweep, pair,
+// segment).  The E-forming reverse sweep (kSweepReverseE) runs once per
+// forward: its last workgroup sets *a.eflag, and a launch that finds the
+// flag set (a repeated backward) leaves E as it is.
+// ERV: the E-forming reverse sweep (its own instance: the forward states it
+// reads take registers the other sweeps do not need).
+template <bool ERV>
 __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a) {
   constexpr int W = kBandsPerWG;
   __shared__ double ring[W + 1][kRingC + kCH];   // + pad, see band_sweep
   __shared__ unsigned wr[W + 1], rd[W + 1];
-  __shared__ unsigned s_ticket;
+  __shared__ unsigned s_ticket, s_skip;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  constexpr bool eform = ERV;
   if (threadIdx.x == 0) {
     s_ticket = atomicAdd(&a.ctrl[0], 1u);
+    s_skip = eform ? __hip_atomic_load(a.eflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : 0u;
     launch_shared_init(a);
   }
   __syncthreads();
   const unsigned ticket = s_ticket;
-  const int rev = (int)(ticket & 1u);
-  const unsigned rest = ticket >> 1;
+  const bool both = !ERV && a.sweeps == kSweepsBoth;
+  const int rev = both ? (int)(ticket & 1u) : (eform ? 1 : 0);
+  const unsigned rest = both ? ticket >> 1 : ticket;
   const int seg = (int)(rest / (unsigned)a.B);
   const int b = (int)(rest % (unsigned)a.B);
   // The first band of a pair reads its top row (the +inf boundary) from
@@ -252,7 +307,9 @@ __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a)
   const int nb_seg = min(W, a.nbands - seg * W);
   const int64_t per_sweep = (int64_t)a.B * a.nseg;
 
-  if (w == W) {
+  if (s_skip) {
+    // E already formed for this forward: nothing to do.
+  } else if (w == W) {
     const int64_t pb = rev * per_sweep + (int64_t)b * a.nseg;
     const int64_t sin = pb + (seg > 0 ? seg - 1 : 0), sout = pb + seg;
     GlobalRow gr{0u, nullptr, nullptr};
@@ -261,12 +318,16 @@ __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a)
                     a.H + sin * a.M, a.H + sout * a.M, ring[0], &wr[0], &rd[0], ring[W],
                     &wr[W], &rd[W], (unsigned)a.M, lane, gr);
   } else if (w < nb_seg) {
-    if (rev)
+    if constexpr (ERV)
+      band_sweep<true, true>(a, b, seg, w, nb_seg, ring, wr, rd, lane);
+    else if (rev)
       band_sweep<true>(a, b, seg, w, nb_seg, ring, wr, rd, lane);
     else
       band_sweep<false>(a, b, seg, w, nb_seg, ring, wr, rd, lane);
   }
-  release_ctrl(a.ctrl, 2 * per_sweep);
+  const bool last = release_ctrl(a.ctrl, 2 * per_sweep);
+  if (last && eform && !s_skip && threadIdx.x == 0)
+    __hip_atomic_store(a.eflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Control words to zero and hand-off entries to kHEmpty, in one launch.
@@ -321,9 +382,13 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_dp_both(const DPArgs& a, hipStream_t s) {
-  const unsigned grid = 2u * (unsigned)a.B * (unsigned)a.nseg;
-  TimedLaunch timed_("dp_both", s);
-  hipLaunchKernelGGL(k_dp_unfused, dim3(grid), dim3((kBandsPerWG + 1) * 64), 0, s, a);
+  const unsigned grid = (a.sweeps == kSweepsBoth ? 2u : 1u) * (unsigned)a.B * (unsigned)a.nseg;
+  TimedLaunch timed_(a.sweeps == kSweepsBoth ? "dp_both"
+                     : a.sweeps == kSweepForward ? "dp_forward" : "dp_reverse_e", s);
+  if (a.sweeps == kSweepReverseE)
+    hipLaunchKernelGGL(k_dp_unfused<true>, dim3(grid), dim3((kBandsPerWG + 1) * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_dp_unfused<false>, dim3(grid), dim3((kBandsPerWG + 1) * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -94,7 +94,8 @@ __device__ __forceinline__ void poison_outputs() {
 // workspace starts clean without a separate clearing launch (every other
 // workgroup has stopped touching them once it has counted itself finished),
 // and, if any wait of the launch gave up, poisons the launch's outputs.
-__device__ __forceinline__ void release_ctrl(unsigned* ctrl, int64_t nprog) {
+// Returns true in the last workgroup (every other one has finished).
+__device__ __forceinline__ bool release_ctrl(unsigned* ctrl, int64_t nprog) {
   __shared__ unsigned s_last;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -112,6 +113,7 @@ __device__ __forceinline__ void release_ctrl(unsigned* ctrl, int64_t nprog) {
   unsigned* const err = launch_shared().err;
   if (s_last && err && __hip_atomic_load(err, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0u)
     poison_outputs();
+  return s_last;
 }
 
 // Hand-off stress (debug builds only: SDTW_STRESS=1, built as

@@ -80,7 +80,15 @@ struct DPArgs {
   // replaces the wait caps (0: built-in caps; sdtw_debug_wait_limit).
   unsigned* err;
   unsigned wait_cap;
+  // Unfused sweeps of one launch: kSweepsBoth (forward and reverse at once,
+  // the reverse keeping T' in R2), kSweepForward, or kSweepReverseE (the
+  // reverse after a completed forward: it reads X from R and writes E over
+  // the distances, then sets *eflag; a launch that finds *eflag set does
+  // nothing, so E is formed once per forward).
+  int sweeps;
+  unsigned* eflag;
 };
+constexpr int kSweepsBoth = 0, kSweepForward = 1, kSweepReverseE = 2;
 // Padding on each side of a stored checkpoint row (columns the band wave
 // touches outside 0..M-1 land there).
 constexpr int64_t kCkPad = 80;
@@ -138,7 +146,9 @@ hipError_t launch_clear(unsigned* zero, int64_t nzero, double* empty, int64_t ne
 hipError_t launch_unskew(const float* esk, float* out, int64_t B, int64_t N,
                          int64_t M, int64_t S, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
-// Unfused: both sweeps of every pair in one launch (X into R, T' into R2).
+// Unfused: the sweeps of a.sweeps for every pair in one launch: both (X into
+// R, T' into R2), the forward alone (X into R), or the reverse alone forming
+// E over the distances (see DPArgs::sweeps).
 hipError_t launch_dp_both(const DPArgs& a, hipStream_t s);
 // Fused: one sweep per launch (the reverse one with the chain rule inside).
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s);
@@ -156,7 +166,8 @@ hipError_t launch_fill_u32(unsigned* p, int64_t n, unsigned v, hipStream_t s);
 // gx is given, writes dx; the column pass reads E from `esk` and writes dy.
 // With D <= 64 and E not wanted afterwards (keep_e false) the row pass
 // writes the bands' shares of dy into `esk` instead and a short pass adds
-// them up.
+// them up.  e_ready: E is already in `esk` (formed by the reverse sweep);
+// every pass reads it and R, R2 are not used.
 // Small problems split each sum over several workgroups: `part` holds
 // chain_part_floats() floats of partial sums and the counters (B*nbands for
 // the rows, B*ceil(M/64) for the columns) start at zero and are left at zero.
@@ -167,6 +178,6 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
                         const double* loss64, const float* x, const float* y,
                         const float* gl, float* gx, float* gy, int64_t B, int64_t N,
                         int64_t M, int64_t D, int64_t S, float* part, unsigned* cnt_rows,
-                        unsigned* cnt_cols, bool keep_e, hipStream_t s);
+                        unsigned* cnt_cols, bool keep_e, bool e_ready, hipStream_t s);
 
 }  // namespace sdtw

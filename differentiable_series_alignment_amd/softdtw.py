@@ -119,34 +119,45 @@ def _loss_only(x: torch.Tensor, y: torch.Tensor, gamma: float):
     return loss
 
 
-def choose_fused(fused, B: int, N: int, M: int, D: int, device=None) -> bool:
-    """Resolve ``fused``: True/False as given; None or "auto" selects the mode
-    (README "Time Series Barycenters", key options: fused auto-selects
-    between memory and speed).  Reading: the unfused mode is the faster one
-    here, so it is kept unless its workspace would take more than half of
-    the free device memory and fused mode supports D."""
+def choose_mode(fused, B: int, N: int, M: int, D: int, device=None) -> int:
+    """The training mode for ``fused``: True -> fused, False -> unfused; None
+    or "auto" selects between memory and speed (README "Time Series
+    Barycenters", key options: fused auto-selects between memory and speed).
+    Reading: the fastest mode whose workspace takes at most half of the free
+    device memory, in the order unfused (about 20 bytes per cell),
+    low-memory unfused (about 12), fused (8, D <= 256); unfused if none
+    does."""
     if fused is None or (isinstance(fused, str) and fused == "auto"):
-        if L.sdtw_workspace_bytes(B, N, M, D, L.SDTW_MODE_FUSED) == 0:
-            return False
-        need = L.sdtw_workspace_bytes(B, N, M, D, L.SDTW_MODE_UNFUSED)
         free, _ = torch.cuda.mem_get_info(device)
-        return need == 0 or need > free // 2
+        for mode in (L.SDTW_MODE_UNFUSED, L.SDTW_MODE_UNFUSED_LOWMEM, L.SDTW_MODE_FUSED):
+            need = L.sdtw_workspace_bytes(B, N, M, D, mode)
+            if 0 < need <= free // 2:
+                return mode
+        return L.SDTW_MODE_UNFUSED
     if isinstance(fused, str):
         raise ValueError(f"fused must be True, False, None or 'auto', got {fused!r}")
-    return bool(fused)
+    return L.SDTW_MODE_FUSED if bool(fused) else L.SDTW_MODE_UNFUSED
+
+
+def choose_fused(fused, B: int, N: int, M: int, D: int, device=None) -> bool:
+    """Whether choose_mode picks the fused mode."""
+    return choose_mode(fused, B, N, M, D, device) == L.SDTW_MODE_FUSED
 
 
 def soft_dtw(x: torch.Tensor, y: torch.Tensor, gamma: float = 1.0,
-             fused=False, checkpoint: bool = False) -> torch.Tensor:
+             fused=False, checkpoint: bool = False, low_memory: bool = False) -> torch.Tensor:
     """Per-pair Soft-DTW loss (B,) with autograd support.  When no gradient
     can be asked for (autograd off, or neither input requires one) the loss
     comes from the inference mode, which keeps no state; its value is bitwise
     the one of the other modes.  ``fused``: True, False, or None / "auto"
-    (see choose_fused).  ``checkpoint=True`` trains with distances recomputed
+    (see choose_mode).  ``checkpoint=True`` trains with distances recomputed
     as in fused mode and without the B x N x M forward state: the backward
     recomputes it group by group of rows from checkpoint rows (about
     sqrt(N/64) groups), for a workspace of about sqrt(N/64) x 64 rows of M
-    states per pair instead of N."""
+    states per pair instead of N.  ``low_memory=True`` (with fused=False)
+    trains in the low-memory unfused mode: the sweeps run one after the
+    other and the reverse one forms the alignment matrix over the distances
+    (about 12 instead of 20 bytes of workspace per cell; same results)."""
     _validate(x, y, gamma)
     if not (torch.is_grad_enabled() and (x.requires_grad or y.requires_grad)):
         loss = _loss_only(x, y, float(gamma))
@@ -156,8 +167,9 @@ def soft_dtw(x: torch.Tensor, y: torch.Tensor, gamma: float = 1.0,
     if checkpoint:
         mode = L.SDTW_MODE_CHECKPOINT
     else:
-        use_fused = choose_fused(fused, B, N, y.shape[1], D, x.device)
-        mode = L.SDTW_MODE_FUSED if use_fused else L.SDTW_MODE_UNFUSED
+        mode = choose_mode(fused, B, N, y.shape[1], D, x.device)
+        if low_memory and mode == L.SDTW_MODE_UNFUSED:
+            mode = L.SDTW_MODE_UNFUSED_LOWMEM
     return _SoftDTWFunction.apply(x, y, float(gamma), mode)
 
 
@@ -169,7 +181,8 @@ class SoftDTW(torch.nn.Module):
     terms run as one batch of 3B pairs."""
 
     def __init__(self, gamma: float = 1.0, dist: str = "sqeuclidean",
-                 fused=False, normalize: bool = False, checkpoint: bool = False):
+                 fused=False, normalize: bool = False, checkpoint: bool = False,
+                 low_memory: bool = False):
         super().__init__()
         if dist != "sqeuclidean":
             raise ValueError(f"only dist='sqeuclidean' is supported, got {dist!r}")
@@ -183,6 +196,7 @@ class SoftDTW(torch.nn.Module):
         self.fused = fused if (fused is None or isinstance(fused, str)) else bool(fused)
         self.normalize = bool(normalize)
         self.checkpoint = bool(checkpoint)
+        self.low_memory = bool(low_memory)
 
     def forward(self, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
         if self.normalize:
@@ -194,13 +208,14 @@ class SoftDTW(torch.nn.Module):
             # reach x and y through the concatenation.
             B = x.shape[0]
             loss = soft_dtw(torch.cat([x, x, y], 0), torch.cat([y, x, y], 0),
-                            self.gamma, self.fused, self.checkpoint)
+                            self.gamma, self.fused, self.checkpoint, self.low_memory)
             return loss[:B] - 0.5 * (loss[B:2 * B] + loss[2 * B:])
-        return soft_dtw(x, y, self.gamma, self.fused, self.checkpoint)
+        return soft_dtw(x, y, self.gamma, self.fused, self.checkpoint, self.low_memory)
 
     def extra_repr(self) -> str:
         return (f"gamma={self.gamma}, dist={self.dist!r}, fused={self.fused}, "
-                f"normalize={self.normalize}, checkpoint={self.checkpoint}")
+                f"normalize={self.normalize}, checkpoint={self.checkpoint}, "
+                f"low_memory={self.low_memory}")
 
 
 def sqeuclidean(x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
@@ -280,7 +295,7 @@ def softdtw_barycenter(sequences: torch.Tensor, gamma: float = 1.0,
     at the pointwise mean and minimises mean_k SoftDTW(z, X_k).
 
     Options of the README ("Time Series Barycenters" key options and
-    "Benchmarking"): ``fused`` True/False or None/"auto" (choose_fused);
+    "Benchmarking"): ``fused`` True/False or None/"auto" (choose_mode);
     ``early_stopping`` (EarlyStopping(patience, tol)); ``cosine_annealing``
     (the learning rate follows lr*(1+cos(pi*t/max_iter))/2 over the
     iterations, torch's CosineAnnealingLR); ``grad_clip`` (the gradient's L2
@@ -296,8 +311,7 @@ def softdtw_barycenter(sequences: torch.Tensor, gamma: float = 1.0,
     K, N, D = X.shape
     g = float(gamma)
     dev = X.device
-    use_fused = choose_fused(fused, K, N, N, D, dev)
-    mode = L.SDTW_MODE_FUSED if use_fused else L.SDTW_MODE_UNFUSED
+    mode = choose_mode(fused, K, N, N, D, dev)
     z = X.mean(dim=0).clone().requires_grad_(True)
     # torch's single-kernel Adam: the same update as the default one, with a
     # fraction of its host time (which bounds this loop: its kernels take

@@ -25,7 +25,19 @@
  *                      (fp64); the backward forms E from them and applies
  *                      the chain rule, using the distance region for E (or,
  *                      for D <= 64 without an alignment output, for each
- *                      64-row band's share of grad_y).
+ *                      64-row band's share of grad_y).  About 20 bytes of
+ *                      workspace per cell.
+ *   SDTW_MODE_UNFUSED_LOWMEM the unfused computation with the sweeps one
+ *                      after the other: the forward runs the forward sweep
+ *                      and keeps its state; the backward runs the reverse
+ *                      sweep, which forms E over the distances (once per
+ *                      forward: a repeated backward reuses it), then the
+ *                      chain rule with the column pass for grad_y.  About
+ *                      12 bytes per cell; slower than SDTW_MODE_UNFUSED
+ *                      (one sweep at a time keeps fewer loads in flight),
+ *                      faster than SDTW_MODE_FUSED.  Loss, E and grad_x are
+ *                      bitwise those of SDTW_MODE_UNFUSED, grad_y too where
+ *                      that mode takes the column pass (D > 64 or align).
  *   SDTW_MODE_FUSED    recomputes distances from x and y inside the dynamic
  *                      programme; no B x N x M distance or E tensor exists.
  *                      Supports D <= 256 (sdtw_workspace_bytes returns 0 and
@@ -102,7 +114,7 @@
 extern "C" {
 #endif
 
-#define SDTW_ABI_VERSION 2
+#define SDTW_ABI_VERSION 3
 
 typedef enum {
     SDTW_OK = 0,
@@ -117,7 +129,8 @@ typedef enum {
     SDTW_MODE_UNFUSED = 0,
     SDTW_MODE_FUSED = 1,
     SDTW_MODE_INFERENCE = 2,
-    SDTW_MODE_CHECKPOINT = 3
+    SDTW_MODE_CHECKPOINT = 3,
+    SDTW_MODE_UNFUSED_LOWMEM = 4
 } sdtw_mode_t;
 
 /* Version of this ABI (SDTW_ABI_VERSION). */

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = L.lib()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert L.sdtw_abi_version() == 2
+    assert L.sdtw_abi_version() == 3
 
 
 def test_stress_build_exports_the_same_symbols():
@@ -84,7 +84,7 @@ def _bwd(**kw):
 @pytest.mark.parametrize("kw", [
     dict(gamma=0.0), dict(gamma=-1.0), dict(gamma=float("nan")), dict(gamma=float("inf")),
     dict(B=0), dict(N=0), dict(M=0), dict(D=0), dict(N=-3),
-    dict(x=None), dict(y=None), dict(mode=4), dict(mode=-1), dict(workspace=None),
+    dict(x=None), dict(y=None), dict(mode=5), dict(mode=-1), dict(workspace=None),
     dict(workspace=FAKE * 256 + 8),
 ])
 def test_forward_backward_reject_invalid(kw):
@@ -264,6 +264,18 @@ def test_status_query_and_wait_limit_validation():
     assert L.sdtw_debug_wait_limit(1 << 32) == L.SDTW_ERR_INVALID_ARG
     assert L.sdtw_debug_wait_limit(0) == L.SDTW_OK
     assert "gave up" in L.sdtw_status_string(L.SDTW_ERR_STALLED)
+
+
+def test_low_memory_unfused_workspace():
+    """The low-memory unfused mode keeps no reverse state: at least 8 bytes
+    per cell less than the unfused mode and more than the fused one."""
+    cells = 32 * 512 * 512
+    unf = L.sdtw_workspace_bytes(32, 512, 512, 64, L.SDTW_MODE_UNFUSED)
+    low = L.sdtw_workspace_bytes(32, 512, 512, 64, L.SDTW_MODE_UNFUSED_LOWMEM)
+    fus = L.sdtw_workspace_bytes(32, 512, 512, 64, L.SDTW_MODE_FUSED)
+    assert (unf - low) >= 8 * cells and low > fus > 0
+    assert L.sdtw_workspace_bytes(2, 10, 10, 1000, L.SDTW_MODE_UNFUSED_LOWMEM) > 0   # any D
+    assert L.sdtw_workspace_bytes(1, 4, 4, 1, 5) == 0
 
 
 def test_static_forward_validation_on_host():

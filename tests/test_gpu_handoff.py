@@ -46,6 +46,7 @@ def run(L, mode, x, y, gamma, ws, grads=True):
     (2, (3, 1100, 700, 5)),    # inference through 512-column rings
     (2, (3, 130, 90, 4)),      # inference with whole rows
     (3, (2, 300, 200, 5)),     # checkpointed training
+    (4, (4, 300, 500, 8)),     # low-memory unfused: forward sweep, then the E-forming reverse
 ])
 def test_wait_giveup_is_reported(L, mode, shape):
     B, N, M, D = shape

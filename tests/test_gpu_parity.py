@@ -30,10 +30,10 @@ def S():
     return pkg
 
 
-def gpu_value_and_grad(S, x, y, gamma, fused=False, checkpoint=False):
+def gpu_value_and_grad(S, x, y, gamma, fused=False, checkpoint=False, low_memory=False):
     xd = x.to(DEV).requires_grad_(True)
     yd = y.to(DEV).requires_grad_(True)
-    loss = S.soft_dtw(xd, yd, gamma, fused=fused, checkpoint=checkpoint)
+    loss = S.soft_dtw(xd, yd, gamma, fused=fused, checkpoint=checkpoint, low_memory=low_memory)
     loss.mean().backward()
     torch.cuda.synchronize()
     return (loss.detach().cpu().double().numpy(), xd.grad.cpu().double().numpy(),
@@ -53,8 +53,8 @@ def assert_grad(g, g0, what=""):
                            f"out of tolerance, max err {err.max():.3e}")
 
 
-def check_against_oracle(O, S, x, y, gamma, fused=False, pairs=None, what=""):
-    l, gx, gy = gpu_value_and_grad(S, x, y, gamma, fused)
+def check_against_oracle(O, S, x, y, gamma, fused=False, pairs=None, what="", low_memory=False):
+    l, gx, gy = gpu_value_and_grad(S, x, y, gamma, fused, low_memory=low_memory)
     assert np.isfinite(l).all() and np.isfinite(gx).all() and np.isfinite(gy).all()
     B = x.shape[0]
     idx = list(range(B)) if pairs is None else list(pairs)
@@ -189,6 +189,19 @@ def test_long_sequences(O, S, N, M, gamma, fused):
     assert (np.abs(s) <= 1e-4 * scale).all()
 
 
+@pytest.mark.parametrize("N,M", [(2048, 2048), (4096, 1000)])
+@pytest.mark.parametrize("gamma", [1.0, 0.01])
+def test_long_sequences_low_memory(O, S, N, M, gamma):
+    """The low-memory unfused mode at B=32, D=128 against the oracle (pairs
+    0 and 31), with every pair finite and translation invariant."""
+    x, y = pair_batch(32, N, M, 128, seed=0)
+    l, gx, gy = check_against_oracle(O, S, x, y, gamma, pairs=[0, 31], low_memory=True,
+                                     what=f"low-memory {N}x{M} g={gamma}")
+    s = gx.sum(axis=1) + gy.sum(axis=1)
+    scale = np.abs(gx).sum(axis=1) + np.abs(gy).sum(axis=1) + 1e-30
+    assert (np.abs(s) <= 1e-4 * scale).all()
+
+
 def test_barycenter_iterates(O, S):
     """10 block waves (100, 3), Adam lr 0.1, 100 iterations, gamma=1.  Both
     runs start from the same fp32 pointwise mean (computed on the CPU).  The
@@ -247,7 +260,11 @@ def test_fused_auto_select(S):
     it; a problem whose unfused workspace exceeds the free memory does."""
     assert S.choose_fused(None, 2, 50, 40, 3, DEV) is False
     assert S.choose_fused("auto", 2, 10, 10, 300, DEV) is False
-    assert S.choose_fused(None, 32, 16384, 16384, 128, DEV) is True
+    # unfused would take more than half the free memory: low-memory unfused
+    # where that fits, else fused
+    assert S.choose_mode(None, 32, 16384, 16384, 128, DEV) == 4
+    assert S.choose_mode(None, 32, 20000, 20000, 128, DEV) == 1
+    assert S.choose_fused(None, 32, 20000, 20000, 128, DEV) is True
     x, y = pair_batch(2, 50, 40, 3, seed=4)
     xd = x.to(DEV).requires_grad_(True)
     la = S.SoftDTW(gamma=0.5, fused="auto")(xd, y.to(DEV))
@@ -480,6 +497,77 @@ def test_abi_backward_repeatable(S):
     for a, b in zip(outs[0], outs[1]):
         torch.testing.assert_close(a, b, rtol=0, atol=0)
     assert torch.isfinite(outs[0][2]).all()
+
+
+def _unfused_step(L, x, y, gamma, mode, want_e=True, backwards=1):
+    """Unfused (mode 0) or low-memory unfused (mode 4) forward + backward(s)
+    through the C ABI; returns the workspace size, loss and a list of (dx,
+    dy, E) per backward."""
+    B, N, D = x.shape
+    M = y.shape[1]
+    nb = L.sdtw_workspace_bytes(B, N, M, D, mode)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    loss = torch.empty(B, device=DEV)
+    gl = torch.full((B,), 0.5, device=DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    L.check(L.sdtw_forward(x.data_ptr(), y.data_ptr(), B, N, M, D, gamma, mode, ws.data_ptr(),
+                           nb, loss.data_ptr(), s), "sdtw_forward")
+    outs = []
+    for _ in range(backwards):
+        gx, gy = torch.empty_like(x), torch.empty_like(y)
+        E = torch.empty(B, N, M, device=DEV) if want_e else None
+        L.check(L.sdtw_backward(x.data_ptr(), y.data_ptr(), B, N, M, D, gamma, mode,
+                                ws.data_ptr(), nb, gl.data_ptr(), gx.data_ptr(), gy.data_ptr(),
+                                E.data_ptr() if want_e else None, s), "sdtw_backward")
+        outs.append((gx, gy, E))
+    assert L.sdtw_workspace_status(ws.data_ptr(), nb, B, N, M, D, mode, s) == L.SDTW_OK
+    torch.cuda.synchronize()
+    return nb, loss, outs
+
+
+@pytest.mark.parametrize("B,N,M,D,gamma", [(3, 70, 45, 3, 1.0), (2, 300, 700, 5, 0.3),
+                                           (3, 1100, 700, 5, 1.0), (2, 129, 600, 100, 0.1),
+                                           (4, 512, 512, 64, 1.0)])
+def test_low_memory_mode_matches_unfused(S, B, N, M, D, gamma):
+    """The low-memory unfused mode (sweeps one after the other, the reverse
+    sweep forming E over the distances in the backward) gives bitwise the
+    loss, E and dx of the unfused mode, in a smaller workspace; dy too where
+    both take the column pass (D > 64 or E requested), to rounding where the
+    unfused mode sums the bands' shares instead.  A repeated backward reuses
+    E."""
+    from differentiable_series_alignment_amd import _lib as L
+    x, y = (t.to(DEV) for t in pair_batch(B, N, M, D, seed=B + N + M))
+    print(f"low-memory mode: {B}x{N}x{M}x{D}", flush=True)
+    n1, l1, o1 = _unfused_step(L, x, y, gamma, 0)
+    n2, l2, o2 = _unfused_step(L, x, y, gamma, 4, backwards=2)
+    assert n2 < n1
+    torch.testing.assert_close(l2, l1, rtol=0, atol=0)
+    for gx, gy, E in o2:
+        torch.testing.assert_close(E, o1[0][2], rtol=0, atol=0)
+        torch.testing.assert_close(gx, o1[0][0], rtol=0, atol=0)
+        torch.testing.assert_close(gy, o1[0][1], rtol=0, atol=0)   # E requested: column pass
+    # without E the unfused mode takes the dy shares (D <= 64)
+    _, _, o3 = _unfused_step(L, x, y, gamma, 0, want_e=False)
+    _, _, o4 = _unfused_step(L, x, y, gamma, 4, want_e=False, backwards=2)
+    for gx, gy, _ in o4:
+        torch.testing.assert_close(gx, o3[0][0], rtol=0, atol=0)
+        torch.testing.assert_close(gy, o3[0][1], rtol=1e-4, atol=1e-6)
+
+
+def test_low_memory_mode_launch_order(S):
+    """Low-memory unfused: the forward call launches the distances and the
+    forward sweep, the backward call the E-forming reverse sweep and the
+    chain rule (row pass reading E, column pass)."""
+    from differentiable_series_alignment_amd import _lib as L
+    x, y = (t.to(DEV) for t in pair_batch(2, 100, 90, 8, seed=12))
+    L.sdtw_timing(True)
+    try:
+        _unfused_step(L, x, y, 1.0, 4, want_e=False)
+        recs = L.sdtw_timing_collect()
+    finally:
+        L.sdtw_timing(False)
+    names = [n for n, _ in recs]
+    assert names == ["dist_skew", "dp_forward", "dp_reverse_e", "chain_rows", "chain_cols"], names
 
 
 def test_unfused_gradient_paths_agree(S):
