@@ -63,8 +63,8 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_dp_common.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h"],
-    "sha256": "4a268bf7f9759586c351cb1e310480d991145ee424cfebf27a406d09b1bef452",
-    "fetch_kib": 37593, "fetch_scale": 2.0,
+    "sha256": "e2f872bbece3feccd13ae04c825bb7a6bd98aa89f44205ded4848e75d223d37c",
+    "fetch_kib": 37599, "fetch_scale": 2.0,
     "write_kib": 148109, "write_scale": 1.0,
 }
 
