@@ -146,8 +146,11 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   const int bpw = mode == SDTW_MODE_FUSED ? sdtw::fused_bands_per_wg(D) : sdtw::kBandsPerWG;
   if (bpw == 0) return false;  // fused mode: D beyond what the kernels hold on chip
   L->nseg = (L->nbands + bpw - 1) / bpw;
-  L->S = sdtw::skew_steps(M);
-  const size_t cells = (size_t)B * (size_t)L->nbands * (size_t)L->S * 64;
+  // Band stride of the unfused arrays (see band_stride); the fused sweeps'
+  // lanes address R with their own offsets and keep the padded stride.
+  const bool unfused = mode == SDTW_MODE_UNFUSED || mode == SDTW_MODE_UNFUSED_LOWMEM;
+  L->S = unfused ? sdtw::band_stride(N, M) : sdtw::skew_steps(M);
+  const size_t cells = (size_t)sdtw::band_array_elems(B * L->nbands, L->S, M);
   size_t off = 0;
   L->ctrl = off;
   // DP words (two halves of ticket, done, progress), then the counters of
@@ -164,7 +167,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   off += align_up(2 * (size_t)B * (size_t)L->nseg * (size_t)M * 8);
   L->R = off;
   off += align_up(cells * 8);
-  if (mode == SDTW_MODE_UNFUSED || mode == SDTW_MODE_UNFUSED_LOWMEM) {
+  if (unfused) {
     // Low-memory unfused: the sweeps one after the other, the reverse one
     // forming E over the distances, so T' is never stored.
     L->seq = mode == SDTW_MODE_UNFUSED_LOWMEM;
@@ -173,9 +176,11 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
       off += align_up(cells * 8);
     }
     L->part = off;
-    off += align_up(sdtw::chain_part_floats(B, N, M, D, L->S) * 4);
+    off += align_up(sdtw::chain_part_floats(B, N, M, D) * 4);
+    // Distances, then E or the row pass's dy shares.
+    const size_t shares = sdtw::chain_share_floats(B, N, M, D);
     L->dist = off;
-    off += align_up(cells * 4);
+    off += align_up((cells > shares ? cells : shares) * 4);
   }
   L->total = off;
   return true;

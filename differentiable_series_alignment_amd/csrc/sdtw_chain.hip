@@ -68,8 +68,10 @@ struct Stage32 {
 // E = 2^(Xnm - X - T') for each cell, written both to the LDS ring and to
 // the band-step E array (the distance array, no longer needed) for the
 // column pass and the optional alignment output.  Cells outside the grid
-// (rows from rows_left on, columns outside 0..M-1) are stored as 0, so the
-// products and sums over the ring need no masks.
+// (rows from rows_left on, columns outside 0..M-1) go to the ring as 0, so
+// the products and sums over the ring need no masks; the E array receives
+// only the grid's columns (a window's steps past a band's cells reach the
+// next band's cells).
 typedef double v2d __attribute__((ext_vector_type(2)));
 struct StageXT {
   double xv[8], tv[8];
@@ -113,7 +115,17 @@ struct StageXT {
 #pragma unroll
         for (int j = 0; j < 4; ++j) ring[(slot + kRingSteps) * kRingPitch + (e & 63) + j] = q[j];
       }
-      if (EOUT) __builtin_nontemporal_store(q, reinterpret_cast<v4f*>(ebp + off[k]));
+      if (EOUT) {
+        // Columns col0 - 3 .. col0 of the four lanes; whole when all are in
+        // the grid (the steps inside a band's ramps are stored word by word).
+        if (col0 - 3 >= 0 && col0 < M) {
+          __builtin_nontemporal_store(q, reinterpret_cast<v4f*>(ebp + off[k]));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (col0 - j >= 0 && col0 - j < M) ebp[off[k] + j] = q[j];
+        }
+      }
     }
   }
 };
@@ -243,7 +255,7 @@ __global__ __launch_bounds__(256) void k_chain_rows(float* __restrict__ esk,
   const double* xbp = R + boff;
   const double* tbp = R2 + boff;
   const double xnm = FORM ? loss64[b] : 0.0;
-  const int64_t smax = S - kSkewOff;
+  const int64_t smax = skew_steps(M) - kSkewOff;   // reads stay in the array
   const float* yb = y + b * M * D;
   int64_t dcol[NTW];
 #pragma unroll
@@ -433,7 +445,7 @@ __global__ __launch_bounds__(256) void k_chain_cols(const float* __restrict__ es
   const int ct = w & 1, dsel = w >> 1;
   const int jl = 32 * ct + r;
   const bool col_ok = j0 + jl < M;
-  const int64_t smax = S - kSkewOff;
+  const int64_t smax = skew_steps(M) - kSkewOff;   // reads stay in the array
   const float* xb = x + b * N * D;
   int64_t dcol[NTW];
 #pragma unroll
@@ -554,28 +566,32 @@ __global__ __launch_bounds__(256) void k_chain_gy(const float* __restrict__ P,
   }
 }
 
-// Whether the per-band shares of dy fit where the distances were.
-bool chain_gy_fits(int64_t M, int64_t D, int64_t S) {
-  return D <= 64 && M * gy_pitch(D) <= S * 64;
+// Whether the row pass makes the per-band shares of dy: D <= 64 (one d
+// tile), and the shares of a band take no more floats than a band of the
+// padded band-step layout (skew_steps(M) steps); beyond that (M > 3296) E
+// is stored and read back by the column pass.
+static bool chain_gy_path(int64_t M, int64_t D) {
+  return D <= 64 && M * gy_pitch(D) <= skew_steps(M) * 64;
+}
+
+size_t chain_share_floats(int64_t B, int64_t N, int64_t M, int64_t D) {
+  return chain_gy_path(M, D) ? (size_t)(B * ((N + 63) / 64) * M * gy_pitch(D)) : 0;
 }
 
 // Row-pass splits when it makes the dy shares.  Every part first loads a
 // 96-step window, so short parts mostly load: the parts fill the GPU with
 // one workgroup per CU keeping at least two column blocks each, or with two
-// per CU keeping at least four, whichever splits more; and only as far as
-// their partial sums fit in the distance region after the shares.
+// per CU keeping at least four, whichever splits more.
 // Measured: 32x256x256 31 us with two parts per band against 34 with four;
 // 10x100x100 18 us with two against 22 unsplit; 32x1024x1024 194 us
 // unsplit against 213 with two; 32x512x512 the same with two to four.
-int chain_splits_rows_gy(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S) {
+static int chain_splits_rows_gy(int64_t B, int64_t N, int64_t M) {
   const int64_t nb = (N + 63) / 64, groups = B * nb, nblk = (M + 31) / 32;
   int64_t p1 = (256 + groups - 1) / groups, p2 = (512 + groups - 1) / groups;
   p1 = p1 < nblk / 2 ? p1 : nblk / 2;
   p2 = p2 < nblk / 4 ? p2 : nblk / 4;
   int64_t p = p1 > p2 ? p1 : p2;
   p = p < 1 ? 1 : (p > 8 ? 8 : p);
-  const int64_t room = groups * (S * 64 - M * gy_pitch(D));
-  while (p > 1 && groups * p * 17 * 256 > room) --p;
   return (int)p;
 }
 
@@ -587,8 +603,8 @@ int chain_splits_rows_gy(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S) 
 // splits as the share path does whether or not E is requested, so dx is
 // summed in the same order either way.
 constexpr int64_t kChainFill = 256;
-int chain_splits_rows(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S) {
-  if (chain_gy_fits(M, D, S)) return chain_splits_rows_gy(B, N, M, D, S);
+int chain_splits_rows(int64_t B, int64_t N, int64_t M, int64_t D) {
+  if (chain_gy_path(M, D)) return chain_splits_rows_gy(B, N, M);
   const int64_t groups = B * ((N + 63) / 64), nblk = (M + 31) / 32;
   int64_t p = (kChainFill + groups - 1) / groups;
   p = p < nblk / 2 ? p : nblk / 2;
@@ -600,11 +616,14 @@ int chain_splits_cols(int64_t B, int64_t N, int64_t M) {
   p = p < nb / 2 ? p : nb / 2;
   return (int)(p < 1 ? 1 : (p > 8 ? 8 : p));
 }
-size_t chain_part_floats(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S) {
-  const int64_t pr = chain_splits_rows(B, N, M, D, S), pc = chain_splits_cols(B, N, M);
+// Each split part holds 16 * NTW + 1 rows of 256 floats; NTW = 2 only where
+// a D slice is wider than 64.
+size_t chain_part_floats(int64_t B, int64_t N, int64_t M, int64_t D) {
+  const int64_t pr = chain_splits_rows(B, N, M, D), pc = chain_splits_cols(B, N, M);
   const int64_t rows = pr > 1 ? B * ((N + 63) / 64) * pr : 0;
   const int64_t cols = pc > 1 ? B * ((M + 63) / 64) * pc : 0;
-  return (size_t)(rows > cols ? rows : cols) * 33 * 256;
+  const int64_t k = D > 64 ? 33 : 17;
+  return (size_t)(rows > cols ? rows : cols) * k * 256;
 }
 
 template <int NTW, bool FORM, bool GYP = false>
@@ -629,16 +648,13 @@ hipError_t launch_chain(float* esk, const double* R, const double* R2,
                         int64_t M, int64_t D, int64_t S, float* part, unsigned* cnt_rows,
                         unsigned* cnt_cols, bool keep_e, bool e_ready, hipStream_t s) {
   const int nb = (int)((N + 63) / 64);
-  const unsigned pr = (unsigned)chain_splits_rows(B, N, M, D, S);
+  const unsigned pr = (unsigned)chain_splits_rows(B, N, M, D);
   const unsigned pc = (unsigned)chain_splits_cols(B, N, M);
-  if (gy && !keep_e && !e_ready && chain_gy_fits(M, D, S)) {
+  if (gy && !keep_e && !e_ready && chain_gy_path(M, D)) {
     // One row pass makes dx and the bands' shares of dy (in place of E);
-    // a short pass adds the shares up.  Its split partial sums go after the
-    // shares.
-    const unsigned pg = (unsigned)chain_splits_rows_gy(B, N, M, D, S);
-    float* gpart = esk + B * nb * M * gy_pitch(D);
-    launch_rows<1, true, true>(B, pg, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, 0,
-                               gpart, cnt_rows);
+    // a short pass adds the shares up.
+    launch_rows<1, true, true>(B, pr, s, esk, R, R2, loss64, x, y, gl, gx, N, M, D, S, nb, 0,
+                               part, cnt_rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TimedLaunch timed_("chain_gy", s);

@@ -14,8 +14,21 @@ namespace sdtw {
 //     index(b, r, c) = ((b * nbands + r / 64) * S + (c + l + kSkewOff)) * 64 + l
 // so the 64 cells one wavefront step touches (lane l at column t - l) are 64
 // consecutive elements.  The reverse sweep, whose lanes walk columns from the
-// right, reads the same steps with its lanes in reverse order.  S leaves room
-// for every step either sweep touches, padding included.
+// right, reads the same steps with its lanes in reverse order.
+//
+// S is the distance between consecutive bands.  The sweeps store at every
+// step they run, columns outside the grid included, so no such store may
+// land on another band's cell.  A band's cells occupy its steps
+// [kSkewOff, kSkewOff + M + 63).  With N a multiple of 64 the reverse
+// sweep's lanes map onto the rows of one band in reverse order, and each
+// sweep touches that range widened by p = sweep_steps(M) - M - 63 < 16
+// steps on either side; with S = sweep_steps(M) the widening falls on steps
+// that hold no cell of the neighbouring band.  Otherwise a reverse band
+// straddles two bands of storage and its lanes reach up to 126 steps past a
+// row's first cell: S = skew_steps(M).  Kernels other than the sweeps store
+// only cells.  The array holds band_array_elems(G, S, M) elements for G
+// bands (the last band's frame extends over skew_steps(M) steps, room for
+// any reader that clamps its steps below that).
 // ---------------------------------------------------------------------------
 constexpr int64_t kSkewOff = 80;
 
@@ -30,6 +43,12 @@ __host__ __device__ inline int64_t skew_index(int64_t b, int64_t r, int64_t c,
 // Steps a sweep runs per band: columns 0..M-1 for lanes 0..63, in chunks of 16.
 __host__ __device__ inline int64_t sweep_steps(int64_t M) {
   return ((M + 63 + 15) / 16) * 16;
+}
+__host__ __device__ inline int64_t band_stride(int64_t N, int64_t M) {
+  return N % 64 == 0 ? sweep_steps(M) : skew_steps(M);
+}
+__host__ __device__ inline int64_t band_array_elems(int64_t G, int64_t S, int64_t M) {
+  return ((G - 1) * S + skew_steps(M)) * 64;
 }
 
 // Marker of a hand-off entry not written yet: a signalling-NaN pattern,
@@ -165,15 +184,18 @@ hipError_t launch_fill_u32(unsigned* p, int64_t n, unsigned v, hipStream_t s);
 // from R and R2 into `esk` (the distance array, no longer needed) and, if
 // gx is given, writes dx; the column pass reads E from `esk` and writes dy.
 // With D <= 64 and E not wanted afterwards (keep_e false) the row pass
-// writes the bands' shares of dy into `esk` instead and a short pass adds
-// them up.  e_ready: E is already in `esk` (formed by the reverse sweep);
-// every pass reads it and R, R2 are not used.
+// writes the bands' shares of dy into `esk` instead (chain_share_floats()
+// floats, which `esk` must hold) and a short pass adds them up.  e_ready: E
+// is already in `esk` (formed by the reverse sweep); every pass reads it and
+// R, R2 are not used.  The arrays use the unfused band-step layout (band
+// stride S = M).
 // Small problems split each sum over several workgroups: `part` holds
 // chain_part_floats() floats of partial sums and the counters (B*nbands for
 // the rows, B*ceil(M/64) for the columns) start at zero and are left at zero.
-int chain_splits_rows(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S);
+int chain_splits_rows(int64_t B, int64_t N, int64_t M, int64_t D);
 int chain_splits_cols(int64_t B, int64_t N, int64_t M);
-size_t chain_part_floats(int64_t B, int64_t N, int64_t M, int64_t D, int64_t S);
+size_t chain_part_floats(int64_t B, int64_t N, int64_t M, int64_t D);
+size_t chain_share_floats(int64_t B, int64_t N, int64_t M, int64_t D);
 hipError_t launch_chain(float* esk, const double* R, const double* R2,
                         const double* loss64, const float* x, const float* y,
                         const float* gl, float* gx, float* gy, int64_t B, int64_t N,

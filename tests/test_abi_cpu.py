@@ -278,6 +278,24 @@ def test_low_memory_unfused_workspace():
     assert L.sdtw_workspace_bytes(1, 4, 4, 1, 5) == 0
 
 
+def test_unfused_band_stride():
+    """The unfused arrays' bands are M + 63 steps apart (rounded up to 16)
+    when N is a multiple of 64, and M + 206 (rounded) apart otherwise, where
+    the reverse sweep's bands straddle two bands of storage: two fp64 and one
+    fp32 array of ((bands - 1) * stride + skew) * 64 elements (the last band
+    spans the padded extent either way), each region rounded to 256 bytes."""
+    def ws(N, M, mode=L.SDTW_MODE_UNFUSED):
+        return L.sdtw_workspace_bytes(4, N, M, 8, mode)
+    for M in (1, 16, 17, 100, 513):
+        tight, padded = ws(128, M), ws(127, M)
+        steps = ((M + 221) // 16) * 16 - ((M + 78) // 16) * 16
+        assert abs(padded - tight - (4 * 2 - 1) * steps * 64 * 20) <= 3 * 256, M
+    # the headline workload: B=32, N=M=512, D=64 (576-step bands)
+    head = L.sdtw_workspace_bytes(32, 512, 512, 64, L.SDTW_MODE_UNFUSED)
+    assert head < 190 << 20, head / 2**20
+    assert L.sdtw_workspace_bytes(32, 512, 512, 64, L.SDTW_MODE_UNFUSED_LOWMEM) < 118 << 20
+
+
 def test_static_forward_validation_on_host():
     """sdtw_forward_static rejects null pointers, bad sizes and problems whose
     inference workspace exceeds its device array before any HIP call."""

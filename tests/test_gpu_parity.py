@@ -554,6 +554,35 @@ def test_low_memory_mode_matches_unfused(S, B, N, M, D, gamma):
         torch.testing.assert_close(gy, o3[0][1], rtol=1e-4, atol=1e-6)
 
 
+@pytest.mark.parametrize("N", [64, 192])
+@pytest.mark.parametrize("M", [1, 2, 15, 16, 17, 33, 49, 63, 64, 65, 80, 81, 97])
+def test_band_stride_edges_against_oracle(O, S, N, M):
+    """With N a multiple of 64 the unfused arrays' bands lie sweep_steps(M)
+    apart (M + 63 rounded up to 16), so the steps a sweep runs outside the
+    grid's columns sit next to the neighbouring band's cells; M over every
+    rounding residue checks that neither sweep, the E-forming reverse sweep
+    nor the chain rule's E store writes over them.  Both unfused modes, E
+    requested or not, against the oracle (loss, dx, dy, E)."""
+    from differentiable_series_alignment_amd import _lib as L
+    B, D, gamma = 3, 3, 0.5
+    x, y = pair_batch(B, N, M, D, seed=N + M)
+    l0, gx0, gy0, E0 = O.value_and_grad(x.numpy(), y.numpy(), gamma, np.full(B, 0.5),
+                                        round_dist_f32=True, want_E=True)
+    xd, yd = x.to(DEV), y.to(DEV)
+    for mode in (L.SDTW_MODE_UNFUSED, L.SDTW_MODE_UNFUSED_LOWMEM):
+        for want_e in (True, False):
+            what = f"{B}x{N}x{M} mode {mode} E={want_e}"
+            print(what, flush=True)
+            _, loss, outs = _unfused_step(L, xd, yd, gamma, mode, want_e=want_e)
+            gx, gy, E = outs[0]
+            assert_loss(loss.cpu().double().numpy(), l0, what)
+            assert_grad(gx.cpu().double().numpy(), gx0, what + " dx")
+            assert_grad(gy.cpu().double().numpy(), gy0, what + " dy")
+            if want_e:
+                np.testing.assert_allclose(E.cpu().double().numpy(), E0, rtol=1e-4, atol=1e-6,
+                                           err_msg=what + " E")
+
+
 def test_low_memory_mode_launch_order(S):
     """Low-memory unfused: the forward call launches the distances and the
     forward sweep, the backward call the E-forming reverse sweep and the
