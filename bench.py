@@ -62,9 +62,10 @@ TRAFFIC_RECORD = {
     "sources": ["differentiable_series_alignment_amd/csrc/sdtw_dp.hip",
                 "differentiable_series_alignment_amd/csrc/sdtw_dp_common.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
-                "differentiable_series_alignment_amd/csrc/sdtw_kernels.h"],
-    "sha256": "e2f872bbece3feccd13ae04c825bb7a6bd98aa89f44205ded4848e75d223d37c",
-    "fetch_kib": 37599, "fetch_scale": 2.0,
+                "differentiable_series_alignment_amd/csrc/sdtw_kernels.h",
+                "differentiable_series_alignment_amd/csrc/sdtw_api.hip"],
+    "sha256": "3c9f14f640c46accf0456f0971a990b837c1d51f73635fe5ffa360dd3a10a9cd",
+    "fetch_kib": 37593, "fetch_scale": 2.0,
     "write_kib": 148109, "write_scale": 1.0,
 }
 
