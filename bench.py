@@ -64,8 +64,8 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_api.hip"],
-    "sha256": "3c9f14f640c46accf0456f0971a990b837c1d51f73635fe5ffa360dd3a10a9cd",
-    "fetch_kib": 37593, "fetch_scale": 2.0,
+    "sha256": "f792a8a4548735bd1df870ad8423f2e8cec9708379b11998a9f40bde608f5386",
+    "fetch_kib": 37595, "fetch_scale": 2.0,
     "write_kib": 148109, "write_scale": 1.0,
 }
 

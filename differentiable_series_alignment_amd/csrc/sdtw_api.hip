@@ -149,7 +149,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   // Band stride of the unfused arrays (see band_stride); the fused sweeps'
   // lanes address R with their own offsets and keep the padded stride.
   const bool unfused = mode == SDTW_MODE_UNFUSED || mode == SDTW_MODE_UNFUSED_LOWMEM;
-  L->S = unfused ? sdtw::band_stride(N, M) : sdtw::skew_steps(M);
+  L->S = unfused ? sdtw::band_stride(M) : sdtw::skew_steps(M);
   const size_t cells = (size_t)sdtw::band_array_elems(B * L->nbands, L->S, M);
   size_t off = 0;
   L->ctrl = off;

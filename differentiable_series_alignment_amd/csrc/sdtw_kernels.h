@@ -18,17 +18,20 @@ namespace sdtw {
 //
 // S is the distance between consecutive bands.  The sweeps store at every
 // step they run, columns outside the grid included, so no such store may
-// land on another band's cell.  A band's cells occupy its steps
-// [kSkewOff, kSkewOff + M + 63).  With N a multiple of 64 the reverse
-// sweep's lanes map onto the rows of one band in reverse order, and each
-// sweep touches that range widened by p = sweep_steps(M) - M - 63 < 16
-// steps on either side; with S = sweep_steps(M) the widening falls on steps
-// that hold no cell of the neighbouring band.  Otherwise a reverse band
-// straddles two bands of storage and its lanes reach up to 126 steps past a
-// row's first cell: S = skew_steps(M).  Kernels other than the sweeps store
-// only cells.  The array holds band_array_elems(G, S, M) elements for G
-// bands (the last band's frame extends over skew_steps(M) steps, room for
-// any reader that clamps its steps below that).
+// land on a cell of another band.  The cells at lane position l (the index
+// mod 64) are one row's, at steps kSkewOff + l .. kSkewOff + l + M - 1 of
+// their band, and a store at position l can only meet those.  A sweep lane
+// working on the row at position l touches steps kSkewOff + [0, T) of the
+// row's band (forward) or kSkewOff + l + j + M - 1 - [0, T) (reverse; j <=
+// 63 is its lane in the reverse band), T = sweep_steps(M) >= M + 63.  With
+// the unfused stride S = T both ranges lie after the previous band's last
+// cell at that position (step kSkewOff + l + M - 1 - S) and before the next
+// band's first (kSkewOff + l + S), for any N.  Kernels other than the
+// sweeps store only cells.  The array holds band_array_elems(G, S, M)
+// elements for G bands: the last band's frame extends over skew_steps(M)
+// steps, room for every sweep access and for readers that clamp their steps
+// below that.  The fused R array keeps S = skew_steps(M), whose sweeps
+// address it with their own offsets.
 // ---------------------------------------------------------------------------
 constexpr int64_t kSkewOff = 80;
 
@@ -44,9 +47,7 @@ __host__ __device__ inline int64_t skew_index(int64_t b, int64_t r, int64_t c,
 __host__ __device__ inline int64_t sweep_steps(int64_t M) {
   return ((M + 63 + 15) / 16) * 16;
 }
-__host__ __device__ inline int64_t band_stride(int64_t N, int64_t M) {
-  return N % 64 == 0 ? sweep_steps(M) : skew_steps(M);
-}
+__host__ __device__ inline int64_t band_stride(int64_t M) { return sweep_steps(M); }
 __host__ __device__ inline int64_t band_array_elems(int64_t G, int64_t S, int64_t M) {
   return ((G - 1) * S + skew_steps(M)) * 64;
 }

@@ -279,17 +279,23 @@ def test_low_memory_unfused_workspace():
 
 
 def test_unfused_band_stride():
-    """The unfused arrays' bands are M + 63 steps apart (rounded up to 16)
-    when N is a multiple of 64, and M + 206 (rounded) apart otherwise, where
-    the reverse sweep's bands straddle two bands of storage: two fp64 and one
-    fp32 array of ((bands - 1) * stride + skew) * 64 elements (the last band
-    spans the padded extent either way), each region rounded to 256 bytes."""
-    def ws(N, M, mode=L.SDTW_MODE_UNFUSED):
-        return L.sdtw_workspace_bytes(4, N, M, 8, mode)
-    for M in (1, 16, 17, 100, 513):
-        tight, padded = ws(128, M), ws(127, M)
-        steps = ((M + 221) // 16) * 16 - ((M + 78) // 16) * 16
-        assert abs(padded - tight - (4 * 2 - 1) * steps * 64 * 20) <= 3 * 256, M
+    """The unfused arrays' bands are sweep_steps(M) = M + 63 rounded up to 16
+    steps apart for any N (the steps a sweep runs outside the grid's columns
+    reach no other band's cell), and the last band spans skew_steps(M) =
+    M + 206 rounded: the reverse-state array, the one region the low-memory
+    mode leaves out, holds ((bands - 1) * stride + skew) * 64 doubles."""
+    def ws(B, N, M, mode):
+        return L.sdtw_workspace_bytes(B, N, M, 8, mode)
+    for B, N, M in [(4, 128, 1), (4, 127, 16), (3, 65, 17), (2, 1000, 100), (4, 64, 513),
+                    (1, 1, 1), (2, 333, 1024)]:
+        G = B * ((N + 63) // 64)
+        stride = ((M + 78) // 16) * 16
+        skew = ((M + 221) // 16) * 16
+        t_bytes = ((G - 1) * stride + skew) * 64 * 8
+        diff = ws(B, N, M, L.SDTW_MODE_UNFUSED) - ws(B, N, M, L.SDTW_MODE_UNFUSED_LOWMEM)
+        assert diff == (t_bytes + 255) // 256 * 256, (B, N, M, diff, t_bytes)
+    # ragged N costs nothing beyond its bands
+    assert ws(4, 127, 100, 0) == ws(4, 128, 100, 0) == ws(4, 65, 100, 0)
     # the headline workload: B=32, N=M=512, D=64 (576-step bands)
     head = L.sdtw_workspace_bytes(32, 512, 512, 64, L.SDTW_MODE_UNFUSED)
     assert head < 190 << 20, head / 2**20

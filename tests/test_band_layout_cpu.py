@@ -5,8 +5,8 @@ the grid included, so the band stride S of the arrays they write must keep
 those stores off every other band's cells.  This model takes the cursor
 formulas of the sweeps (forward: lane l of band k at step t holds cell
 (64k + l, t - l); reverse: sweep row i is grid row N-1-i, the lane walks the
-columns from the right) and the stride rule of the layout (sweep_steps(M)
-when N is a multiple of 64, skew_steps(M) otherwise), and checks for every
+columns from the right) and the stride of the layout (sweep_steps(M), M + 63
+rounded up to 16, for any N), and checks for every
 lane of every band of both sweeps that a store inside the grid's columns
 lands on its own cell, a store outside them on no cell at all, and every
 access stays inside the array (the last band's frame spans skew_steps(M)
@@ -27,7 +27,7 @@ def sweep_steps(M):
 
 
 def band_stride(N, M):
-    return sweep_steps(M) if N % 64 == 0 else skew_steps(M)
+    return sweep_steps(M)
 
 
 def check_layout(B, N, M):
@@ -72,7 +72,9 @@ def check_layout(B, N, M):
                                    (3, 64, 64), (2, 65, 15), (2, 63, 100), (1, 128, 16),
                                    (2, 128, 47), (3, 200, 33), (2, 191, 300), (1, 70, 45),
                                    (2, 128, 1100), (1, 320, 200), (2, 192, 511),
-                                   (2, 64, 513), (1, 256, 1000)])
+                                   (2, 64, 513), (1, 256, 1000), (2, 127, 17), (2, 129, 64),
+                                   (1, 97, 80), (2, 190, 79), (2, 255, 47), (1, 1000, 100),
+                                   (2, 33, 513)])
 def test_sweep_stores_stay_off_other_cells(B, N, M):
     check_layout(B, N, M)
 
@@ -84,7 +86,8 @@ def test_model_catches_a_too_small_stride():
     keep = band_stride
     try:
         band_stride = lambda N, M: keep(N, M) - 16
-        with pytest.raises(AssertionError):
-            check_layout(2, 128, 100)
+        for shape in [(2, 128, 100), (2, 100, 100)]:
+            with pytest.raises(AssertionError):
+                check_layout(*shape)
     finally:
         band_stride = keep

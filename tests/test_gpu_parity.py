@@ -554,15 +554,16 @@ def test_low_memory_mode_matches_unfused(S, B, N, M, D, gamma):
         torch.testing.assert_close(gy, o3[0][1], rtol=1e-4, atol=1e-6)
 
 
-@pytest.mark.parametrize("N", [64, 192])
+@pytest.mark.parametrize("N", [64, 127, 192])
 @pytest.mark.parametrize("M", [1, 2, 15, 16, 17, 33, 49, 63, 64, 65, 80, 81, 97])
 def test_band_stride_edges_against_oracle(O, S, N, M):
-    """With N a multiple of 64 the unfused arrays' bands lie sweep_steps(M)
-    apart (M + 63 rounded up to 16), so the steps a sweep runs outside the
-    grid's columns sit next to the neighbouring band's cells; M over every
-    rounding residue checks that neither sweep, the E-forming reverse sweep
-    nor the chain rule's E store writes over them.  Both unfused modes, E
-    requested or not, against the oracle (loss, dx, dy, E)."""
+    """The unfused arrays' bands lie sweep_steps(M) apart (M + 63 rounded up
+    to 16), so the steps a sweep runs outside the grid's columns sit next to
+    the neighbouring band's cells; M over every rounding residue, N whole and
+    ragged (the reverse sweep's bands then straddle two bands of storage),
+    checks that neither sweep, the E-forming reverse sweep nor the chain
+    rule's E store writes over them.  Both unfused modes, E requested or
+    not, against the oracle (loss, dx, dy, E)."""
     from differentiable_series_alignment_amd import _lib as L
     B, D, gamma = 3, 3, 0.5
     x, y = pair_batch(B, N, M, D, seed=N + M)
