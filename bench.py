@@ -64,8 +64,8 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_api.hip"],
-    "sha256": "f792a8a4548735bd1df870ad8423f2e8cec9708379b11998a9f40bde608f5386",
-    "fetch_kib": 37595, "fetch_scale": 2.0,
+    "sha256": "17b88bf6d13b43d0dafe1e1bff54829ae7a2e076f0ed956663e8129708101d82",
+    "fetch_kib": 37593, "fetch_scale": 2.0,
     "write_kib": 148109, "write_scale": 1.0,
 }
 

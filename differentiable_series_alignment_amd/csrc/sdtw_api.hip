@@ -100,7 +100,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
     if (sdtw::fused_bands_per_wg(D) == 0) return false;
     L->nseg = L->nbands;
     L->hcols = infer_ring_cols(B, L->nbands, M, N, D);
-    L->S = sdtw::skew_steps(M);
+    L->S = sdtw::band_stride(M);
     L->G = ckpt_group(L->nbands);
     L->ng = (L->nbands + L->G - 1) / L->G;
     const size_t row = L->hcols ? L->hcols : (size_t)M;
@@ -121,7 +121,7 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
     L->rh = off;
     off += align_up(2 * (size_t)B * (size_t)M * 8);
     L->R = off;
-    off += align_up((size_t)B * (size_t)L->G * (size_t)L->S * 64 * 8);
+    off += align_up((size_t)sdtw::band_array_elems(B * L->G, L->S, M) * 8);
     L->total = off;
     return true;
   }
@@ -146,10 +146,8 @@ bool make_layout(int64_t B, int64_t N, int64_t M, int64_t D, int mode, Layout* L
   const int bpw = mode == SDTW_MODE_FUSED ? sdtw::fused_bands_per_wg(D) : sdtw::kBandsPerWG;
   if (bpw == 0) return false;  // fused mode: D beyond what the kernels hold on chip
   L->nseg = (L->nbands + bpw - 1) / bpw;
-  // Band stride of the unfused arrays (see band_stride); the fused sweeps'
-  // lanes address R with their own offsets and keep the padded stride.
   const bool unfused = mode == SDTW_MODE_UNFUSED || mode == SDTW_MODE_UNFUSED_LOWMEM;
-  L->S = unfused ? sdtw::band_stride(M) : sdtw::skew_steps(M);
+  L->S = sdtw::band_stride(M);
   const size_t cells = (size_t)sdtw::band_array_elems(B * L->nbands, L->S, M);
   size_t off = 0;
   L->ctrl = off;

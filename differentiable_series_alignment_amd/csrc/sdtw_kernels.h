@@ -24,14 +24,16 @@ namespace sdtw {
 // working on the row at position l touches steps kSkewOff + [0, T) of the
 // row's band (forward) or kSkewOff + l + j + M - 1 - [0, T) (reverse; j <=
 // 63 is its lane in the reverse band), T = sweep_steps(M) >= M + 63.  With
-// the unfused stride S = T both ranges lie after the previous band's last
-// cell at that position (step kSkewOff + l + M - 1 - S) and before the next
-// band's first (kSkewOff + l + S), for any N.  Kernels other than the
-// sweeps store only cells.  The array holds band_array_elems(G, S, M)
+// S = T (band_stride) both ranges lie after the previous band's last cell
+// at that position (step kSkewOff + l + M - 1 - S) and before the next
+// band's first (kSkewOff + l + S), for any N.  The fused kernels' R array
+// uses the same stride: only their forward sweep stores into it, with the
+// forward lanes' steps (a range launch's storage rows start at its first
+// sweep row), and their reverse sweep only loads.  Kernels other than the
+// sweeps store only cells.  An array holds band_array_elems(G, S, M)
 // elements for G bands: the last band's frame extends over skew_steps(M)
 // steps, room for every sweep access and for readers that clamp their steps
-// below that.  The fused R array keeps S = skew_steps(M), whose sweeps
-// address it with their own offsets.
+// below that.
 // ---------------------------------------------------------------------------
 constexpr int64_t kSkewOff = 80;
 
