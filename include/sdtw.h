@@ -26,7 +26,8 @@
  *                      the chain rule, using the distance region for E (or,
  *                      for D <= 64 without an alignment output, for each
  *                      64-row band's share of grad_y).  About 20 bytes of
- *                      workspace per cell.
+ *                      workspace per cell: 8 + 8 + 4 bytes for each of M + 63
+ *                      columns (rounded up to 16) of every row.
  *   SDTW_MODE_UNFUSED_LOWMEM the unfused computation with the sweeps one
  *                      after the other: the forward runs the forward sweep
  *                      and keeps its state; the backward runs the reverse
@@ -64,7 +65,7 @@
  *                      sweep group by group of G bands from the bottom,
  *                      each after a forward sweep that recomputes the
  *                      group's states from the checkpoint row above it.
- *                      Workspace about B*(G*64*(M+222)*8 + N/(64G)*M*8)
+ *                      Workspace about B*(G*64*(M+78)*8 + N/(64G)*M*8)
  *                      bytes, plus the inference mode's hand-off rows (the
  *                      same CU condition applies to its forward).  Loss, alignment matrix and grad_x are
  *                      bitwise those of SDTW_MODE_FUSED (same arithmetic on
