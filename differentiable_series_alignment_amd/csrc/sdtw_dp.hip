@@ -216,9 +216,10 @@ __device__ __forceinline__ void band_sweep(const DPArgs& a, int b, int seg, int 
       double v = 0.0;
 #pragma unroll
       for (int u = 0; u < kCH; ++u) v = (u == ulast) ? bottom[u] : v;
-      if (lane == (int)(lastrow & 63)) {
-        a.loss64[b] = v;
-        a.loss[b] = (float)(v * a.g_ln2);
+      if (lane == (int)(lastrow & 63)) {   // device-coherent (see release_ctrl)
+        __hip_atomic_store(a.loss64 + b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.loss + b, (float)(v * a.g_ln2), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     // Next chunk's top entries, read after the count (see above), and ahead
@@ -325,7 +326,7 @@ __global__ __launch_bounds__((kBandsPerWG + 1) * 64) void k_dp_unfused(DPArgs a)
     else
       band_sweep<false>(a, b, seg, w, nb_seg, ring, wr, rd, lane);
   }
-  const bool last = release_ctrl(a.ctrl, 2 * per_sweep);
+  const bool last = release_ctrl(a.ctrl, 2 * per_sweep, true);
   if (last && eform && !s_skip && threadIdx.x == 0)
     __hip_atomic_store(a.eflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -200,9 +200,10 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
       double v = 0.0;
 #pragma unroll
       for (int u = 0; u < kCH; ++u) v = (u == ulast) ? bottom[u] : v;
-      if (lane == (int)(lastrow & 63)) {
-        a.loss64[b] = v;
-        a.loss[b] = (float)(v * a.g_ln2);
+      if (lane == (int)(lastrow & 63)) {   // device-coherent (see release_ctrl)
+        __hip_atomic_store(a.loss64 + b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.loss + b, (float)(v * a.g_ln2), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (top_ring && lane == 0) lds_publish(&sh.rd_in, umin_u((unsigned)t0 + kCH, Mu));
@@ -584,7 +585,9 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             const int64_t dc = dbeg + 32 * t + r32;
-            if (dc < dend) gxr[dc] = g2 * (rs * xs[(32 * rt + rowi) * P + dc] - gxa[rt][t][e]);
+            if (dc < dend)   // device-coherent (see release_ctrl)
+              __hip_atomic_store(gxr + dc, g2 * (rs * xs[(32 * rt + rowi) * P + dc] - gxa[rt][t][e]),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       }
@@ -677,7 +680,9 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
                     &sh.wr_in, &sh.rd_in, sh.ring_out, &sh.wr_out, &sh.rd_out,
                     (unsigned)a.M, lane, gr);
   }
-  release_ctrl(a.ctrl, (INFER && hcols ? 2 : 1) * (int64_t)a.B * a.nseg);
+  // The alignment-matrix output is written with ordinary stores.
+  release_ctrl(a.ctrl, (INFER && hcols ? 2 : 1) * (int64_t)a.B * a.nseg,
+               !(REV && a.align != nullptr));
 }
 
 template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC>
