@@ -64,9 +64,9 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_api.hip"],
-    "sha256": "17b88bf6d13b43d0dafe1e1bff54829ae7a2e076f0ed956663e8129708101d82",
-    "fetch_kib": 37593, "fetch_scale": 2.0,
-    "write_kib": 148109, "write_scale": 1.0,
+    "sha256": "86a29d2928e28e97c0f4dc6016b37f43f333fca1e1409a1ac430dba43fe994ba",
+    "fetch_kib": 37596, "fetch_scale": 2.0,
+    "write_kib": 148110, "write_scale": 1.0,
 }
 
 
