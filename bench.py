@@ -35,9 +35,10 @@ WORKLOAD = dict(B=32, N=512, M=512, D=64, gamma=1.0)
 # FMA as two), i.e. 39.3 T lane-operation slots/s.
 PEAK_ALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 # Algorithmic ALU work of one cell, forward and backward dynamic programme
-# together (the survey's per-cell estimate): about 13 transcendentals (exp,
-# log), each taking four issue slots at quarter rate, and about 45 other
-# operations, i.e. 97 lane-operation slots per cell.  At the headline
+# together, as the log-space formulation counts it (a logsumexp of three
+# terms per sweep and the final exponential of the alignment entry): about
+# 13 transcendentals (exp, log), each taking four issue slots at quarter
+# rate, and about 45 other operations, i.e. 97 lane-operation slots per cell.  At the headline
 # workload that is 20.7 us at PEAK_ALU_TOPS.
 TRANS_PER_CELL = 13
 OTHER_OPS_PER_CELL = 45
