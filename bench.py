@@ -65,8 +65,8 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_api.hip"],
-    "sha256": "86a29d2928e28e97c0f4dc6016b37f43f333fca1e1409a1ac430dba43fe994ba",
-    "fetch_kib": 37596, "fetch_scale": 2.0,
+    "sha256": "fb7a59b148e42eb3cc0b302646dacc0304a165d9e323327d326bbf4d953d8c1a",
+    "fetch_kib": 37604, "fetch_scale": 2.0,
     "write_kib": 148110, "write_scale": 1.0,
 }
 
