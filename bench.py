@@ -65,7 +65,7 @@ TRAFFIC_RECORD = {
                 "differentiable_series_alignment_amd/csrc/sdtw_device.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_kernels.h",
                 "differentiable_series_alignment_amd/csrc/sdtw_api.hip"],
-    "sha256": "fb7a59b148e42eb3cc0b302646dacc0304a165d9e323327d326bbf4d953d8c1a",
+    "sha256": "d97cd41000128c1cd8b38c93ca25d0d4c0a6aa5b749487fc9c628cc8deaf10e5",
     "fetch_kib": 37604, "fetch_scale": 2.0,
     "write_kib": 148110, "write_scale": 1.0,
 }

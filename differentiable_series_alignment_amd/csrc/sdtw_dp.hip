@@ -15,7 +15,7 @@
 //  - R[i-1,j] arrives from lane l-1 by a whole-wave DPP shift; lane 0 takes
 //    it from the band above;
 //  - the state of a cell is fp64; exp/log are the fp32 hardware ones applied
-//    to fp64 differences (see softmin_cell);
+//    to fp64 differences (see softmin2_cell);
 //  - the kBandsPerWG band waves of a workgroup run decoupled, each at its own
 //    pace, chunk by chunk (16 steps); band w reads its top row from an LDS
 //    ring that band w-1's lane 63 fills, with written/released column
