@@ -27,7 +27,9 @@
 
 namespace sdtw {
 
-constexpr int kFR = 128;     // distance/E ring columns per band (8 blocks of 16)
+// Distance/E ring columns per band: 256 (16 blocks of 16) where the LDS
+// holds them, else 128 (see launch_fused_one).
+constexpr int kFRDeep = 256, kFRShallow = 128;
 constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
 constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
 constexpr int kRevHelpD = 2; // distance helpers, reverse sweep (3 for 64 < D <= 128)
@@ -43,8 +45,8 @@ __host__ __device__ constexpr int chain_y_floats(int DC) { return 2 * 16 * (DC +
 // Dynamic LDS of one workgroup: the band's x rows and the distance/E ring,
 // plus (reverse sweep, HC chain-rule helpers of DC columns of D each) the
 // helpers' staged y rows.
-size_t fused_lds_bytes(int64_t D, int DC = 0, int HC = 0) {
-  return (size_t)64 * fused_pitch(D) * 4 + (size_t)kFR * kFPitch * 4 +
+size_t fused_lds_bytes(int64_t D, int DC, int HC, int FR) {
+  return (size_t)64 * fused_pitch(D) * 4 + (size_t)FR * kFPitch * 4 +
          (DC ? (size_t)HC * chain_y_floats(DC) * 4 : 0);
 }
 
@@ -67,7 +69,7 @@ __device__ __forceinline__ unsigned umin_u(unsigned a, unsigned b) { return a < 
 // ---------------------------------------------------------------------------
 // Band wave.
 // ---------------------------------------------------------------------------
-template <bool REV, bool STORE, bool CKPT, bool SPLIT>
+template <bool REV, bool STORE, bool CKPT, bool SPLIT, int FR>
 __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, float* dr, int b,
                                            int band, int lane) {
   const int64_t N = a.N, M = a.M, S = a.S;
@@ -139,7 +141,7 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
     if (seen_d < (unsigned)q + 1) seen_d = lds_wait_ge(&sh.d_ready, (unsigned)q + 1);
     float dn[kCH];
 #pragma unroll
-    for (int u = 0; u < kCH; ++u) dn[u] = dr[((t0 + u - lane) & (kFR - 1)) * kFPitch + lane];
+    for (int u = 0; u < kCH; ++u) dn[u] = dr[((t0 + u - lane) & (FR - 1)) * kFPitch + lane];
 
     double bottom[kCH];
     double* sp = rbase + (int64_t)t0 * dir;
@@ -170,7 +172,7 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
           if (CKPT && band_ck && ckp) ckp[t] = c;
         } else if (!boundary) {
           const float ev = align_entry(xnm, rn[u], tp);
-          dr[((t - lane) & (kFR - 1)) * kFPitch + lane] = ev;
+          dr[((t - lane) & (FR - 1)) * kFPitch + lane] = ev;
           if (ALIGN) {
             const int col = t - lane;
             if (alignp && col < M) alignp[M - 1 - col] = ev;
@@ -250,7 +252,7 @@ __device__ __forceinline__ void fused_band(const DPArgs& a, FusedShared& sh, flo
 // ---------------------------------------------------------------------------
 // Distance helper h of nh: blocks p = h, h+nh, ... (sweep columns [16p, 16p+16)).
 // ---------------------------------------------------------------------------
-template <bool REV, int NHC>
+template <bool REV, int NHC, int FR>
 __device__ __forceinline__ void fused_dist_helper(const DPArgs& a, FusedShared& sh,
                                                   const float* xs, float* dr, int b, int h,
                                                   int nh, int lane) {
@@ -276,15 +278,18 @@ __device__ __forceinline__ void fused_dist_helper(const DPArgs& a, FusedShared& 
   }
   unsigned seen_dp = 0, seen_e = 0;
   for (int p = h; p < qcount; p += nh) {
-    // Block p takes the slots of block p-8: the band wave must be past it
-    // (chunk p-4 done) and, in the reverse sweep, the chain-rule helpers
-    // must have released it.
-    if (p >= kFR / kCH) {
-      const unsigned need = (unsigned)(p - 3);
+    // Block p takes the slots of block p - R (R = FR / 16 blocks in the
+    // ring): the band wave must be past it (its last reader is chunk
+    // p - R + 4, i.e. dp_done >= p - R + 5) and, in the reverse sweep, the
+    // chain-rule helpers must have released it (e_free >= p - R + 1).
+    constexpr int R = FR / kCH;
+    if (p >= R) {
+      const unsigned need = (unsigned)(p - R + 5);
       if (seen_dp < need) seen_dp = lds_wait_ge(&sh.dp_done, need);
-      if (REV && seen_e < (unsigned)(p - 7)) {
+      if (REV && seen_e < (unsigned)(p - R + 1)) {
         unsigned m = ~0u;
-        for (int c = 0; c < NHC; ++c) m = umin_u(m, lds_wait_ge(&sh.e_free[c], (unsigned)(p - 7)));
+        for (int c = 0; c < NHC; ++c)
+          m = umin_u(m, lds_wait_ge(&sh.e_free[c], (unsigned)(p - R + 1)));
         seen_e = m;
       }
     }
@@ -327,7 +332,7 @@ __device__ __forceinline__ void fused_dist_helper(const DPArgs& a, FusedShared& 
     if (s0 < steps4) batch(s0, std::true_type{});
     ny += __shfl_xor(ny, 16, 64);
     ny += __shfl_xor(ny, 32, 64);
-    float* col = dr + (int)(sc & (kFR - 1)) * kFPitch;
+    float* col = dr + (int)(sc & (FR - 1)) * kFPitch;
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -363,7 +368,7 @@ __host__ __device__ inline int chain_xch_floats(int64_t D, int DC, int nhc) {
   return (int)((D + DC - 1) / DC) * (chain_phases(D, DC, nhc) - 1) * 64 * (32 * (DC / 32) + 2);
 }
 
-template <int DC>
+template <int DC, int FR>
 __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared& sh,
                                                    const float* xs, const float* dr,
                                                    float* ys, float* xch, int b, int band,
@@ -447,7 +452,7 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
       if (kBatch) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const float* ecol = dr + (int)((c0 + 2 * s + h) & (kFR - 1)) * kFPitch;
+          const float* ecol = dr + (int)((c0 + 2 * s + h) & (FR - 1)) * kFPitch;
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) ev[s][rt] = ecol[32 * rt + r32];
         }
@@ -456,7 +461,7 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
       for (int s = 0; s < 8; ++s) {
         const int cl = 2 * s + h;                 // column of the block
         const bool cok = c0 + cl < M;
-        const float* ecol = dr + (int)((c0 + cl) & (kFR - 1)) * kFPitch;
+        const float* ecol = dr + (int)((c0 + cl) & (FR - 1)) * kFPitch;
         float av[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -482,7 +487,7 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
 #pragma unroll
       for (int t = 0; t < 2 * NT; ++t) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
       const bool cok = c0 + r16 < M;
-      const float* ecol = dr + (int)((c0 + r16) & (kFR - 1)) * kFPitch;
+      const float* ecol = dr + (int)((c0 + r16) & (FR - 1)) * kFPitch;
       // Up to DC = 64, E and the x operands are read as one batch; columns
       // of D past dend then read a clamped in-range entry whose products are
       // never written out.
@@ -603,7 +608,7 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
 // rows handed between bands are either whole (hcols = 0) or global rings of
 // hcols columns; with rings tickets run pair by pair (see above).
 // ---------------------------------------------------------------------------
-template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC>
+template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC, int FR>
 __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsigned hcols) {
   extern __shared__ float smem[];
   __shared__ FusedShared sh;
@@ -642,15 +647,15 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
   __syncthreads();
 
   if (w == 0) {
-    fused_band<REV, !INFER, CKPT, (HD + HC + 2 <= 8)>(a, sh, dr, b, band, lane);
+    fused_band<REV, !INFER, CKPT, (HD + HC + 2 <= 8), FR>(a, sh, dr, b, band, lane);
   } else if (w <= HD) {
-    fused_dist_helper<REV, HC>(a, sh, xs, dr, b, w - 1, HD, lane);
+    fused_dist_helper<REV, HC, FR>(a, sh, xs, dr, b, w - 1, HD, lane);
   } else if (w < kIO) {
     if (REV) {
       const int c = w - 1 - HD;
-      float* ys = dr + kFR * kFPitch + c * chain_y_floats(DC);
-      float* xch = dr + kFR * kFPitch + HC * chain_y_floats(DC);
-      fused_chain_helper<DC>(a, sh, xs, dr, ys, xch, b, band, c, HC, lane);
+      float* ys = dr + FR * kFPitch + c * chain_y_floats(DC);
+      float* xch = dr + FR * kFPitch + HC * chain_y_floats(DC);
+      fused_chain_helper<DC, FR>(a, sh, xs, dr, ys, xch, b, band, c, HC, lane);
     }
   } else {
     const int64_t pb = (int64_t)b * a.nseg;
@@ -685,12 +690,10 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
                !(REV && a.align != nullptr));
 }
 
-template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC>
-static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcols = 0) {
-  auto kern = k_dp_fused<REV, INFER, CKPT, HD, HC, DC>;
-  static_assert(HC <= kRevHelpCMax, "chain-rule helpers");
-  const size_t lds = fused_lds_bytes(a.D, REV ? DC : 0, HC) +
-                     (REV ? (size_t)chain_xch_floats(a.D, DC, HC) * 4 : 0);
+template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC, int FR>
+static hipError_t launch_fused_ring(const DPArgs& a, hipStream_t s, unsigned hcols,
+                                    size_t lds) {
+  auto kern = k_dp_fused<REV, INFER, CKPT, HD, HC, DC, FR>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -698,6 +701,38 @@ static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcol
   TimedLaunch timed_(INFER ? "dp_infer" : (REV ? "dp_fused_rev" : "dp_fused_fwd"), s);
   hipLaunchKernelGGL(kern, dim3(grid), dim3((HD + HC + 2) * 64), lds, s, a, hcols);
   return hipGetLastError();
+}
+
+// Largest dynamic LDS a workgroup may take next to the static FusedShared
+// (gfx950: 160 KiB per workgroup).
+static size_t fused_lds_limit() {
+  int dev = 0, lim = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    lim = 160 * 1024;
+  return (size_t)lim > sizeof(FusedShared) ? (size_t)lim - sizeof(FusedShared) : 0;
+}
+
+// The deep ring (16 blocks) lets the distance helpers run up to 12 blocks
+// ahead of the band wave, and in the reverse sweep lets a block's slot wait
+// for the chain-rule helpers that long: with 8 blocks, a helper's block
+// (y loads and fp64 MFMAs, ~4.4 us at D = 64) plus the chain-rule helpers'
+// release of the slot did not fit in the four chunks of slack, and the band
+// wave waited ~1 us per chunk for distances.  Measured (rocprof, fused
+// reverse / forward, us): B=32, N=M=512, D=64 224.6 / 129.2 -> 189.4 / 125.9;
+// 32 x 256^2, D=128 155.7 / 102.2 -> 130.9 / 91.2; 32 x 4096 x 1000, D=128
+// 2623 / 1583 -> 2556 / 1537; inference at B=32, N=M=512 124.2 -> 120.0.
+// The shallow ring is kept where the deep one does not fit (the reverse
+// sweep from D ~ 220 on, with its 64-column chain-rule helpers).
+template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC>
+static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcols = 0) {
+  static_assert(HC <= kRevHelpCMax, "chain-rule helpers");
+  const size_t xch = REV ? (size_t)chain_xch_floats(a.D, DC, HC) * 4 : 0;
+  const size_t deep = fused_lds_bytes(a.D, REV ? DC : 0, HC, kFRDeep) + xch;
+  if (deep <= fused_lds_limit())
+    return launch_fused_ring<REV, INFER, CKPT, HD, HC, DC, kFRDeep>(a, s, hcols, deep);
+  return launch_fused_ring<REV, INFER, CKPT, HD, HC, DC, kFRShallow>(
+      a, s, hcols, fused_lds_bytes(a.D, REV ? DC : 0, HC, kFRShallow) + xch);
 }
 
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
