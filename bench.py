@@ -13,8 +13,9 @@ starts.  Prints one JSON line.
 Metric: DP cells per second, B*N*M / (seconds per step), plus peak memory of
 the autograd path.  `roofline` describes the dominant kernel (the launch that
 runs both sweeps), its duration taken from HIP events that the library
-records on the launch stream (sdtw_timing); `kernels` lists every launch of
-a step the same way.  `cpu_baseline` is the fp64 oracle on the host, timed
+records on the launch stream (sdtw_timing); `dist` puts the distance kernel
+against the HBM and fp64-MFMA roofs; `kernels` lists every launch of a step
+the same way.  `cpu_baseline` is the fp64 oracle on the host, timed
 on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -507,6 +508,19 @@ def main():
                for k, v in per_kernel.items()}
     dom_ms = sum(per_kernel[DOMINANT]) / len(per_kernel[DOMINANT])
     achieved = ALU_SLOTS_PER_CELL * cells / (dom_ms * 1e-3) / 1e12
+    # The distance kernel against both of its roofs: HBM on its algorithmic
+    # bytes (the fp32 distances written, x and y read once) and fp64 MFMA on
+    # its 2*D flops per cell.
+    dist_ms = sum(per_kernel["dist_skew"]) / len(per_kernel["dist_skew"])
+    dist_bytes = 4 * cells + 4 * B * (N + M) * D
+    dist_gbs = dist_bytes / (dist_ms * 1e-3) / 1e9
+    dist_tflops = 2 * cells * D / (dist_ms * 1e-3) / 1e12
+    dist = {"kernel": "distances into the band-step layout (k_dist)", "launch_us": dist_ms * 1e3,
+            "algorithmic_bytes": dist_bytes, "achieved_gbs": dist_gbs,
+            "frac_hbm": dist_gbs * 1e9 / PEAK_HBM, "achieved_tflops": dist_tflops,
+            "frac_f64_mfma": dist_tflops * 1e12 / PEAK_F64_MFMA,
+            "min_us_f64_mfma": 2 * cells * D / PEAK_F64_MFMA * 1e6,
+            "min_us_hbm": dist_bytes / PEAK_HBM * 1e6}
 
     peak, peak_over = peak_mib(torch, SoftDTW, x, y, gamma, False)
     ms_f, _, _, _ = measure(L, torch, x, y, gamma, L.SDTW_MODE_FUSED,
@@ -576,6 +590,7 @@ def main():
                      "traffic": recorded_traffic(), "traffic_unit": "bytes per launch",
                      "launch_us": dom_ms * 1e3,
                      "algorithmic_gbs": DP_BYTES_PER_CELL * cells / (dom_ms * 1e-3) / 1e9},
+        "dist": dist,
         "kernels": kernels,
         "per_config": per_config,
     }

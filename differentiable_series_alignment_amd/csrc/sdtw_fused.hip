@@ -27,25 +27,29 @@
 
 namespace sdtw {
 
-// Distance/E ring columns per band: 256 (16 blocks of 16) where the LDS
-// holds them, else 128 (see launch_fused_one).
-constexpr int kFRDeep = 256, kFRShallow = 128;
+// Distance/E ring columns per band (16 blocks of 16; see launch_fused_one).
+constexpr int kFR = 256;
 constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
 constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
 constexpr int kRevHelpD = 2; // distance helpers, reverse sweep (3 for 64 < D <= 128)
 constexpr int kRevHelpCMax = 4;
 constexpr int kYB = 16;      // feature steps (of 4) per batch of y loads
 
-__host__ __device__ inline int fused_pitch(int64_t D) { return (int)(((D + 3) / 4) * 4 + 4); }
+__host__ __device__ constexpr int fused_pitch(int64_t D) { return (int)(((D + 3) / 4) * 4 + 4); }
 
-// y rows staged for a chain-rule helper: two blocks of 16 rows, DC columns of
-// D each, rows padded by 2 floats (LDS banks).
-__host__ __device__ constexpr int chain_y_floats(int DC) { return 2 * 16 * (DC + 2); }
+// y rows staged for a chain-rule helper: blocks of 16 rows, DC columns of D
+// each, rows padded by 2 floats (LDS banks).  Two blocks (the next one
+// staged while the current one is in use) up to DC = 32; one for the
+// 64-column helpers, whose workgroups (D > 128) could not otherwise hold the
+// 256-column ring next to x rows of up to 256 features: 32 x 256^2, D=256,
+// reverse sweep 306 -> 259 us with the deeper ring, no change at D = 192.
+__host__ __device__ constexpr int chain_y_bufs(int DC) { return DC > 32 ? 1 : 2; }
+__host__ __device__ constexpr int chain_y_floats(int DC) { return chain_y_bufs(DC) * 16 * (DC + 2); }
 
 // Dynamic LDS of one workgroup: the band's x rows and the distance/E ring,
 // plus (reverse sweep, HC chain-rule helpers of DC columns of D each) the
 // helpers' staged y rows.
-size_t fused_lds_bytes(int64_t D, int DC, int HC, int FR) {
+constexpr size_t fused_lds_bytes(int64_t D, int DC, int HC, int FR) {
   return (size_t)64 * fused_pitch(D) * 4 + (size_t)FR * kFPitch * 4 +
          (DC ? (size_t)HC * chain_y_floats(DC) * 4 : 0);
 }
@@ -358,13 +362,13 @@ __device__ __forceinline__ void fused_dist_helper(const DPArgs& a, FusedShared& 
 // a block is processed and staged in the helper's LDS area `ys` (two
 // blocks), so a block never waits on memory.
 // ---------------------------------------------------------------------------
-__host__ __device__ inline int chain_phases(int64_t D, int DC, int nhc) {
+__host__ __device__ constexpr int chain_phases(int64_t D, int DC, int nhc) {
   const int nsl = (int)((D + DC - 1) / DC);
   const int nph = nhc / nsl;
   return nph < 1 ? 1 : nph;
 }
 // LDS floats for the dx hand-over between the helpers of a slice.
-__host__ __device__ inline int chain_xch_floats(int64_t D, int DC, int nhc) {
+__host__ __device__ constexpr int chain_xch_floats(int64_t D, int DC, int nhc) {
   return (int)((D + DC - 1) / DC) * (chain_phases(D, DC, nhc) - 1) * 64 * (32 * (DC / 32) + 2);
 }
 
@@ -420,7 +424,7 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
     }
   };
   auto stage_y = [&](int k) {             // k: the helper's own block count
-    float* yd = ys + (k & 1) * 16 * YP;
+    float* yd = ys + (chain_y_bufs(DC) == 2 ? (k & 1) : 0) * 16 * YP;
 #pragma unroll
     for (int k = 0; k < YL; ++k) {
       const int idx = lane + 64 * k;
@@ -440,7 +444,7 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
     const unsigned need = umin_u((unsigned)p + 5, (unsigned)qcount);
     if (seen_dp < need) seen_dp = lds_wait_ge(&sh.dp_done, need);
     const int64_t c0 = (int64_t)p * kCH;
-    const float* yc = ys + (k & 1) * 16 * YP;
+    const float* yc = ys + (chain_y_bufs(DC) == 2 ? (k & 1) : 0) * 16 * YP;
     if (want_gx) {
       // dx += E[64 x 16] . Y[16 x DC] on v_mfma_f32_32x32x2_f32.  Up to
       // DC = 64 the block's E entries are read as one batch (unconditional
@@ -519,9 +523,10 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
       cs += __shfl_xor(cs, 16, 64);
       cs += __shfl_xor(cs, 32, 64);
     }
-    // The next block's y rows go into the other staging slot (last read in
-    // the block before this one) before this block's atomics are issued.
-    if (more) stage_y(k + 1);
+    // With two staging slots the next block's y rows go into the other one
+    // (last read in the block before this one) before this block's atomics
+    // are issued.
+    if (chain_y_bufs(DC) == 2 && more) stage_y(k + 1);
     if (want_gy) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -540,6 +545,9 @@ __device__ __forceinline__ void fused_chain_helper(const DPArgs& a, FusedShared&
         }
       }
     }
+    // With one slot they replace this block's rows after its last reads
+    // (the LDS performs one wave's operations in order).
+    if (chain_y_bufs(DC) == 1 && more) stage_y(k + 1);
     if (lane == 0) lds_publish(&sh.e_free[c], umin_u((unsigned)(p + nph), (unsigned)qcount));
   }
   if (lane == 0) lds_publish(&sh.e_free[c], (unsigned)qcount);
@@ -613,8 +621,16 @@ __global__ __launch_bounds__((HD + HC + 2) * 64) void k_dp_fused(DPArgs a, unsig
   extern __shared__ float smem[];
   __shared__ FusedShared sh;
   constexpr int kIO = HD + HC + 1;
+  constexpr int kNW = HD + HC + 2;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // Role of each wave: 0 the band wave, 1..HD the distance helpers, then the
+  // chain-rule helpers, kIO the hand-off wave.  A workgroup's waves go to
+  // the CU's four SIMDs in turn, so wave 4 shares the band wave's SIMD: in a
+  // workgroup of more than five waves it takes the light hand-off role and
+  // the helpers go to the other SIMDs (fused reverse, B=32, N=M=512, D=64:
+  // 190-201 -> 177 us; 32 x 256^2, D=64: 96-115 -> 87 us).
+  const int wi = threadIdx.x >> 6;
+  const int w = (kNW > 5 && wi == 4) ? kIO : ((kNW > 5 && wi == kIO) ? 4 : wi);
   if (threadIdx.x == 0) sh.ticket = atomicAdd(&a.ctrl[0], 1u);
   if (threadIdx.x == 0) {
     launch_shared_init(a);
@@ -713,27 +729,40 @@ static size_t fused_lds_limit() {
   return (size_t)lim > sizeof(FusedShared) ? (size_t)lim - sizeof(FusedShared) : 0;
 }
 
-// The deep ring (16 blocks) lets the distance helpers run up to 12 blocks
+// The ring of 16 blocks lets the distance helpers run up to 12 blocks
 // ahead of the band wave, and in the reverse sweep lets a block's slot wait
 // for the chain-rule helpers that long: with 8 blocks, a helper's block
 // (y loads and fp64 MFMAs, ~4.4 us at D = 64) plus the chain-rule helpers'
 // release of the slot did not fit in the four chunks of slack, and the band
 // wave waited ~1 us per chunk for distances.  Measured (rocprof, fused
-// reverse / forward, us): B=32, N=M=512, D=64 224.6 / 129.2 -> 189.4 / 125.9;
-// 32 x 256^2, D=128 155.7 / 102.2 -> 130.9 / 91.2; 32 x 4096 x 1000, D=128
-// 2623 / 1583 -> 2556 / 1537; inference at B=32, N=M=512 124.2 -> 120.0.
-// The shallow ring is kept where the deep one does not fit (the reverse
-// sweep from D ~ 220 on, with its 64-column chain-rule helpers).
+// reverse / forward, us, 8 -> 16 blocks): B=32, N=M=512, D=64 224.6 / 129.2
+// -> 189.4 / 125.9; 32 x 256^2, D=128 155.7 / 102.2 -> 130.9 / 91.2;
+// 32 x 4096 x 1000, D=128 2623 / 1583 -> 2556 / 1537; inference at B=32,
+// N=M=512 124.2 -> 120.0.
 template <bool REV, bool INFER, bool CKPT, int HD, int HC, int DC>
 static hipError_t launch_fused_one(const DPArgs& a, hipStream_t s, unsigned hcols = 0) {
   static_assert(HC <= kRevHelpCMax, "chain-rule helpers");
-  const size_t xch = REV ? (size_t)chain_xch_floats(a.D, DC, HC) * 4 : 0;
-  const size_t deep = fused_lds_bytes(a.D, REV ? DC : 0, HC, kFRDeep) + xch;
-  if (deep <= fused_lds_limit())
-    return launch_fused_ring<REV, INFER, CKPT, HD, HC, DC, kFRDeep>(a, s, hcols, deep);
-  return launch_fused_ring<REV, INFER, CKPT, HD, HC, DC, kFRShallow>(
-      a, s, hcols, fused_lds_bytes(a.D, REV ? DC : 0, HC, kFRShallow) + xch);
+  const size_t lds = fused_lds_bytes(a.D, REV ? DC : 0, HC, kFR) +
+                     (REV ? (size_t)chain_xch_floats(a.D, DC, HC) * 4 : 0);
+  if (lds > fused_lds_limit()) return hipErrorNotSupported;   // see fused_lds_fits
+  return launch_fused_ring<REV, INFER, CKPT, HD, HC, DC, kFR>(a, s, hcols, lds);
 }
+
+// Every D the fused kernels take fits the 160 KiB of LDS of a gfx950
+// workgroup with the full ring: the forward's x rows and ring, and the
+// reverse's chain-rule helpers (DC = 32 up to D = 128, then 64) on top.
+constexpr bool fused_lds_fits() {
+  for (int64_t D = 1; D <= kFusedMaxD; ++D) {
+    const int DC = D <= 4 * 32 ? 32 : 64;
+    const size_t rev = fused_lds_bytes(D, DC, kRevHelpCMax, kFR) +
+                       (size_t)chain_xch_floats(D, DC, kRevHelpCMax) * 4;
+    const size_t fwd = fused_lds_bytes(D, 0, 0, kFR);
+    if (fwd + sizeof(FusedShared) > 160 * 1024 || rev + sizeof(FusedShared) > 160 * 1024)
+      return false;
+  }
+  return true;
+}
+static_assert(fused_lds_fits(), "fused workgroup LDS");
 
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
