@@ -31,7 +31,7 @@ namespace sdtw {
 constexpr int kFR = 256;
 constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
 constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
-constexpr int kRevHelpD = 2; // distance helpers, reverse sweep (3 for 64 < D <= 128)
+constexpr int kRevHelpD = 2; // distance helpers, reverse sweep (3 for D <= 32, 64 < D <= 128)
 constexpr int kRevHelpCMax = 4;
 constexpr int kYB = 16;      // feature steps (of 4) per batch of y loads
 
@@ -773,7 +773,13 @@ hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   // each slice's blocks (the helpers, not the band wave, set the pace there).
   // Up to D = 64 two distance helpers keep ahead of the band wave; beyond,
   // a third one (32x1024x1024, D=128: 826 us against 891; with 64-column
-  // chain helpers a third would push the registers into scratch).
+  // chain helpers a third would push the registers into scratch).  Up to
+  // D = 32 (one slice) two chain-rule helpers keep up, and the third
+  // distance helper that their room allows gains 5-7 % (32 x 512^2, D=16:
+  // 163 -> 153 us; 32 x 1024^2, D=16: 391 -> 363 us; 32 x 256^2, D=1:
+  // 81 -> 76 us); at D = 64 two would fall behind (C2 177 -> 212 us).
+  if (a.D <= 32)
+    return launch_fused_one<true, false, false, kRevHelpD + 1, 2, 32>(a, s);
   if (a.D <= 2 * 32)
     return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 32>(a, s);
   if (a.D <= 4 * 32)
