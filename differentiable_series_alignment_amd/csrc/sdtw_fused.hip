@@ -31,7 +31,7 @@ namespace sdtw {
 constexpr int kFR = 256;
 constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
 constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
-constexpr int kRevHelpD = 2; // distance helpers, reverse sweep (3 for D <= 32, 64 < D <= 128)
+constexpr int kRevHelpD = 2; // distance helpers, reverse sweep (3 for D <= 32, 64 < D <= 192)
 constexpr int kRevHelpCMax = 4;
 constexpr int kYB = 16;      // feature steps (of 4) per batch of y loads
 
@@ -784,6 +784,15 @@ hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
     return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 32>(a, s);
   if (a.D <= 4 * 32)
     return launch_fused_one<true, false, false, kRevHelpD + 1, kRevHelpCMax, 32>(a, s);
+  // Up to D = 192 the 64-column slices are three: three chain-rule helpers
+  // (the fourth had no slice) and a third distance helper, eight waves that
+  // pair each distance helper with a chain-rule helper on one SIMD
+  // (32 x 256^2, D=160: 219 -> 172 us; D=192: 229 -> 186 us; 8 x 1024^2,
+  // D=160: 875 -> 818 us).  Beyond, four slices need four helpers, and a
+  // third distance helper would make nine waves, too many for the
+  // 64-column helpers' registers.
+  if (a.D <= 3 * 64)
+    return launch_fused_one<true, false, false, kRevHelpD + 1, 3, 64>(a, s);
   return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 64>(a, s);
 }
 

@@ -106,12 +106,12 @@ def test_ragged_shapes(O, S, N, M, gamma, fused):
     check_against_oracle(O, S, x, y, gamma, fused=fused, what=f"{N}x{M} g={gamma}")
 
 
-@pytest.mark.parametrize("N,M,D", [(150, 333, 240), (70, 130, 160)])
+@pytest.mark.parametrize("N,M,D", [(150, 333, 240), (70, 130, 160), (90, 210, 136)])
 @pytest.mark.parametrize("fused", [False, True])
 def test_ragged_wide_features(O, S, N, M, D, fused):
     """D above 128 on ragged lengths: the fused reverse's 64-column chain-rule
-    helpers (the last slice partial), each restaging its y rows for every
-    one of the band's 16-column blocks."""
+    helpers (three up to D = 192, four beyond; the last slice partial), each
+    restaging its y rows for every one of the band's 16-column blocks."""
     x, y = pair_batch(3, N, M, D, seed=N + M + D)
     check_against_oracle(O, S, x, y, 0.5, fused=fused, what=f"{N}x{M} D={D}")
 
@@ -326,7 +326,7 @@ def test_barycenter_api(S):
 # --- fused mode against unfused mode ------------------------------------------------------
 
 @pytest.mark.parametrize("N,M,D", [(70, 45, 4), (300, 260, 64), (129, 700, 100), (257, 64, 200),
-                                   (150, 333, 240)])
+                                   (150, 333, 240), (200, 150, 176), (65, 90, 20)])
 def test_fused_matches_unfused(S, N, M, D):
     """Both modes see bit-identical distances and run the same recurrence, so
     the loss and the alignment matrix agree bitwise; gradients are summed in
@@ -353,7 +353,8 @@ def test_fused_matches_unfused(S, N, M, D):
     (2, 1100, 70, 8),      # 18 bands, groups of 5
     (2, 130, 1100, 16),    # long M
     (2, 2100, 300, 32),    # 33 bands, groups of 6 (last group of 3)
-    (2, 330, 150, 240),    # 6 bands, groups of 3, 64-column chain-rule helpers
+    (2, 330, 150, 240),    # 6 bands, groups of 3, four 64-column chain-rule helpers
+    (2, 200, 170, 176),    # 4 bands, groups of 2, three 64-column chain-rule helpers
 ])
 def test_checkpoint_matches_fused(S, B, N, M, D):
     """Checkpointed training recomputes the forward state group by group of
