@@ -767,30 +767,35 @@ static_assert(fused_lds_fits(), "fused workgroup LDS");
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
   if (!reverse) return launch_fused_one<false, false, false, kFwdHelpD, 0, 32>(a, s);
-  // Four chain-rule helpers on slices of DC columns of D: 32 up to D = 128,
-  // then 64 (wider helpers would not keep their accumulators in registers).
-  // Up to D = 64 the slices are one or two, and four or two helpers share
-  // each slice's blocks (the helpers, not the band wave, set the pace there).
-  // Up to D = 64 two distance helpers keep ahead of the band wave; beyond,
-  // a third one (32x1024x1024, D=128: 826 us against 891; with 64-column
-  // chain helpers a third would push the registers into scratch).  Up to
-  // D = 32 (one slice) two chain-rule helpers keep up, and the third
-  // distance helper that their room allows gains 5-7 % (32 x 512^2, D=16:
-  // 163 -> 153 us; 32 x 1024^2, D=16: 391 -> 363 us; 32 x 256^2, D=1:
-  // 81 -> 76 us); at D = 64 two would fall behind (C2 177 -> 212 us).
+  // The reverse workgroup: the band wave, HD distance helpers, HC chain-rule
+  // helpers on slices of DC columns of D (32 up to D = 128, then 64: wider
+  // slices would not keep their accumulators in registers) and the hand-off
+  // wave.  Where there are fewer slices than helpers, the helpers of a slice
+  // take its blocks in turn.  Per range of D (rocprof, fused reverse, us):
+  //   D <= 32 (one slice):       HD 3, HC 2; two chain-rule helpers keep up
+  //                              (32 x 512^2, D=16: 163 with HD 2, HC 4 ->
+  //                              153; 32 x 1024^2, D=16: 391 -> 363)
+  //   D <= 64 (two slices):      HD 2, HC 4; two chain-rule helpers fall
+  //                              behind (B=32, N=M=512: 177 -> 212 with
+  //                              HD 3, HC 2)
+  //   D <= 96 (three slices):    HD 3, HC 3, eight waves, each distance
+  //                              helper beside a chain-rule helper (32 x
+  //                              256^2, D=80: 129 with HD 3, HC 4 -> 106;
+  //                              32 x 1024^2, D=72: 655 -> 603)
+  //   D <= 128 (four slices):    HD 3, HC 4 (32 x 1024^2: 826 against 891
+  //                              with HD 2)
+  //   D <= 192 (three slices):   HD 3, HC 3 (32 x 256^2, D=160: 219 with
+  //                              HD 2, HC 4 -> 172)
+  //   D <= 256 (four slices):    HD 2, HC 4; nine waves would leave the
+  //                              64-column helpers too few registers
   if (a.D <= 32)
     return launch_fused_one<true, false, false, kRevHelpD + 1, 2, 32>(a, s);
   if (a.D <= 2 * 32)
     return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 32>(a, s);
+  if (a.D <= 3 * 32)
+    return launch_fused_one<true, false, false, kRevHelpD + 1, 3, 32>(a, s);
   if (a.D <= 4 * 32)
     return launch_fused_one<true, false, false, kRevHelpD + 1, kRevHelpCMax, 32>(a, s);
-  // Up to D = 192 the 64-column slices are three: three chain-rule helpers
-  // (the fourth had no slice) and a third distance helper, eight waves that
-  // pair each distance helper with a chain-rule helper on one SIMD
-  // (32 x 256^2, D=160: 219 -> 172 us; D=192: 229 -> 186 us; 8 x 1024^2,
-  // D=160: 875 -> 818 us).  Beyond, four slices need four helpers, and a
-  // third distance helper would make nine waves, too many for the
-  // 64-column helpers' registers.
   if (a.D <= 3 * 64)
     return launch_fused_one<true, false, false, kRevHelpD + 1, 3, 64>(a, s);
   return launch_fused_one<true, false, false, kRevHelpD, kRevHelpCMax, 64>(a, s);

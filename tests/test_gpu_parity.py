@@ -106,7 +106,7 @@ def test_ragged_shapes(O, S, N, M, gamma, fused):
     check_against_oracle(O, S, x, y, gamma, fused=fused, what=f"{N}x{M} g={gamma}")
 
 
-@pytest.mark.parametrize("N,M,D", [(150, 333, 240), (70, 130, 160), (90, 210, 136)])
+@pytest.mark.parametrize("N,M,D", [(150, 333, 240), (70, 130, 160), (90, 210, 136), (130, 77, 80)])
 @pytest.mark.parametrize("fused", [False, True])
 def test_ragged_wide_features(O, S, N, M, D, fused):
     """D above 128 on ragged lengths: the fused reverse's 64-column chain-rule
@@ -355,6 +355,7 @@ def test_fused_matches_unfused(S, N, M, D):
     (2, 2100, 300, 32),    # 33 bands, groups of 6 (last group of 3)
     (2, 330, 150, 240),    # 6 bands, groups of 3, four 64-column chain-rule helpers
     (2, 200, 170, 176),    # 4 bands, groups of 2, three 64-column chain-rule helpers
+    (2, 140, 260, 90),     # 3 bands, groups of 2, three 32-column chain-rule helpers
 ])
 def test_checkpoint_matches_fused(S, B, N, M, D):
     """Checkpointed training recomputes the forward state group by group of
