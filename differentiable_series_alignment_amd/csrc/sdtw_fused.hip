@@ -30,7 +30,8 @@ namespace sdtw {
 // Distance/E ring columns per band (16 blocks of 16; see launch_fused_one).
 constexpr int kFR = 256;
 constexpr int kFPitch = 66;  // floats per ring column: 64 rows + 2 (LDS banks)
-constexpr int kFwdHelpD = 3; // distance helpers, forward sweep
+constexpr int kFwdHelpD = 3; // distance helpers, forward sweep (D <= 64)
+constexpr int kFwdHelpDWide = 6; // distance helpers, forward sweep (D > 64)
 constexpr int kRevHelpD = 2; // distance helpers, reverse sweep (3 for D <= 32, 64 < D <= 192)
 constexpr int kRevHelpCMax = 4;
 constexpr int kYB = 16;      // feature steps (of 4) per batch of y loads
@@ -766,7 +767,16 @@ static_assert(fused_lds_fits(), "fused workgroup LDS");
 
 hipError_t launch_dp_fused(const DPArgs& a, bool reverse, hipStream_t s) {
   if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
-  if (!reverse) return launch_fused_one<false, false, false, kFwdHelpD, 0, 32>(a, s);
+  // Forward: the distance helpers alone keep the ring ahead of the band
+  // wave.  Up to D = 64 three do (six change nothing); beyond, six, two
+  // on each SIMD but the band wave's (rocprof, us, three -> six helpers:
+  // 32 x 256^2, D=128 91 -> 83, D=256 146 -> 131; 32 x 1024^2, D=128
+  // 452 -> 402; 32 x 4096 x 1000, D=128 1541 -> 1356; four or five
+  // helpers gain less or lose).
+  if (!reverse) {
+    if (a.D > 64) return launch_fused_one<false, false, false, kFwdHelpDWide, 0, 32>(a, s);
+    return launch_fused_one<false, false, false, kFwdHelpD, 0, 32>(a, s);
+  }
   // The reverse workgroup: the band wave, HD distance helpers, HC chain-rule
   // helpers on slices of DC columns of D (32 up to D = 128, then 64: wider
   // slices would not keep their accumulators in registers) and the hand-off
@@ -811,6 +821,11 @@ hipError_t launch_fused_range(const DPArgs& a, bool reverse, hipStream_t s) {
 
 hipError_t launch_infer(const DPArgs& a, unsigned hcols, hipStream_t s) {
   if (fused_bands_per_wg(a.D) == 0) return hipErrorNotSupported;
+  // The distance helpers as in the training forward (launch_dp_fused).
+  if (a.D > 64) {
+    if (a.ckpt) return launch_fused_one<false, true, true, kFwdHelpDWide, 0, 32>(a, s, hcols);
+    return launch_fused_one<false, true, false, kFwdHelpDWide, 0, 32>(a, s, hcols);
+  }
   if (a.ckpt) return launch_fused_one<false, true, true, kFwdHelpD, 0, 32>(a, s, hcols);
   return launch_fused_one<false, true, false, kFwdHelpD, 0, 32>(a, s, hcols);
 }
