@@ -671,6 +671,7 @@ def test_launch_timing_records_each_kernel(S, D, chain):
     (3, 1100, 700, 5), (2, 300, 2000, 4), (1, 64, 5000, 2), (4, 130, 513, 8),  # rings
     (40, 500, 600, 3),                                    # whole rows, band-major
     (9, 2048, 8192, 2),                                   # rings, more bands than CUs
+    (2, 300, 700, 100), (3, 200, 300, 160),               # D > 64: six distance helpers
 ])
 def test_inference_mode_matches_training_loss(S, B, N, M, D):
     """The inference mode (no state kept; rows handed between bands whole
